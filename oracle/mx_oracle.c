@@ -1,0 +1,336 @@
+/*
+ * mx_oracle.c -- plain, slow CPU oracle for the MXFP8 microscaled hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, loads or
+ * calls this file; only the tests, the package's smoke check and the bench's
+ * CPU-baseline leg do.  It shares no code, header, table or constant
+ * generator with the HIP kernels.
+ *
+ * Everything is computed in IEEE binary64 from the definitions:
+ *
+ *   - MX block quantisation: a block of 32 consecutive elements (or a 32x32
+ *     weight tile) shares one E8M0 scale that is recomputed from the data on
+ *     every call.  Sources: torchtitan-npu MXFP8/HiF8 tutorial, "MXFP8 / HiF8
+ *     architecture overview" (the MXFP8 bullet: 32 elements share one e8m0
+ *     scale, dynamic quantisation, BF16 output); MindSpeed RFC "add
+ *     MXFP8-32x32 quantisation support to FSDP", sections 1.1, 3.1 and 3.3.3
+ *     (block size [1,32,32], forward and backward share one FP8 weight and
+ *     differ only in the scale).
+ *   - The scale rule is "rceil": the scale exponent is the smallest integer e
+ *     with amax <= 448 * 2^e, i.e. ceil(log2(amax / 448)); the tutorial's
+ *     step-3 log names the recipe "mxfp8_rceil".  Elements are divided by
+ *     2^e, rounded to nearest (ties to even) and saturated to E4M3 (the RFC,
+ *     section 3.3.1, fixes the element type to E4M3).
+ *   - The number formats E4M3 (OCP OFP8 "E4M3FN": bias 7, max 448, no
+ *     infinities, S.1111.111 = NaN) and E8M0 (unsigned power-of-two exponent,
+ *     bias 127, 0xFF = NaN) are named, not defined, by the pages; they are
+ *     written out here from the OCP definitions.
+ *
+ * Readings taken where the pages are silent (each also listed with its
+ * justification in the design notes of the repository):
+ *   R1  amax == 0: the exponent is clamped to its smallest value, -127, so the
+ *       scale byte is 0x00.
+ *   R2  the exponent is clamped to the finite E8M0 range [-127, 127].
+ *   R3  a block holding a NaN or an infinity gets scale byte 0xFF (NaN) and
+ *       every payload byte 0x7F (E4M3 NaN).
+ *   R4  the sign of a zero result is kept (-0 and tiny negatives give 0x80).
+ *   R5  BF16 subnormal inputs are not flushed.
+ *   R6  saturation clamps to +-448 (unreachable for finite blocks: every
+ *       |x| <= amax <= 448 * 2^e).
+ *   R7  column-axis output is written transposed: q_t[c][r], s_t[c][r/32].
+ *   R8  the 32x32 forward and backward scales are two views of one tile
+ *       array s[R/32][C/32].
+ *
+ * Threading: OpenMP over independent rows / blocks only; no element's
+ * arithmetic is split or reordered.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ------------------------------------------------------------------------ */
+/* Number formats                                                            */
+/* ------------------------------------------------------------------------ */
+
+/* BF16: 1 sign, 8 exponent bits (bias 127), 7 mantissa bits; the top half of
+ * an IEEE binary32.  Exact in binary64. */
+double orc_bf16_value(uint16_t bits)
+{
+    int s = bits >> 15;
+    int E = (bits >> 7) & 0xFF;
+    int m = bits & 0x7F;
+    double mag;
+    if (E == 0xFF)
+        mag = m ? NAN : INFINITY;
+    else if (E == 0)
+        mag = ldexp((double)m, -126 - 7);          /* subnormal: 0.m * 2^-126 */
+    else
+        mag = ldexp(1.0 + m / 128.0, E - 127);
+    return s ? -mag : mag;
+}
+
+/* OCP E4M3: S.EEEE.MMM, bias 7.  E=0 is subnormal (2^-6 * M/8); E=15,M=7 is
+ * NaN; there is no infinity.  Largest finite value 0x7E = 448. */
+double orc_e4m3_value(uint8_t code)
+{
+    int s = code >> 7;
+    int E = (code >> 3) & 0xF;
+    int M = code & 0x7;
+    double mag;
+    if (E == 15 && M == 7)
+        return NAN;
+    if (E == 0)
+        mag = ldexp(M / 8.0, -6);
+    else
+        mag = ldexp(1.0 + M / 8.0, E - 7);
+    return s ? -mag : mag;
+}
+
+/* E8M0: unsigned exponent, value 2^(b-127); 0xFF is NaN. */
+double orc_e8m0_value(uint8_t b)
+{
+    if (b == 0xFF)
+        return NAN;
+    return ldexp(1.0, (int)b - 127);
+}
+
+/* Round a binary64 value to E4M3: nearest representable value, ties to the
+ * even mantissa, saturating to +-448 (R6), NaN -> 0x7F, sign of zero kept
+ * (R4).  The grid of E4M3 magnitudes has spacing 2^-9 below 2^-6 (subnormal
+ * range) and 2^(floor(log2|v|) - 3) above. */
+uint8_t orc_e4m3_round(double v)
+{
+    if (isnan(v))
+        return 0x7F;
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    double a = fabs(v);
+    if (a >= 448.0)
+        return sign | 0x7E;
+    int p; /* a lies on the grid k * 2^p */
+    if (a < 0x1p-6) {
+        p = -9;
+    } else {
+        int ex;
+        frexp(a, &ex);          /* a = f * 2^ex, f in [0.5, 1) */
+        p = (ex - 1) - 3;       /* three fraction bits below the leading one */
+    }
+    double k = nearbyint(ldexp(a, -p)); /* default rounding mode: ties to even */
+    double r = ldexp(k, p);             /* the rounded magnitude, <= 448 here */
+    if (r == 0.0)
+        return sign;
+    if (r < 0x1p-6) /* subnormal code: r = M * 2^-9 */
+        return sign | (uint8_t)ldexp(r, 9);
+    int ex;
+    double f = frexp(r, &ex); /* r = f * 2^ex = (2f) * 2^(ex-1) */
+    int E = (ex - 1) + 7;
+    int M = (int)((2.0 * f - 1.0) * 8.0);
+    return sign | (uint8_t)((E << 3) | M);
+}
+
+/* rceil: the smallest integer e with amax <= 448 * 2^e, i.e. the ceiling of
+ * log2(amax / 448), clamped to [-127, 127] (R1, R2). */
+int orc_rceil_exponent(double amax)
+{
+    if (amax == 0.0)
+        return -127;
+    int e = (int)ceil(log2(amax / 448.0));
+    if (e < -127)
+        e = -127;
+    if (e > 127)
+        e = 127;
+    /* make the log2 estimate exactly the definition */
+    while (e > -127 && amax <= ldexp(448.0, e - 1))
+        e--;
+    while (e < 127 && amax > ldexp(448.0, e))
+        e++;
+    return e;
+}
+
+/* ------------------------------------------------------------------------ */
+/* One MX block                                                              */
+/* ------------------------------------------------------------------------ */
+
+/* Quantise n values (already decoded to binary64) sharing one scale.
+ * Writes n codes and returns the scale byte. */
+static uint8_t quant_block(int n, const double *v, uint8_t *codes)
+{
+    for (int i = 0; i < n; i++) {
+        if (!isfinite(v[i])) { /* R3 */
+            for (int j = 0; j < n; j++)
+                codes[j] = 0x7F;
+            return 0xFF;
+        }
+    }
+    double amax = 0.0;
+    for (int i = 0; i < n; i++)
+        if (fabs(v[i]) > amax)
+            amax = fabs(v[i]);
+    int e = orc_rceil_exponent(amax);
+    for (int i = 0; i < n; i++)
+        codes[i] = orc_e4m3_round(ldexp(v[i], -e)); /* exact power-of-two scaling */
+    return (uint8_t)(e + 127);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Quantisation modes.  x is BF16 [R, C] row-major.                          */
+/* ------------------------------------------------------------------------ */
+
+/* 1x32 along the row (the contraction axis of a TN GEMM):
+ * q[R][C], s[R][C/32].  Requires C % 32 == 0. */
+void orc_quant_row(const uint16_t *x, int64_t R, int64_t C, uint8_t *q, uint8_t *s)
+{
+    int64_t nb = C / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < R; r++) {
+        double v[32];
+        for (int64_t j = 0; j < nb; j++) {
+            for (int i = 0; i < 32; i++)
+                v[i] = orc_bf16_value(x[r * C + 32 * j + i]);
+            s[r * nb + j] = quant_block(32, v, q + r * C + 32 * j);
+        }
+    }
+}
+
+/* 32x1 along the column (blocks of 32 consecutive rows of one column),
+ * written transposed (R7): q_t[C][R], s_t[C][R/32].  Requires R % 32 == 0. */
+void orc_quant_col(const uint16_t *x, int64_t R, int64_t C, uint8_t *q_t, uint8_t *s_t)
+{
+    int64_t nb = R / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < C; c++) {
+        double v[32];
+        for (int64_t i = 0; i < nb; i++) {
+            for (int k = 0; k < 32; k++)
+                v[k] = orc_bf16_value(x[(32 * i + k) * C + c]);
+            s_t[c * nb + i] = quant_block(32, v, q_t + c * R + 32 * i);
+        }
+    }
+}
+
+/* 32x32 tiles (RFC block size [1,32,32]): one scale per tile, payload in the
+ * original layout: q[R][C], s[R/32][C/32] (R8).  Requires R, C % 32 == 0. */
+void orc_quant_block32(const uint16_t *x, int64_t R, int64_t C, uint8_t *q, uint8_t *s)
+{
+    int64_t tr = R / 32, tc = C / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < tr * tc; t++) {
+        int64_t i = t / tc, j = t % tc;
+        double v[1024];
+        uint8_t codes[1024];
+        for (int a = 0; a < 32; a++)
+            for (int b = 0; b < 32; b++)
+                v[32 * a + b] = orc_bf16_value(x[(32 * i + a) * C + 32 * j + b]);
+        s[i * tc + j] = quant_block(1024, v, codes);
+        for (int a = 0; a < 32; a++)
+            memcpy(q + (32 * i + a) * C + 32 * j, codes + 32 * a, 32);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* GEMM: C[m][n] = sum_k A[m][k] * B[n][k] on the dequantised operands       */
+/* ------------------------------------------------------------------------ */
+
+/* How the B operand and its scales are laid out:
+ *   0  B bytes [N][K], scales [N][K/32]           (1x32 blocks along K)
+ *   1  B bytes [N][K], tile scales [N/32][K/32]   (32x32 weight, forward)
+ *   2  B bytes [K][N], tile scales [K/32][N/32]   (the same 32x32 weight
+ *      stored [out=K][in=N], contracted over its rows: backward data) */
+static double b_value(int bkind, int64_t N, int64_t K, const uint8_t *b, const uint8_t *sb,
+                      int64_t n, int64_t k)
+{
+    switch (bkind) {
+    case 0:
+        return orc_e4m3_value(b[n * K + k]) * orc_e8m0_value(sb[n * (K / 32) + k / 32]);
+    case 1:
+        return orc_e4m3_value(b[n * K + k]) * orc_e8m0_value(sb[(n / 32) * (K / 32) + k / 32]);
+    default:
+        return orc_e4m3_value(b[k * N + n]) * orc_e8m0_value(sb[(k / 32) * (N / 32) + n / 32]);
+    }
+}
+
+/* ref[M][N] = sum_k a*b in binary64 and bound[M][N] = sum_k |a*b| (the
+ * tolerance scale).  a: bytes [M][K] with scales [M][K/32].  Either output
+ * pointer may be NULL.  Returns 0, or -1 on a shape the layout forbids. */
+int orc_gemm(int bkind, int64_t M, int64_t N, int64_t K,
+             const uint8_t *a, const uint8_t *sa, const uint8_t *b, const uint8_t *sb,
+             double *ref, double *bound)
+{
+    if (K % 32 != 0 || M < 0 || N < 0)
+        return -1;
+    if (bkind != 0 && N % 32 != 0)
+        return -1;
+    if (M == 0 || N == 0)
+        return 0;
+    /* dequantise B once: bt[n][k] */
+    double *bt = (double *)malloc((size_t)N * (size_t)(K ? K : 1) * sizeof(double));
+    if (!bt)
+        return -2;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; n++)
+        for (int64_t k = 0; k < K; k++)
+            bt[n * K + k] = b_value(bkind, N, K, b, sb, n, k);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t m = 0; m < M; m++) {
+        double *av = (double *)malloc((size_t)(K ? K : 1) * sizeof(double));
+        if (!av)
+            abort();
+        for (int64_t k = 0; k < K; k++)
+            av[k] = orc_e4m3_value(a[m * K + k]) * orc_e8m0_value(sa[m * (K / 32) + k / 32]);
+        for (int64_t n = 0; n < N; n++) {
+            const double *bv = bt + n * K;
+            double acc = 0.0, mag = 0.0;
+            for (int64_t k = 0; k < K; k++) {
+                double p = av[k] * bv[k];
+                acc += p;
+                mag += fabs(p);
+            }
+            if (ref)
+                ref[m * N + n] = acc;
+            if (bound)
+                bound[m * N + n] = mag;
+        }
+        free(av);
+    }
+    free(bt);
+    return 0;
+}
+
+/* Grouped GEMM for MoE experts: rows offsets[g] .. offsets[g+1]-1 of the
+ * token matrix a [T][K] are multiplied by expert g's weight b[g] ([N][K],
+ * scales [N][K/32]); ref/bound are [T][N].  Empty groups contribute no rows.
+ * Returns 0, or -1 if the offsets are not a non-decreasing cover of [0, T]. */
+int orc_grouped_gemm(int64_t G, const int64_t *offsets, int64_t T, int64_t N, int64_t K,
+                     const uint8_t *a, const uint8_t *sa, const uint8_t *b, const uint8_t *sb,
+                     double *ref, double *bound)
+{
+    if (K % 32 != 0 || offsets[0] != 0 || offsets[G] != T)
+        return -1;
+    for (int64_t g = 0; g < G; g++)
+        if (offsets[g + 1] < offsets[g])
+            return -1;
+    for (int64_t g = 0; g < G; g++) {
+        int64_t r0 = offsets[g], rows = offsets[g + 1] - offsets[g];
+        if (rows == 0)
+            continue;
+        int rc = orc_gemm(0, rows, N, K, a + r0 * K, sa + r0 * (K / 32),
+                          b + g * N * K, sb + g * N * (K / 32),
+                          ref ? ref + r0 * N : NULL, bound ? bound + r0 * N : NULL);
+        if (rc)
+            return rc;
+    }
+    return 0;
+}
+
+int orc_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
