@@ -1,0 +1,326 @@
+#!/usr/bin/env python3
+"""Throughput of the MXFP8 hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+
+  linear stack, 4 layers of hidden 7168 -> 18432 -> 7168 at 32768 tokens,
+    1x32 variant:  per layer dual-axis quantisation of X, W, dY for both
+                   projections, then fprop, dgrad and wgrad MXFP8 GEMMs;
+    32x32 variant: the same with the weights quantised in 32x32 tiles (one
+                   shared FP8 weight; fprop and the transposed-read dgrad use
+                   tile scales), same seeds;
+  MoE experts, 131072 routed tokens over 64 experts (Zipf(1.1) sizes):
+    1x32 quantisation of tokens and expert weights, then the grouped
+    gate_up (4096 -> 4096) and down (2048 -> 4096) MXFP8 GEMMs.
+
+Inputs are generated on the GPU and resident in HBM before timing; outputs
+are preallocated.  `value` = GEMM FLOP of the step / step time (TFLOP/s).
+Per-kernel times come from HIP events on the launch stream.  Prints one JSON
+line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MXFP8 GEMM TFLOP/s (% FP8 MFMA peak) + quant GB/s (% HBM peak), 1 GPU"
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--layers", type=int, default=4)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="rough budget for the oracle sample")
+    return p.parse_args()
+
+
+class Launcher:
+    """Runs C-ABI calls on torch's current stream, optionally bracketing each
+    with HIP events (torch.cuda.Event records on the same stream)."""
+
+    def __init__(self, torch, mx):
+        self.torch, self.mx = torch, mx
+        self.stream = torch.cuda.current_stream().cuda_stream
+        self.record = False
+        self.events = []   # (kind, work, unit, start, end)
+
+    def _wrap(self, kind, work, unit, fn):
+        if self.record:
+            s = self.torch.cuda.Event(enable_timing=True)
+            e = self.torch.cuda.Event(enable_timing=True)
+            s.record()
+            st = fn()
+            e.record()
+            self.events.append((kind, work, unit, s, e))
+        else:
+            st = fn()
+        if st != 0:
+            raise RuntimeError(f"{kind}: status {st}: {self.mx.mx_last_error()}")
+
+    def quant(self, kind, mode, x, outs):
+        mx = self.mx
+        R, C = x.shape
+        q, s, qt, st = outs
+        nbytes = {0: 2 + 1 + 1 / 32, 1: 2 + 1 + 1 / 32, 2: 2 + 2 + 2 / 32,
+                  3: 2 + 1 + 1 / 1024}[mode] * R * C
+        self._wrap(kind, nbytes, "B", lambda: mx.mx_quant(
+            mode, x.data_ptr(), R, C, _p(q), _p(s), _p(qt), _p(st), self.stream))
+
+    def gemm(self, kind, layout, bkind, M, N, K, a, sa, b, sb, c):
+        mx = self.mx
+        self._wrap(kind, 2.0 * M * N * K, "FLOP", lambda: mx.mx_gemm(
+            layout, bkind, M, N, K, a.data_ptr(), sa.data_ptr(), b.data_ptr(), sb.data_ptr(),
+            c.data_ptr(), self.stream))
+
+    def grouped(self, kind, G, offs, T, N, K, a, sa, b, sb, c, flops):
+        mx = self.mx
+        self._wrap(kind, flops, "FLOP", lambda: mx.mx_grouped_gemm(
+            G, offs.data_ptr(), T, N, K, a.data_ptr(), sa.data_ptr(), b.data_ptr(),
+            sb.data_ptr(), c.data_ptr(), self.stream))
+
+
+def _p(t):
+    return 0 if t is None else t.data_ptr()
+
+
+def build_workload(torch, W, layers):
+    dev = "cuda"
+    u8, bf = torch.uint8, torch.bfloat16
+    stack = [W.stack_layer(l, dev) for l in range(layers)]
+    T, H = stack[0]["X_up"].shape
+    F = stack[0]["W_up"].shape[0]
+
+    def dual_out(R, C):
+        return (torch.empty((R, C), dtype=u8, device=dev), torch.empty((R, C // 32), dtype=u8, device=dev),
+                torch.empty((C, R), dtype=u8, device=dev), torch.empty((C, R // 32), dtype=u8, device=dev))
+
+    def tile_out(R, C):
+        return (torch.empty((R, C), dtype=u8, device=dev),
+                torch.empty((R // 32, C // 32), dtype=u8, device=dev), None, None)
+
+    bufs = {
+        "X_up": dual_out(T, H), "X_dn": dual_out(T, F), "dY_up": dual_out(T, F),
+        "dY_dn": dual_out(T, H), "W_up": dual_out(F, H), "W_dn": dual_out(H, F),
+        "W_up32": tile_out(F, H), "W_dn32": tile_out(H, F),
+        "Y_up": torch.empty((T, F), dtype=bf, device=dev),
+        "dX_up": torch.empty((T, H), dtype=bf, device=dev),
+        "dW_up": torch.empty((F, H), dtype=bf, device=dev),
+        "Y_dn": torch.empty((T, H), dtype=bf, device=dev),
+        "dX_dn": torch.empty((T, F), dtype=bf, device=dev),
+        "dW_dn": torch.empty((H, F), dtype=bf, device=dev),
+    }
+    moe = W.moe(dev)
+    off = moe["offsets"]
+    Tm = int(off[-1])
+    G, Ngu, Hm = moe["W_gu"].shape
+    _, Ndn, Fm = moe["W_dn"].shape
+    row = lambda R, C: (torch.empty((R, C), dtype=u8, device=dev),
+                        torch.empty((R, C // 32), dtype=u8, device=dev), None, None)
+    moe_bufs = {
+        "offs": torch.from_numpy(off).to(dev),
+        "X": row(Tm, Hm), "H": row(Tm, Fm), "W_gu": row(G * Ngu, Hm), "W_dn": row(G * Ndn, Fm),
+        "Y_gu": torch.empty((Tm, Ngu), dtype=bf, device=dev),
+        "Y_dn": torch.empty((Tm, Ndn), dtype=bf, device=dev),
+    }
+    dims = dict(T=T, H=H, F=F, Tm=Tm, G=G, Ngu=Ngu, Hm=Hm, Ndn=Ndn, Fm=Fm)
+    return stack, bufs, moe, moe_bufs, dims
+
+
+def run_step(L, stack, b, moe, mb, d):
+    T, H, F = d["T"], d["H"], d["F"]
+    FP, DG, WG = 0, 1, 2
+    B1, B32 = 0, 1
+    for variant in ("1x32", "32x32"):
+        for t in stack:
+            # activations and gradients: dual-axis (forward row + backward column copies)
+            L.quant("quant_dual", 2, t["X_up"], b["X_up"])
+            L.quant("quant_dual", 2, t["dY_up"], b["dY_up"])
+            L.quant("quant_dual", 2, t["X_dn"], b["X_dn"])
+            L.quant("quant_dual", 2, t["dY_dn"], b["dY_dn"])
+            qx, sx, qxt, sxt = b["X_up"]
+            qd, sd, qdt, sdt = b["dY_up"]
+            qx2, sx2, qxt2, sxt2 = b["X_dn"]
+            qd2, sd2, qdt2, sdt2 = b["dY_dn"]
+            if variant == "1x32":
+                L.quant("quant_dual", 2, t["W_up"], b["W_up"])
+                L.quant("quant_dual", 2, t["W_dn"], b["W_dn"])
+                qw, sw, qwt, swt = b["W_up"]
+                qw2, sw2, qwt2, swt2 = b["W_dn"]
+                L.gemm("gemm", FP, B1, T, F, H, qx, sx, qw, sw, b["Y_up"])
+                L.gemm("gemm", DG, B1, T, H, F, qd, sd, qwt, swt, b["dX_up"])
+                L.gemm("gemm", FP, B1, T, H, F, qx2, sx2, qw2, sw2, b["Y_dn"])
+                L.gemm("gemm", DG, B1, T, F, H, qd2, sd2, qwt2, swt2, b["dX_dn"])
+            else:
+                L.quant("quant_32x32", 3, t["W_up"], b["W_up32"])
+                L.quant("quant_32x32", 3, t["W_dn"], b["W_dn32"])
+                qw, sw = b["W_up32"][:2]
+                qw2, sw2 = b["W_dn32"][:2]
+                L.gemm("gemm_32x32", FP, B32, T, F, H, qx, sx, qw, sw, b["Y_up"])
+                L.gemm("gemm_32x32_dgrad", DG, B32, T, H, F, qd, sd, qw, sw, b["dX_up"])
+                L.gemm("gemm_32x32", FP, B32, T, H, F, qx2, sx2, qw2, sw2, b["Y_dn"])
+                L.gemm("gemm_32x32_dgrad", DG, B32, T, F, H, qd2, sd2, qw2, sw2, b["dX_dn"])
+            L.gemm("gemm", WG, B1, F, H, T, qdt, sdt, qxt, sxt, b["dW_up"])
+            L.gemm("gemm", WG, B1, H, F, T, qdt2, sdt2, qxt2, sxt2, b["dW_dn"])
+    # MoE experts
+    G, Tm = d["G"], d["Tm"]
+    L.quant("quant_row", 0, moe["X"], mb["X"])
+    L.quant("quant_row", 0, moe["H"], mb["H"])
+    L.quant("quant_row", 0, moe["W_gu"].reshape(-1, d["Hm"]), mb["W_gu"])
+    L.quant("quant_row", 0, moe["W_dn"].reshape(-1, d["Fm"]), mb["W_dn"])
+    qa, sa = mb["X"][:2]
+    qw, sw = mb["W_gu"][:2]
+    L.grouped("grouped_gemm", G, mb["offs"], Tm, d["Ngu"], d["Hm"], qa, sa, qw, sw, mb["Y_gu"],
+              2.0 * Tm * d["Ngu"] * d["Hm"])
+    qa, sa = mb["H"][:2]
+    qw, sw = mb["W_dn"][:2]
+    L.grouped("grouped_gemm", G, mb["offs"], Tm, d["Ndn"], d["Fm"], qa, sa, qw, sw, mb["Y_dn"],
+              2.0 * Tm * d["Ndn"] * d["Fm"])
+
+
+def cpu_baseline(W, x_dev, w_dev, budget_s):
+    """The oracle (untuned) on a bounded sample of the step: dual-axis
+    quantisation of the first 64 token rows of the up-projection input and
+    of leading rows of its weight (the same bytes the GPU step uses), then
+    the binary64 GEMM of those rows (the up-projection fprop, K = hidden)."""
+    import numpy as np
+    import oracle
+    oracle.lib()
+    nthreads = oracle.num_threads()
+    xb = W.bf16_bits(x_dev[:64])
+    wb = W.bf16_bits(w_dev[:2048])
+    H = xb.shape[1]
+    # calibrate on 256 weight rows, then size the sample to the budget
+    t0 = time.perf_counter()
+    qa, sa = oracle.quant_row(xb)
+    qb, sb = oracle.quant_row(wb[:256])
+    oracle.gemm(qa, sa, qb, sb)
+    dt = time.perf_counter() - t0
+    ncols = int(min(wb.shape[0], max(256, 256 * budget_s / max(dt, 1e-3))))
+    ncols = (ncols // 32) * 32
+    t0 = time.perf_counter()
+    qa, sa, _, _ = oracle.quant_dual(np.ascontiguousarray(xb))
+    qb, sb, _, _ = oracle.quant_dual(np.ascontiguousarray(wb[:ncols]))
+    oracle.gemm(qa, sa, qb, sb)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * qa.shape[0] * ncols * H
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": nthreads,
+            "kind": "oracle",
+            "sample": f"dual-axis quantisation of {qa.shape[0]} token rows and {ncols} weight rows "
+                      f"(K={H}) of the up projection, then the binary64 GEMM of the "
+                      f"{qa.shape[0]}x{ncols} fprop outputs; {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import mxfp8_microscaled_precision_amd as mx
+    from mxfp8_microscaled_precision_amd import workloads as W
+    torch.cuda.set_device(0)
+    st = mx.mx_device_check(0)
+    if st != 0:
+        raise SystemExit(f"device check failed: {mx.mx_last_error()}")
+    print("[bench] generating inputs", file=sys.stderr, flush=True)
+    stack, bufs, moe, mbufs, d = build_workload(torch, W, args.layers)
+    torch.cuda.synchronize()
+    L = Launcher(torch, mx)
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        run_step(L, stack, bufs, moe, mbufs, d)
+    torch.cuda.synchronize()
+    # timed region: K steps, HIP events around every launch on the launch
+    # stream (the same stream as torch's current stream)
+    print("[bench] timing", file=sys.stderr, flush=True)
+    L.record = True
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        run_step(L, stack, bufs, moe, mbufs, d)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    per = {}
+    for kind, work, unit, s, e in L.events:
+        ms = s.elapsed_time(e)
+        k = per.setdefault(kind, {"ms": 0.0, "work": 0.0, "unit": unit, "launches": 0})
+        k["ms"] += ms
+        k["work"] += work
+        k["launches"] += 1
+    reps = args.steps
+    kernels = {}
+    for kind, k in per.items():
+        rate = k["work"] / (k["ms"] * 1e-3)
+        if k["unit"] == "FLOP":
+            kernels[kind] = {"tflops": rate / 1e12, "frac_peak": rate / 1e12 / PEAK_FP8_TFLOPS,
+                             "ms_per_step": k["ms"] / reps, "launches_per_step": k["launches"] // reps}
+        else:
+            kernels[kind] = {"gbps": rate / 1e9, "frac_peak": rate / 1e9 / PEAK_HBM_GBPS,
+                             "ms_per_step": k["ms"] / reps, "launches_per_step": k["launches"] // reps}
+    gemm_flop = sum(k["work"] for k in per.values() if k["unit"] == "FLOP") / reps
+    quant_bytes = sum(k["work"] for k in per.values() if k["unit"] == "B") / reps
+    quant_ms = sum(k["ms"] for k in per.values() if k["unit"] == "B") / reps
+    value = gemm_flop / (ms_step * 1e-3) / 1e12
+    g = per["gemm"]
+    g_rate = g["work"] / (g["ms"] * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"MXFP8 linear stack, {args.layers} layers {d['H']}->{d['F']}->{d['H']} at "
+                         f"{d['T']} tokens, 1x32 dual-axis and 32x32-weight variants "
+                         f"(quantise + fprop/dgrad/wgrad) + MoE grouped gate_up/down over "
+                         f"{d['Tm']} routed tokens, {d['G']} experts"),
+            "tokens": d["T"], "hidden": d["H"], "ffn": d["F"], "layers": args.layers,
+            "moe_tokens": d["Tm"], "experts": d["G"],
+            "gemm_tflop_per_step": round(gemm_flop / 1e12, 3),
+            "quant_gb_per_step": round(quant_bytes / 1e9, 3),
+        },
+        "roofline": {
+            "bound": "mfma", "achieved": round(g_rate, 2), "peak": PEAK_FP8_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(g_rate / PEAK_FP8_TFLOPS, 4), "traffic": None,
+            "kernel": "gemm_kernel<B_ROW> (1x32 fprop/dgrad/wgrad)",
+        },
+        "quant": {"gbps": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
+                  "frac_hbm_peak": round(quant_bytes / (quant_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                  "ms_per_step": round(quant_ms, 3)},
+        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in kernels.items()},
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(W, stack[0]["X_up"], stack[0]["W_up"], args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,148 @@
+/*
+ * mxfp8.h -- C ABI of the MXFP8 microscaled-precision hot path on MI355X
+ * (gfx950): dynamic MX quantisation of BF16 tensors and the MXFP8 GEMMs that
+ * consume the quantised operands and restore a BF16 result.
+ *
+ * Formats (OCP MX / OFP8, named by the pages, defined by OCP):
+ *   BF16   input elements (IEEE binary32 upper half), subnormals honoured.
+ *   E4M3   payload byte, bias 7, largest finite 448, 0x7F/0xFF = NaN.
+ *   E8M0   scale byte b = 2^(b-127), 0xFF = NaN.
+ *
+ * Conventions for every call:
+ *   - Pointers named x, q, s, q_t, s_t, a, sa, b, sb, c, offsets are DEVICE
+ *     pointers owned by the caller; the library never allocates, frees or
+ *     retains them beyond the completion of the work it enqueued.
+ *   - All work is enqueued asynchronously on `stream` (0 = the null stream)
+ *     of the current device; results are visible after the stream syncs.
+ *   - Arguments are validated on the host before anything is launched; on a
+ *     non-zero status nothing was launched and no output was touched.
+ *     Validation errors mirror the ValueError the pages raise for an
+ *     unsupported block size or recipe (MindSpeed RFC "add MXFP8-32x32
+ *     quantisation support to FSDP", sections 3.4 and 3.5.2.1).
+ *   - The current device must be gfx950; otherwise calls return
+ *     MX_ERR_UNSUPPORTED_DEVICE (the pages' init-time hardware gate:
+ *     torchtitan-npu MXFP8/HiF8 tutorial, "hardware requirement").
+ *   - No exception crosses the ABI; the last error detail of the calling
+ *     thread is available from mx_last_error().
+ */
+#ifndef MXFP8_H
+#define MXFP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mx_status {
+    MX_OK = 0,
+    MX_ERR_INVALID_ARG = 1,        /* null pointer, negative size, unknown enum value */
+    MX_ERR_UNSUPPORTED_SHAPE = 2,  /* a dimension the mode's block size does not divide */
+    MX_ERR_UNSUPPORTED_DEVICE = 3, /* the current device is not gfx950 */
+    MX_ERR_HIP = 4                 /* a HIP runtime call failed (see mx_last_error) */
+} mx_status;
+
+/* Quantisation modes.  "1x32" is the MX block of 32 consecutive elements
+ * sharing one E8M0 scale (torchtitan-npu MXFP8/HiF8 tutorial, "MXFP8 / HiF8
+ * architecture overview", MXFP8 bullet); dual-axis quantises the same tensor
+ * along both axes in one pass (tutorial, step-2 environment table,
+ * MXFP8_DUAL_AXIS_FORWARD; RFC section 3.3.3); 32x32 is block size
+ * [1,32,32]: one scale per 32x32 weight tile, one FP8 weight shared by
+ * forward and backward (RFC sections 1.1, 3.1, 3.3.3). */
+typedef enum mx_quant_mode {
+    MX_QUANT_ROW_1x32 = 0,   /* blocks of 32 along each row (the last, contiguous dim) */
+    MX_QUANT_COL_1x32 = 1,   /* blocks of 32 down each column, written transposed */
+    MX_QUANT_DUAL_AXIS = 2,  /* ROW and COL outputs from one read of x */
+    MX_QUANT_BLOCK_32x32 = 3 /* one scale per 32x32 tile */
+} mx_quant_mode;
+
+/* Which product of a linear layer a GEMM call computes (operand roles). */
+typedef enum mx_gemm_layout {
+    MX_GEMM_FPROP = 0, /* Y  = X  * W^T : a = X rows,     b = W rows            */
+    MX_GEMM_DGRAD = 1, /* dX = dY * W   : a = dY rows,    b = W columns (W_col_T) */
+    MX_GEMM_WGRAD = 2  /* dW = dY^T * X : a = dY columns, b = X columns          */
+} mx_gemm_layout;
+
+/* Granularity of the B operand's scales. */
+typedef enum mx_bscale_kind {
+    MX_BSCALE_1x32 = 0, /* one scale per 32 K-elements of each B row */
+    MX_BSCALE_32x32 = 1 /* one scale per 32x32 tile of a 32x32-quantised weight */
+} mx_bscale_kind;
+
+/* MX_OK iff `device` is a gfx950 GPU.  MX_ERR_UNSUPPORTED_DEVICE for another
+ * architecture, MX_ERR_HIP if the device cannot be queried. */
+mx_status mx_device_check(int device);
+
+/* 1 iff a HIP architecture name (e.g. "gfx950:sramecc+:xnack-") denotes a
+ * device this library runs on.  Pure host function, no HIP call. */
+int mx_arch_supported(const char* gcn_arch_name);
+
+/* Static description of a status code.  Never NULL. */
+const char* mx_status_string(mx_status s);
+
+/* Detail of the last failing call on this thread ("" if none).  Never NULL;
+ * valid until the next call on this thread. */
+const char* mx_last_error(void);
+
+/* Dynamic MX quantisation of x, BF16 [rows, cols] row-major, to E4M3 payload
+ * bytes and E8M0 scale bytes.  The scale exponent of a block is the smallest
+ * e with amax <= 448 * 2^e (the "rceil" rule), clamped to [-127, 127]; each
+ * element is divided by 2^e and rounded to nearest-even into E4M3 (the
+ * tutorial's step-3 log names the recipe mxfp8_rceil; RFC section 3.3.1 fixes
+ * the element type to E4M3).  An all-zero block gets scale 0x00; a block
+ * holding NaN or Inf gets scale 0xFF and payload 0x7F.
+ *
+ * Outputs by mode (all row-major, uint8):
+ *   ROW_1x32:    q [rows, cols],  s [rows, cols/32]          needs cols % 32 == 0
+ *   COL_1x32:    q_t [cols, rows], s_t [cols, rows/32]       needs both % 32 == 0
+ *                (q_t[c][r] quantises x[r][c] with the block x[32i..32i+31][c])
+ *   DUAL_AXIS:   q, s, q_t, s_t as above, one read of x      needs both % 32 == 0
+ *   BLOCK_32x32: q [rows, cols], s [rows/32, cols/32]        needs both % 32 == 0
+ *                (s is both the forward and the backward scale: the forward
+ *                 view blocks K along cols, the backward view along rows)
+ * Unused output pointers may be NULL.  rows == 0 or cols == 0 is a no-op. */
+mx_status mx_quant(mx_quant_mode mode, const void* x, int64_t rows, int64_t cols, void* q, void* s,
+                   void* q_t, void* s_t, hipStream_t stream);
+
+/* MXFP8 GEMM C = A * B^T with FP32 accumulation and a BF16 result.
+ *   a:  E4M3 [M, K] row-major, sa: E8M0 [M, K/32]
+ *   b/sb by (layout, bkind):
+ *     any layout, MX_BSCALE_1x32:   b [N, K], sb [N, K/32]      ("TN": both K-contiguous)
+ *     MX_GEMM_FPROP, MX_BSCALE_32x32: b [N, K], sb tiles [N/32, K/32]
+ *     MX_GEMM_DGRAD, MX_BSCALE_32x32: b [K, N] -- the one shared FP8 weight
+ *         [out = K, in = N] -- contracted over its rows, sb tiles [K/32, N/32]
+ *     MX_GEMM_WGRAD, MX_BSCALE_32x32: invalid (the weight-gradient product
+ *         has no weight operand)
+ *   c:  BF16 [M, N] row-major.
+ * C[m][n] = sum_k E4M3(a[m][k]) 2^(sa[m][k/32]-127) * E4M3(B[n][k]) 2^(sB-127).
+ * Requires K % 32 == 0 (and N % 32 == 0 for 32x32 scales).  K == 0 writes
+ * zeros; M == 0 or N == 0 is a no-op. */
+mx_status mx_gemm(mx_gemm_layout layout, mx_bscale_kind bkind, int64_t M, int64_t N, int64_t K,
+                  const void* a, const void* sa, const void* b, const void* sb, void* c,
+                  hipStream_t stream);
+
+/* MoE grouped MXFP8 GEMM over per-expert token groups (tutorial, "MXFP8 /
+ * HiF8 architecture overview": MoE expert layers run as grouped matmul; RFC
+ * section 2.2, gate_up_proj / down_proj).
+ *   offsets: DEVICE int64 [G+1], offsets[0] = 0, offsets[G] = T,
+ *            non-decreasing; rows offsets[g] .. offsets[g+1]-1 of a belong
+ *            to expert g (groups may be empty, sizes need not be multiples
+ *            of 32).  Offsets are read on the device and trusted; values
+ *            outside [0, T] are clamped and a decrease is treated as an empty
+ *            group, so bad offsets give wrong rows but never a bad access.
+ *   a: E4M3 [T, K], sa [T, K/32];  b: E4M3 [G, N, K], sb [G, N, K/32]
+ *   c: BF16 [T, N]; row r of expert g is  c[r] = a[r] * b[g]^T.
+ * Requires K % 32 == 0 and 1 <= G <= 512.  T == 0 or N == 0 is a no-op.
+ * Needs no workspace. */
+mx_status mx_grouped_gemm(int64_t G, const int64_t* offsets, int64_t T, int64_t N, int64_t K,
+                          const void* a, const void* sa, const void* b, const void* sb, void* c,
+                          hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFP8_H */

@@ -1,1 +1,230 @@
-"""MXFP8 microscaled-precision hot path for MI355X (gfx950)."""
+"""MXFP8 microscaled-precision hot path for MI355X (gfx950).
+
+Thin Python binding over the C ABI in ``include/mxfp8.h`` (``libmxfp8.so``,
+built in-tree by ``python -m mxfp8_microscaled_precision_amd.build``).  The
+functions named ``mx_*`` take raw device pointers and sizes exactly like the C
+entry points; ``quant``, ``gemm``, ``grouped_gemm`` and
+``process_quant_result`` marshal torch CUDA tensors (device memory and the
+current stream only) into those calls.  Every step of the computation runs in
+the HIP kernels; there is no CPU fallback: without the built library, or on a
+device other than gfx950, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "MXError", "lib", "mx_device_check", "mx_arch_supported", "mx_status_string",
+    "mx_last_error", "mx_quant", "mx_gemm", "mx_grouped_gemm", "quant", "gemm",
+    "grouped_gemm", "process_quant_result", "QUANT_MODES", "GEMM_LAYOUTS", "BSCALE_KINDS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxfp8.so")
+
+MX_OK = 0
+QUANT_MODES = {"row": 0, "col": 1, "dual": 2, "32x32": 3}
+GEMM_LAYOUTS = {"fprop": 0, "dgrad": 1, "wgrad": 2}
+BSCALE_KINDS = {"1x32": 0, "32x32": 1}
+
+
+class MXError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{mx_status_string(status)} (status {status}): {detail}")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmxfp8.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m mxfp8_microscaled_precision_amd.build` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, vp, c_int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        L.mx_device_check.restype = c_int
+        L.mx_device_check.argtypes = [c_int]
+        L.mx_arch_supported.restype = c_int
+        L.mx_arch_supported.argtypes = [ctypes.c_char_p]
+        L.mx_status_string.restype = ctypes.c_char_p
+        L.mx_status_string.argtypes = [c_int]
+        L.mx_last_error.restype = ctypes.c_char_p
+        L.mx_last_error.argtypes = []
+        L.mx_quant.restype = c_int
+        L.mx_quant.argtypes = [c_int, vp, i64, i64, vp, vp, vp, vp, vp]
+        L.mx_gemm.restype = c_int
+        L.mx_gemm.argtypes = [c_int, c_int, i64, i64, i64, vp, vp, vp, vp, vp, vp]
+        L.mx_grouped_gemm.restype = c_int
+        L.mx_grouped_gemm.argtypes = [i64, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp]
+        _lib = L
+    return _lib
+
+
+# ---------------------------------------------------------------------------
+# The C entry points, same names and arguments (raw pointers as ints)
+# ---------------------------------------------------------------------------
+
+def mx_device_check(device: int) -> int:
+    return lib().mx_device_check(device)
+
+
+def mx_arch_supported(name: str) -> int:
+    return lib().mx_arch_supported(name.encode() if name is not None else None)
+
+
+def mx_status_string(status: int) -> str:
+    return lib().mx_status_string(status).decode()
+
+
+def mx_last_error() -> str:
+    return lib().mx_last_error().decode()
+
+
+def mx_quant(mode, x, rows, cols, q, s, q_t, s_t, stream) -> int:
+    return lib().mx_quant(mode, x, rows, cols, q, s, q_t, s_t, stream)
+
+
+def mx_gemm(layout, bkind, M, N, K, a, sa, b, sb, c, stream) -> int:
+    return lib().mx_gemm(layout, bkind, M, N, K, a, sa, b, sb, c, stream)
+
+
+def mx_grouped_gemm(G, offsets, T, N, K, a, sa, b, sb, c, stream) -> int:
+    return lib().mx_grouped_gemm(G, offsets, T, N, K, a, sa, b, sb, c, stream)
+
+
+def _check(status: int):
+    if status != MX_OK:
+        raise MXError(status, mx_last_error())
+
+
+# ---------------------------------------------------------------------------
+# torch marshalling
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device):
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need(t, dtype, name, ndim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+
+
+def quant(x, mode: str = "row"):
+    """Dynamic MX quantisation of a BF16 [rows, cols] tensor.
+
+    mode "row"   -> (q [rows,cols], s [rows,cols/32])
+         "col"   -> (q_t [cols,rows], s_t [cols,rows/32])
+         "dual"  -> (q, s, q_t, s_t)
+         "32x32" -> (q [rows,cols], s [rows/32,cols/32])
+    Payloads are uint8 E4M3 bytes, scales uint8 E8M0 bytes.
+    """
+    torch = _torch()
+    if mode not in QUANT_MODES:
+        raise ValueError(f"unknown quantisation mode {mode!r}; expected one of {list(QUANT_MODES)}")
+    _need(x, torch.bfloat16, "x", 2)
+    R, C = x.shape
+    dev, u8 = x.device, torch.uint8
+    q = s = qt = st = None
+    if mode in ("row", "dual", "32x32"):
+        q = torch.empty((R, C), dtype=u8, device=dev)
+        s = torch.empty((R // 32, C // 32) if mode == "32x32" else (R, C // 32), dtype=u8, device=dev)
+    if mode in ("col", "dual"):
+        qt = torch.empty((C, R), dtype=u8, device=dev)
+        st = torch.empty((C, R // 32), dtype=u8, device=dev)
+    _check(mx_quant(QUANT_MODES[mode], _ptr(x), R, C, _ptr(q), _ptr(s), _ptr(qt), _ptr(st),
+                    _stream(dev)))
+    if mode == "row" or mode == "32x32":
+        return q, s
+    if mode == "col":
+        return qt, st
+    return q, s, qt, st
+
+
+def gemm(a, sa, b, sb, layout: str = "fprop", bscale: str = "1x32", out=None):
+    """MXFP8 GEMM C = A * B^T (FP32 accumulation, BF16 result).
+
+    a [M,K] u8 + sa [M,K/32]; b [N,K] u8 + sb [N,K/32] for 1x32 scales;
+    with bscale "32x32": fprop b [N,K] + tiles [N/32,K/32], dgrad b [K,N]
+    (the shared weight, contracted over rows) + tiles [K/32,N/32].
+    """
+    torch = _torch()
+    if layout not in GEMM_LAYOUTS or bscale not in BSCALE_KINDS:
+        raise ValueError(f"unknown layout {layout!r} or B scale kind {bscale!r}")
+    for t, n in ((a, "a"), (sa, "sa"), (b, "b"), (sb, "sb")):
+        _need(t, torch.uint8, n, 2)
+    M, K = a.shape
+    N = b.shape[1] if (bscale == "32x32" and layout == "dgrad") else b.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    _need(out, torch.bfloat16, "out", 2)
+    if tuple(out.shape) != (M, N):
+        raise ValueError(f"out must be [{M}, {N}]")
+    _check(mx_gemm(GEMM_LAYOUTS[layout], BSCALE_KINDS[bscale], M, N, K, _ptr(a), _ptr(sa), _ptr(b),
+                   _ptr(sb), _ptr(out), _stream(a.device)))
+    return out
+
+
+def grouped_gemm(offsets, a, sa, b, sb, out=None):
+    """MoE grouped MXFP8 GEMM: rows offsets[g]:offsets[g+1] of a times b[g]^T.
+
+    offsets int64 [G+1] on the device; a [T,K] u8 + sa [T,K/32];
+    b [G,N,K] u8 + sb [G,N,K/32]; returns BF16 [T,N].
+    """
+    torch = _torch()
+    _need(offsets, torch.int64, "offsets", 1)
+    for t, n in ((a, "a"), (sa, "sa")):
+        _need(t, torch.uint8, n, 2)
+    for t, n in ((b, "b"), (sb, "sb")):
+        _need(t, torch.uint8, n, 3)
+    G = offsets.numel() - 1
+    T, K = a.shape
+    N = b.shape[1]
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.bfloat16, device=a.device)
+    _need(out, torch.bfloat16, "out", 2)
+    _check(mx_grouped_gemm(G, _ptr(offsets), T, N, K, _ptr(a), _ptr(sa), _ptr(b), _ptr(sb),
+                           _ptr(out), _stream(a.device)))
+    return out
+
+
+def process_quant_result(weight, recipe: str = "mxfp8"):
+    """Quantise a weight for both passes, in the RFC's tuple order
+    (weight_fwd, scale_fwd, weight_bwd, scale_bwd).
+
+    "mxfp8"       -> dual-axis 1x32: two FP8 copies, row and column scales.
+    "mxfp8-32x32" -> 32x32 tiles: weight_bwd IS weight_fwd and the one tile
+                     scale array serves both passes (forward blocks K along
+                     the columns, backward along the rows).
+    (MindSpeed RFC "add MXFP8-32x32 quantisation support to FSDP", sections
+    3.3.3 and 3.5.2.3; an unsupported recipe raises ValueError.)
+    """
+    if recipe == "mxfp8":
+        q, s, qt, st = quant(weight, "dual")
+        return q, s, qt, st
+    if recipe == "mxfp8-32x32":
+        q, s = quant(weight, "32x32")
+        return q, s, q, s
+    raise ValueError(f"unsupported recipe {recipe!r}: expected 'mxfp8' or 'mxfp8-32x32'")

@@ -1,0 +1,198 @@
+// Host side of the C ABI declared in include/mxfp8.h: argument validation
+// (before any HIP call), the gfx950 gate, and dispatch to the kernels.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/mxfp8.h"
+#include "mx_kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+mx_status fail(mx_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+mx_status hip_fail(hipError_t e, const char* what) {
+  return fail(MX_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_mu;
+int g_arch_ok[MAX_DEVICES];  // 0 unknown, 1 gfx950, 2 other
+int g_num_cus[MAX_DEVICES];
+
+mx_status check_device(int dev) {
+  if (dev < 0 || dev >= MAX_DEVICES) return fail(MX_ERR_INVALID_ARG, "device %d out of range", dev);
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (g_arch_ok[dev] == 1) return MX_OK;
+    if (g_arch_ok[dev] == 2)
+      return fail(MX_ERR_UNSUPPORTED_DEVICE, "MXFP8 kernels need a gfx950 (MI355X) device");
+  }
+  hipDeviceProp_t prop;
+  hipError_t e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+  const bool ok = mx_arch_supported(prop.gcnArchName) != 0;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_arch_ok[dev] = ok ? 1 : 2;
+    g_num_cus[dev] = prop.multiProcessorCount;
+  }
+  if (!ok)
+    return fail(MX_ERR_UNSUPPORTED_DEVICE, "MXFP8 kernels need a gfx950 (MI355X) device, found %s",
+                prop.gcnArchName);
+  return MX_OK;
+}
+
+mx_status current_device(int* dev) {
+  hipError_t e = hipGetDevice(dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  return check_device(*dev);
+}
+
+bool mul_overflows(int64_t a, int64_t b) { return a != 0 && b > INT64_MAX / a; }
+
+}  // namespace
+
+extern "C" {
+
+int mx_arch_supported(const char* name) {
+  if (!name) return 0;
+  // "gfx950" optionally followed by target features (":sramecc+:xnack-")
+  return std::strncmp(name, "gfx950", 6) == 0 && (name[6] == '\0' || name[6] == ':');
+}
+
+const char* mx_status_string(mx_status s) {
+  switch (s) {
+    case MX_OK: return "success";
+    case MX_ERR_INVALID_ARG: return "invalid argument";
+    case MX_ERR_UNSUPPORTED_SHAPE: return "unsupported shape for the MX block size";
+    case MX_ERR_UNSUPPORTED_DEVICE: return "MXFP8 is only supported on gfx950 (MI355X)";
+    case MX_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* mx_last_error(void) { return g_err; }
+
+mx_status mx_device_check(int device) {
+  g_err[0] = '\0';
+  int n = 0;
+  hipError_t e = hipGetDeviceCount(&n);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceCount");
+  if (device < 0 || device >= n) return fail(MX_ERR_INVALID_ARG, "no device %d (count %d)", device, n);
+  return check_device(device);
+}
+
+mx_status mx_quant(mx_quant_mode mode, const void* x, int64_t rows, int64_t cols, void* q, void* s,
+                   void* q_t, void* s_t, hipStream_t stream) {
+  g_err[0] = '\0';
+  if (mode < MX_QUANT_ROW_1x32 || mode > MX_QUANT_BLOCK_32x32)
+    return fail(MX_ERR_INVALID_ARG, "unknown quantisation mode %d", (int)mode);
+  if (rows < 0 || cols < 0) return fail(MX_ERR_INVALID_ARG, "negative shape [%lld, %lld]",
+                                        (long long)rows, (long long)cols);
+  if (mul_overflows(rows, cols) || (rows * cols) > (INT64_MAX / 4))
+    return fail(MX_ERR_INVALID_ARG, "shape too large");
+  const bool need_row = mode == MX_QUANT_ROW_1x32 || mode == MX_QUANT_DUAL_AXIS ||
+                        mode == MX_QUANT_BLOCK_32x32;
+  const bool need_col = mode == MX_QUANT_COL_1x32 || mode == MX_QUANT_DUAL_AXIS;
+  // every mode tiles the columns by 32; all but ROW block or tile the rows by 32
+  if (cols % 32 != 0)
+    return fail(MX_ERR_UNSUPPORTED_SHAPE, "cols %lld is not a multiple of 32", (long long)cols);
+  if (mode != MX_QUANT_ROW_1x32 && rows % 32 != 0)
+    return fail(MX_ERR_UNSUPPORTED_SHAPE, "rows %lld is not a multiple of 32", (long long)rows);
+  if (rows == 0 || cols == 0) return MX_OK;
+  if (!x) return fail(MX_ERR_INVALID_ARG, "x is NULL");
+  if (need_row && (!q || !s)) return fail(MX_ERR_INVALID_ARG, "q and s are required for this mode");
+  if (need_col && (!q_t || !s_t))
+    return fail(MX_ERR_INVALID_ARG, "q_t and s_t are required for this mode");
+  int dev;
+  mx_status st = current_device(&dev);
+  if (st != MX_OK) return st;
+  hipError_t e;
+  switch (mode) {
+    case MX_QUANT_ROW_1x32: e = mx::launch_quant_row(x, rows * cols, q, s, stream); break;
+    case MX_QUANT_COL_1x32: e = mx::launch_quant_tile(1, x, rows, cols, q, s, q_t, s_t, stream); break;
+    case MX_QUANT_DUAL_AXIS: e = mx::launch_quant_tile(2, x, rows, cols, q, s, q_t, s_t, stream); break;
+    default: e = mx::launch_quant_tile(3, x, rows, cols, q, s, q_t, s_t, stream); break;
+  }
+  if (e != hipSuccess) return hip_fail(e, "quantisation kernel launch");
+  return MX_OK;
+}
+
+mx_status mx_gemm(mx_gemm_layout layout, mx_bscale_kind bkind, int64_t M, int64_t N, int64_t K,
+                  const void* a, const void* sa, const void* b, const void* sb, void* c,
+                  hipStream_t stream) {
+  g_err[0] = '\0';
+  if (layout < MX_GEMM_FPROP || layout > MX_GEMM_WGRAD)
+    return fail(MX_ERR_INVALID_ARG, "unknown GEMM layout %d", (int)layout);
+  if (bkind != MX_BSCALE_1x32 && bkind != MX_BSCALE_32x32)
+    return fail(MX_ERR_INVALID_ARG, "unknown B scale kind %d", (int)bkind);
+  if (bkind == MX_BSCALE_32x32 && layout == MX_GEMM_WGRAD)
+    return fail(MX_ERR_INVALID_ARG, "the weight-gradient GEMM has no 32x32 weight operand");
+  if (M < 0 || N < 0 || K < 0) return fail(MX_ERR_INVALID_ARG, "negative GEMM shape");
+  if (mul_overflows(M, K) || mul_overflows(N, K) || mul_overflows(M, N))
+    return fail(MX_ERR_INVALID_ARG, "GEMM shape too large");
+  if (K % 32 != 0) return fail(MX_ERR_UNSUPPORTED_SHAPE, "K %lld is not a multiple of 32", (long long)K);
+  if (bkind == MX_BSCALE_32x32 && N % 32 != 0)
+    return fail(MX_ERR_UNSUPPORTED_SHAPE, "N %lld is not a multiple of 32 (32x32 weight tiles)",
+                (long long)N);
+  if (M == 0 || N == 0) return MX_OK;
+  if (!c) return fail(MX_ERR_INVALID_ARG, "c is NULL");
+  if (K > 0 && (!a || !sa || !b || !sb)) return fail(MX_ERR_INVALID_ARG, "an operand is NULL");
+  int dev;
+  mx_status st = current_device(&dev);
+  if (st != MX_OK) return st;
+  hipError_t e;
+  if (K == 0) {
+    e = mx::launch_fill_zero_bf16(c, M * N, stream);
+  } else {
+    int bmode = mx::GEMM_B_ROW;
+    if (bkind == MX_BSCALE_32x32) bmode = layout == MX_GEMM_DGRAD ? mx::GEMM_B_TILE_T : mx::GEMM_B_TILE;
+    e = mx::launch_gemm(bmode, M, N, K, a, sa, b, sb, c, stream);
+  }
+  if (e != hipSuccess) return hip_fail(e, "GEMM kernel launch");
+  return MX_OK;
+}
+
+mx_status mx_grouped_gemm(int64_t G, const int64_t* offsets, int64_t T, int64_t N, int64_t K,
+                          const void* a, const void* sa, const void* b, const void* sb, void* c,
+                          hipStream_t stream) {
+  g_err[0] = '\0';
+  if (G < 1 || G > 512) return fail(MX_ERR_INVALID_ARG, "group count %lld not in [1, 512]", (long long)G);
+  if (T < 0 || N < 0 || K < 0) return fail(MX_ERR_INVALID_ARG, "negative grouped GEMM shape");
+  if (mul_overflows(T, K) || mul_overflows(T, N) || mul_overflows(G, N) || mul_overflows(G * N, K))
+    return fail(MX_ERR_INVALID_ARG, "grouped GEMM shape too large");
+  if (K % 32 != 0) return fail(MX_ERR_UNSUPPORTED_SHAPE, "K %lld is not a multiple of 32", (long long)K);
+  if (T == 0 || N == 0) return MX_OK;
+  if (!offsets || !c) return fail(MX_ERR_INVALID_ARG, "offsets or c is NULL");
+  if (K > 0 && (!a || !sa || !b || !sb)) return fail(MX_ERR_INVALID_ARG, "an operand is NULL");
+  int dev;
+  mx_status st = current_device(&dev);
+  if (st != MX_OK) return st;
+  hipError_t e;
+  if (K == 0) {
+    e = mx::launch_fill_zero_bf16(c, T * N, stream);
+  } else {
+    int cus;
+    {
+      std::lock_guard<std::mutex> lk(g_mu);
+      cus = g_num_cus[dev];
+    }
+    e = mx::launch_grouped_gemm(G, offsets, T, N, K, a, sa, b, sb, c, cus, stream);
+  }
+  if (e != hipSuccess) return hip_fail(e, "grouped GEMM kernel launch");
+  return MX_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,31 @@
+// Internal launchers of the gfx950 kernels (not part of the public C ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mx {
+
+// 1x32 quantisation of a flat BF16 array of n elements (n % 32 == 0).
+hipError_t launch_quant_row(const void* x, int64_t n, void* q, void* s, hipStream_t stream);
+
+// mode 1 = column (q_t, s_t), 2 = dual (q, s, q_t, s_t), 3 = 32x32 tiles (q, s).
+hipError_t launch_quant_tile(int mode, const void* x, int64_t R, int64_t C, void* q, void* s,
+                             void* qt, void* st, hipStream_t stream);
+
+// B operand layouts of the GEMM.
+enum GemmB {
+  GEMM_B_ROW = 0,     // b [N][K], sb [N][K/32]
+  GEMM_B_TILE = 1,    // b [N][K], sb tiles [N/32][K/32]
+  GEMM_B_TILE_T = 2,  // b [K][N] contracted over its rows, sb tiles [K/32][N/32]
+};
+
+hipError_t launch_gemm(int bmode, int64_t M, int64_t N, int64_t K, const void* a, const void* sa,
+                       const void* b, const void* sb, void* c, hipStream_t stream);
+
+hipError_t launch_grouped_gemm(int64_t G, const int64_t* offsets, int64_t T, int64_t N, int64_t K,
+                               const void* a, const void* sa, const void* b, const void* sb,
+                               void* c, int num_cus, hipStream_t stream);
+
+hipError_t launch_fill_zero_bf16(void* c, int64_t n, hipStream_t stream);
+
+}  // namespace mx

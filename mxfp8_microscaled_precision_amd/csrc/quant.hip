@@ -1,0 +1,199 @@
+// MX quantisation kernels for gfx950: BF16 -> E4M3 payload + E8M0 scales.
+//
+// Method: one E8M0 scale per 32 consecutive elements (1x32), computed from
+// the block's absolute maximum on every call (dynamic), rceil rule, elements
+// divided by the scale with round-to-nearest-even into E4M3 (torchtitan-npu
+// MXFP8/HiF8 tutorial, "MXFP8 / HiF8 architecture overview", MXFP8 bullet;
+// MindSpeed RFC "add MXFP8-32x32 quantisation support to FSDP", sections
+// 3.3.1 and 3.3.3).  Dual-axis emits a forward copy blocked along the row and
+// a backward copy blocked along the column from one read of x (tutorial,
+// step-2 environment table, MXFP8_DUAL_AXIS_FORWARD; RFC section 3.3.3).  The
+// 32x32 variant shares one scale per 32x32 tile (RFC sections 1.1, 3.1).
+//
+// All kernels are bound by HBM bandwidth: x is read once with 16-byte loads,
+// every output byte is written once.
+#include "mx_device.h"
+#include "mx_kernels.h"
+
+namespace mx {
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pk_max(uint32_t a, uint32_t b) {
+  u16x2 r = __builtin_elementwise_max(__builtin_bit_cast(u16x2, a), __builtin_bit_cast(u16x2, b));
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// ---------------------------------------------------------------------------
+// 1x32 along rows.  Row-major [R, C] with C % 32 == 0 is the same as the flat
+// array cut into 32-element blocks, so the kernel walks 16-byte chunks of the
+// flat array: four consecutive lanes hold one block.
+// ---------------------------------------------------------------------------
+constexpr int ROW_THREADS = 256;
+constexpr int ROW_UNROLL = 4;
+
+__global__ void __launch_bounds__(ROW_THREADS)
+quant_row_kernel(const uint4* __restrict__ x, uint2* __restrict__ q, uint8_t* __restrict__ s,
+                 int64_t nchunks) {
+  const int64_t span = (int64_t)ROW_THREADS * ROW_UNROLL;
+  for (int64_t base = (int64_t)blockIdx.x * span; base < nchunks; base += (int64_t)gridDim.x * span) {
+    uint4 v[ROW_UNROLL];
+#pragma unroll
+    for (int u = 0; u < ROW_UNROLL; u++) {
+      int64_t c = base + u * ROW_THREADS + threadIdx.x;
+      v[u] = c < nchunks ? load_stream16(x + c) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < ROW_UNROLL; u++) {
+      int64_t c = base + u * ROW_THREADS + threadIdx.x;
+      // quads are either wholly in range or wholly out (nchunks % 4 == 0)
+      uint32_t sb = scale_byte(quad_max(chunk_absmax(v[u])));
+      if (c < nchunks) {
+        q[c] = cvt8(v[u], sb);
+        if ((threadIdx.x & 3) == 0) s[c >> 2] = (uint8_t)sb;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 2-D tile kernel for the column, dual-axis and 32x32 modes.
+//
+// A workgroup of 8 waves covers 128 rows x 128 columns; wave w takes rows
+// 32*(w/2) .. +32 and columns 64*(w%2) .. +64.  In a wave, lane l = 8g + h
+// holds rows 4g .. 4g+3 and columns 8h .. 8h+7 as four 16-byte chunks, so
+// - a row block (32 columns) spans the 4 lanes h = 4b .. 4b+3 of one quad,
+// - a column block (32 rows) spans lanes h, h+8, ..., h+56 (xor 8, 16, 32),
+// - a 32x32 tile is one half of the wave (h < 4 or h >= 4).
+// Column outputs go to q_t[c][r] as one dword (4 rows of one column) per
+// lane and column; a workgroup writes whole 128-byte rows of q_t.
+// ---------------------------------------------------------------------------
+constexpr int TILE_THREADS = 512;
+constexpr int TILE_ROWS = 128;
+constexpr int TILE_COLS = 128;
+
+enum TileMode { TILE_COL = 1, TILE_DUAL = 2, TILE_BLOCK32 = 3 };
+
+template <int MODE>
+__global__ void __launch_bounds__(TILE_THREADS)
+quant_tile_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C, uint8_t* __restrict__ q,
+                  uint8_t* __restrict__ s, uint8_t* __restrict__ qt, uint8_t* __restrict__ st) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 3, h = lane & 7;
+  const int64_t r0 = (int64_t)blockIdx.x * TILE_ROWS + 32 * (wave >> 1);
+  const int64_t c0 = (int64_t)blockIdx.y * TILE_COLS + 64 * (wave & 1);
+  if (r0 >= R || c0 >= C) return;  // whole wave out of range (R, C % 32 == 0)
+  const int64_t c = c0 + 8 * h;
+  const bool live = c < C;  // C % 32 == 0: whole quads are live or dead
+  uint4 v[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+    v[i] = live ? load_stream16(x + (r0 + 4 * g + i) * C + c)
+                : make_uint4(0, 0, 0, 0);
+
+  if (MODE == TILE_BLOCK32) {
+    uint32_t m = umax(umax(chunk_absmax(v[0]), chunk_absmax(v[1])),
+                      umax(chunk_absmax(v[2]), chunk_absmax(v[3])));
+    m = quad_max(m);
+    m = xor_max(m, 8);
+    m = xor_max(m, 16);
+    m = xor_max(m, 32);
+    uint32_t sb = scale_byte(m);
+    if (live) {
+#pragma unroll
+      for (int i = 0; i < 4; i++) *(uint2*)(q + (r0 + 4 * g + i) * C + c) = cvt8(v[i], sb);
+      if (g == 0 && (h & 3) == 0) s[(r0 >> 5) * (C >> 5) + (c >> 5)] = (uint8_t)sb;
+    }
+    return;
+  }
+
+  if (MODE == TILE_DUAL) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      uint32_t sb = scale_byte(quad_max(chunk_absmax(v[i])));
+      if (live) {
+        int64_t r = r0 + 4 * g + i;
+        *(uint2*)(q + r * C + c) = cvt8(v[i], sb);
+        if ((h & 3) == 0) s[r * (C >> 5) + (c >> 5)] = (uint8_t)sb;
+      }
+    }
+  }
+
+  // column maxima, two columns per packed word: cm[k] covers columns 2k, 2k+1
+  const uint32_t M = 0x7FFF7FFFu;
+  uint32_t cm[4];
+  cm[0] = pk_max(pk_max(v[0].x & M, v[1].x & M), pk_max(v[2].x & M, v[3].x & M));
+  cm[1] = pk_max(pk_max(v[0].y & M, v[1].y & M), pk_max(v[2].y & M, v[3].y & M));
+  cm[2] = pk_max(pk_max(v[0].z & M, v[1].z & M), pk_max(v[2].z & M, v[3].z & M));
+  cm[3] = pk_max(pk_max(v[0].w & M, v[1].w & M), pk_max(v[2].w & M, v[3].w & M));
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    cm[k] = pk_max(cm[k], (uint32_t)__shfl_xor((int)cm[k], 8, 64));
+    cm[k] = pk_max(cm[k], (uint32_t)__shfl_xor((int)cm[k], 16, 64));
+    cm[k] = pk_max(cm[k], (uint32_t)__shfl_xor((int)cm[k], 32, 64));
+  }
+  uint32_t sbc[8];
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    sbc[2 * k] = scale_byte(cm[k] & 0xFFFFu);
+    sbc[2 * k + 1] = scale_byte(cm[k] >> 16);
+  }
+  if (!live) return;
+  const uint32_t* w0 = (const uint32_t*)&v[0];
+  const uint32_t* w1 = (const uint32_t*)&v[1];
+  const uint32_t* w2 = (const uint32_t*)&v[2];
+  const uint32_t* w3 = (const uint32_t*)&v[3];
+  const int64_t rq = r0 + 4 * g;
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    const int k = j >> 1;
+    uint32_t p01 = (j & 1) ? pair_hi(w0[k], w1[k]) : pair_lo(w0[k], w1[k]);
+    uint32_t p23 = (j & 1) ? pair_hi(w2[k], w3[k]) : pair_lo(w2[k], w3[k]);
+    uint32_t out = sbc[j] == 0xFFu ? 0x7F7F7F7Fu : cvt4(p01, p23, cvt_scale(sbc[j]));
+    *(uint32_t*)(qt + (c + j) * R + rq) = out;
+  }
+  // lane g stores the scale of column 8h + g
+  uint32_t mine = sbc[0];
+#pragma unroll
+  for (int j = 1; j < 8; j++) mine = (g == j) ? sbc[j] : mine;
+  st[(c + g) * (R >> 5) + (r0 >> 5)] = (uint8_t)mine;
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_quant_row(const void* x, int64_t n, void* q, void* s, hipStream_t stream) {
+  int64_t nchunks = n / 8;
+  int64_t span = (int64_t)ROW_THREADS * ROW_UNROLL;
+  int64_t blocks = (nchunks + span - 1) / span;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(quant_row_kernel, dim3((unsigned)blocks), dim3(ROW_THREADS), 0, stream,
+                     (const uint4*)x, (uint2*)q, (uint8_t*)s, nchunks);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_tile(int mode, const void* x, int64_t R, int64_t C, void* q, void* s,
+                             void* qt, void* st, hipStream_t stream) {
+  dim3 grid((unsigned)((R + TILE_ROWS - 1) / TILE_ROWS), (unsigned)((C + TILE_COLS - 1) / TILE_COLS));
+  const uint16_t* xx = (const uint16_t*)x;
+  switch (mode) {
+    case TILE_COL:
+      hipLaunchKernelGGL(quant_tile_kernel<TILE_COL>, grid, dim3(TILE_THREADS), 0, stream, xx, R, C,
+                         (uint8_t*)q, (uint8_t*)s, (uint8_t*)qt, (uint8_t*)st);
+      break;
+    case TILE_DUAL:
+      hipLaunchKernelGGL(quant_tile_kernel<TILE_DUAL>, grid, dim3(TILE_THREADS), 0, stream, xx, R, C,
+                         (uint8_t*)q, (uint8_t*)s, (uint8_t*)qt, (uint8_t*)st);
+      break;
+    case TILE_BLOCK32:
+      hipLaunchKernelGGL(quant_tile_kernel<TILE_BLOCK32>, grid, dim3(TILE_THREADS), 0, stream, xx, R,
+                         C, (uint8_t*)q, (uint8_t*)s, (uint8_t*)qt, (uint8_t*)st);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mx

@@ -1,0 +1,112 @@
+"""The C ABI library loads, exports every declared symbol, and validates
+arguments on the host before touching a device (CPU only: no compute call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mxfp8_microscaled_precision_amd as mx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = []
+    for fn in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if not fn.endswith(".h"):
+            continue
+        text = open(os.path.join(ROOT, "include", fn)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(mx_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert {"mx_quant", "mx_gemm", "mx_grouped_gemm", "mx_device_check"} <= set(names)
+    L = ctypes.CDLL(mx.LIB_PATH)
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_binding_names_match_the_abi():
+    for n in _declared_functions():
+        assert hasattr(mx, n), n
+
+
+@pytest.mark.parametrize("name,ok", [
+    ("gfx950", 1), ("gfx950:sramecc+:xnack-", 1), ("gfx942", 0), ("gfx9500", 0),
+    ("gfx90a:xnack+", 0), ("", 0),
+])
+def test_arch_gate(name, ok):
+    assert mx.mx_arch_supported(name) == ok
+
+
+def test_status_strings():
+    for s in range(5):
+        assert mx.mx_status_string(s)
+    assert "gfx950" in mx.mx_status_string(3)
+
+
+# Validation happens before any HIP call, so these run without a GPU.
+INVALID, SHAPE = 1, 2
+
+
+@pytest.mark.parametrize("args,status", [
+    ((7, 1, 32, 32, 1, 1, 0, 0, 0), INVALID),          # unknown mode
+    ((0, 1, -1, 32, 1, 1, 0, 0, 0), INVALID),          # negative rows
+    ((0, 1, 4, 33, 1, 1, 0, 0, 0), SHAPE),             # row blocks need cols % 32
+    ((1, 1, 33, 32, 0, 0, 1, 1, 0), SHAPE),            # column blocks need rows % 32
+    ((2, 1, 64, 48, 1, 1, 1, 1, 0), SHAPE),            # dual needs both
+    ((3, 1, 32, 40, 1, 1, 0, 0, 0), SHAPE),            # 32x32 tiles need both
+    ((0, 0, 4, 32, 1, 1, 0, 0, 0), INVALID),           # NULL x
+    ((0, 1, 4, 32, 0, 1, 0, 0, 0), INVALID),           # NULL q
+    ((2, 1, 32, 32, 1, 1, 0, 1, 0), INVALID),          # NULL q_t for dual
+])
+def test_quant_validation(args, status):
+    assert mx.mx_quant(*args) == status
+    assert mx.mx_last_error() != ""
+
+
+def test_quant_empty_is_noop():
+    assert mx.mx_quant(0, 0, 0, 32, 0, 0, 0, 0, 0) == 0
+    assert mx.mx_quant(2, 0, 64, 0, 0, 0, 0, 0, 0) == 0
+
+
+@pytest.mark.parametrize("args,status", [
+    ((5, 0, 4, 4, 32, 1, 1, 1, 1, 1, 0), INVALID),     # layout
+    ((0, 3, 4, 4, 32, 1, 1, 1, 1, 1, 0), INVALID),     # bscale kind
+    ((2, 1, 4, 32, 32, 1, 1, 1, 1, 1, 0), INVALID),    # wgrad has no 32x32 weight
+    ((0, 0, 4, 4, 48, 1, 1, 1, 1, 1, 0), SHAPE),       # K % 32
+    ((0, 1, 4, 40, 32, 1, 1, 1, 1, 1, 0), SHAPE),      # N % 32 for tiles
+    ((0, 0, -4, 4, 32, 1, 1, 1, 1, 1, 0), INVALID),    # negative
+    ((0, 0, 4, 4, 32, 1, 1, 1, 1, 0, 0), INVALID),     # NULL c
+    ((0, 0, 4, 4, 32, 0, 1, 1, 1, 1, 0), INVALID),     # NULL a
+])
+def test_gemm_validation(args, status):
+    assert mx.mx_gemm(*args) == status
+
+
+def test_gemm_empty_is_noop():
+    assert mx.mx_gemm(0, 0, 0, 8, 32, 0, 0, 0, 0, 0, 0) == 0
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 1, 4, 8, 32, 1, 1, 1, 1, 1, 0), INVALID),     # G = 0
+    ((513, 1, 4, 8, 32, 1, 1, 1, 1, 1, 0), INVALID),   # G too large
+    ((4, 1, 4, 8, 40, 1, 1, 1, 1, 1, 0), SHAPE),       # K % 32
+    ((4, 0, 4, 8, 32, 1, 1, 1, 1, 1, 0), INVALID),     # NULL offsets
+])
+def test_grouped_validation(args, status):
+    assert mx.mx_grouped_gemm(*args) == status
+
+
+def test_process_quant_result_rejects_unknown_recipe():
+    with pytest.raises(ValueError):
+        mx.process_quant_result(None, "mxfp4")
+
+
+def test_quant_rejects_unknown_mode_name():
+    with pytest.raises(ValueError):
+        mx.quant(None, "1x64")

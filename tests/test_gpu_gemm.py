@@ -1,0 +1,214 @@
+"""GPU parity of mx_gemm against the oracle: every element of C within
+|gpu - ref| <= 2^-7 * sum_k |a_k b_k| + 1e-6, ref and the bound computed in
+binary64 by the oracle from the same quantised bytes.  Small cases quantise
+with the oracle and upload its bytes; full-size cases check seeded samples of
+C end to end (GPU quant + GEMM against oracle quant + GEMM of the same BF16
+rows and columns)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import mxfp8_microscaled_precision_amd as mx
+from mxfp8_microscaled_precision_amd import workloads as W
+from parity import assert_gemm, bits, dev, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(a, sa, b, sb, layout, bscale, bkind, what):
+    say(f"[gemm] {what} layout={layout} bscale={bscale} A={a.shape} B={b.shape}")
+    c = mx.gemm(dev(a), dev(sa), dev(b), dev(sb), layout, bscale)
+    torch.cuda.synchronize()
+    ref, bound = oracle.gemm(a, sa, b, sb, bkind)
+    assert_gemm(c, ref, bound, what)
+
+
+def test_tiny_config_fprop():
+    d = W.tiny("cpu")
+    qa, sa = oracle.quant_row(bits(d["A"]))
+    qw, sw = oracle.quant_row(bits(d["W"]))
+    _run(qa, sa, qw, sw, "fprop", "1x32", oracle.BKIND_ROW, "tiny")
+
+
+SHAPES = [(1, 1, 32), (64, 64, 32), (300, 200, 160), (257, 513, 96), (512, 256, 4096),
+          (33, 290, 1056), (256, 256, 128)]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+@pytest.mark.parametrize("layout", ["fprop", "dgrad", "wgrad"])
+def test_row_scales_all_layouts(M, N, K, layout):
+    # the three products of a linear layer are all "TN" on 1x32 operands;
+    # build them the way the layer does (row / column quantisation)
+    seed = M * 7 + N * 3 + K
+    if layout == "fprop":      # Y = X W^T: a = X_row [M,K], b = W_row [N,K]
+        qa, sa = oracle.quant_row(bits(W.normal_bf16((M, K), 1.0, seed)))
+        qb, sb = oracle.quant_row(bits(W.normal_bf16((N, K), 0.02, seed + 1)))
+    elif layout == "dgrad":    # dX = dY W: a = dY_row [M,K=out], b = W_col_T [N=in, K=out]
+        qa, sa = oracle.quant_row(bits(W.normal_bf16((M, K), 1e-3, seed)))
+        qb, sb = oracle.quant_col(bits(W.normal_bf16((K, N), 0.02, seed + 1)))
+    else:                      # dW = dY^T X: a = dY_col_T [M=out, K=tok], b = X_col_T [N=in, K=tok]
+        qa, sa = oracle.quant_col(bits(W.normal_bf16((K, M), 1e-3, seed)))
+        qb, sb = oracle.quant_col(bits(W.normal_bf16((K, N), 1.0, seed + 1)))
+    _run(qa, sa, qb, sb, layout, "1x32", oracle.BKIND_ROW, f"{layout} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(64, 64, 64), (300, 224, 160), (257, 544, 1056), (512, 256, 4096)])
+def test_block32_weight_fprop_and_dgrad(M, N, K):
+    # fprop: Y[M, out=N] = X[M, in=K] W[out=N, in=K]^T with W in 32x32 tiles
+    qx, sx = oracle.quant_row(bits(W.normal_bf16((M, K), 1.0, M + K)))
+    qw, sw = oracle.quant_block32(bits(W.normal_bf16((N, K), 0.02, N + K)))
+    _run(qx, sx, qw, sw, "fprop", "32x32", oracle.BKIND_TILE, f"fprop32 {M}x{N}x{K}")
+    # dgrad: dX[M, in=N] = dY[M, out=K] W[out=K, in=N], the same FP8 weight
+    qd, sd = oracle.quant_row(bits(W.normal_bf16((M, K), 1e-3, M + 2 * K)))
+    qw2, sw2 = oracle.quant_block32(bits(W.normal_bf16((K, N), 0.02, 3 * N + K)))
+    _run(qd, sd, qw2, sw2, "dgrad", "32x32", oracle.BKIND_TILE_T, f"dgrad32 {M}x{N}x{K}")
+
+
+def test_one_hot_rows_select_b():
+    """K = 32, A rows one-hot 1.0: C rows are B's rows (exact in BF16)."""
+    N = 96
+    qb, sb = oracle.quant_row(bits(W.normal_bf16((N, 32), 1.0, 3)))
+    qa = np.zeros((32, 32), np.uint8)
+    qa[np.arange(32), np.arange(32)] = 0x38
+    sa = np.full((32, 1), 127, np.uint8)
+    c = mx.gemm(dev(qa), dev(sa), dev(qb), dev(sb))
+    ref, _ = oracle.gemm(qa, sa, qb, sb)
+    assert np.array_equal(c.float().cpu().numpy().astype(np.float64), ref)
+
+
+def test_k_zero_writes_zeros():
+    def e(r):
+        return torch.empty((r, 0), dtype=torch.uint8, device="cuda")
+    out = torch.full((5, 7), 3.0, dtype=torch.bfloat16, device="cuda")
+    mx.gemm(e(5), e(5), e(7), e(7), out=out)
+    torch.cuda.synchronize()
+    assert (out.float() == 0).all()
+
+
+def test_nan_scale_propagates():
+    M, N, K = 40, 48, 64
+    qa, sa = oracle.quant_row(bits(W.normal_bf16((M, K), 1.0, 5)))
+    qb, sb = oracle.quant_row(bits(W.normal_bf16((N, K), 1.0, 6)))
+    sa[3, 1] = 0xFF
+    _run(qa, sa, qb, sb, "fprop", "1x32", oracle.BKIND_ROW, "nan scale")
+
+
+def test_deterministic():
+    qa, sa = oracle.quant_row(bits(W.normal_bf16((512, 1024), 1.0, 8)))
+    qb, sb = oracle.quant_row(bits(W.normal_bf16((384, 1024), 1.0, 9)))
+    A, SA, B, SB = dev(qa), dev(sa), dev(qb), dev(sb)
+    assert torch.equal(mx.gemm(A, SA, B, SB), mx.gemm(A, SA, B, SB))
+
+
+# --------------------------------------------------------------------------
+# Full-size products, sampled
+# --------------------------------------------------------------------------
+
+def _sample(n, k, rng, extra=()):
+    idx = np.unique(np.concatenate([[0, n - 1], list(extra), rng.integers(0, n, k)]))
+    return idx.astype(np.int64)
+
+
+def _end_to_end(what, c_gpu, a_src, a_mode, b_src, b_mode, bkind, rows, cols):
+    """Compare c_gpu[rows][:, cols] with the oracle's quantise-then-multiply
+    of the same BF16 sources.  a_src/b_src: BF16 device tensors; *_mode says
+    how the operand is quantised: 'row' (rows of the source are the operand
+    rows) or 'col' (columns of the source are the operand rows, blocks run
+    down the column), 'tile' / 'tile_t' for the 32x32 weight."""
+    ri = torch.from_numpy(rows).cuda()
+    ci = torch.from_numpy(cols).cuda()
+    if a_mode == "row":
+        qa, sa = oracle.quant_row(bits(a_src.index_select(0, ri)))
+    else:
+        qa, sa = oracle.quant_col(bits(a_src.index_select(1, ri)))
+    if b_mode == "row":
+        qb, sb = oracle.quant_row(bits(b_src.index_select(0, ci)))
+    elif b_mode == "col":
+        qb, sb = oracle.quant_col(bits(b_src.index_select(1, ci)))
+    elif b_mode == "tile":       # cols are whole 32-row groups of the weight [N, K]
+        qb, sb = oracle.quant_block32(bits(b_src.index_select(0, ci)))
+    else:                        # tile_t: cols are whole 32-column groups of weight [K, N]
+        qb, sb = oracle.quant_block32(bits(b_src.index_select(1, ci)))
+    ref, bound = oracle.gemm(qa, sa, qb, sb, bkind)
+    got = c_gpu.index_select(0, ri).index_select(1, ci)
+    assert_gemm(got, ref, bound, what)
+
+
+def _groups32(n, k, rng):
+    g = np.unique(np.concatenate([[0, n // 32 - 1], rng.integers(0, n // 32, k)]))
+    return (g[:, None] * 32 + np.arange(32)[None, :]).ravel().astype(np.int64)
+
+
+def test_dense_full_three_products():
+    d = W.dense("cuda")
+    X, Wt, dY = d["X"], d["W"], d["dY"]
+    M, K = X.shape
+    N = Wt.shape[0]
+    say(f"[gemm] dense full M={M} N={N} K={K}")
+    qx, sx, qxt, sxt = mx.quant(X, "dual")
+    qw, sw, qwt, swt = mx.quant(Wt, "dual")
+    qd, sd, qdt, sdt = mx.quant(dY, "dual")
+    Y = mx.gemm(qx, sx, qw, sw, "fprop")
+    dX = mx.gemm(qd, sd, qwt, swt, "dgrad")
+    dW = mx.gemm(qdt, sdt, qxt, sxt, "wgrad")
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(21)
+    _end_to_end("dense fprop", Y, X, "row", Wt, "row", oracle.BKIND_ROW,
+                _sample(M, 48, rng), _sample(N, 48, rng))
+    _end_to_end("dense dgrad", dX, dY, "row", Wt, "col", oracle.BKIND_ROW,
+                _sample(M, 48, rng), _sample(K, 48, rng))
+    _end_to_end("dense wgrad", dW, dY, "col", X, "col", oracle.BKIND_ROW,
+                _sample(N, 32, rng), _sample(K, 32, rng))
+
+
+def test_block32_full_four_products():
+    d = W.block32("cuda")
+    W1, W2, X1, X2 = d["W1"], d["W2"], d["X1"], d["X2"]
+    say(f"[gemm] block32 full W1={tuple(W1.shape)} W2={tuple(W2.shape)} X1={tuple(X1.shape)}")
+    q1, s1 = mx.quant(W1, "32x32")
+    q2, s2 = mx.quant(W2, "32x32")
+    qx1, sx1 = mx.quant(X1, "row")
+    qx2, sx2 = mx.quant(X2, "row")
+    Y1 = mx.gemm(qx1, sx1, q1, s1, "fprop", "32x32")      # [T, 2048]
+    Y2 = mx.gemm(qx2, sx2, q2, s2, "fprop", "32x32")      # [T, 7168]
+    dX1 = mx.gemm(qx2, sx2, q1, s1, "dgrad", "32x32")     # dY1 = X2 [T, 2048] -> [T, 7168]
+    dX2 = mx.gemm(qx1, sx1, q2, s2, "dgrad", "32x32")     # dY2 = X1 [T, 7168] -> [T, 2048]
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(31)
+    T = X1.shape[0]
+    _end_to_end("block32 fprop1", Y1, X1, "row", W1, "tile", oracle.BKIND_TILE,
+                _sample(T, 40, rng), _groups32(W1.shape[0], 2, rng))
+    _end_to_end("block32 fprop2", Y2, X2, "row", W2, "tile", oracle.BKIND_TILE,
+                _sample(T, 40, rng), _groups32(W2.shape[0], 2, rng))
+    _end_to_end("block32 dgrad1", dX1, X2, "row", W1, "tile_t", oracle.BKIND_TILE_T,
+                _sample(T, 40, rng), _groups32(W1.shape[1], 2, rng))
+    _end_to_end("block32 dgrad2", dX2, X1, "row", W2, "tile_t", oracle.BKIND_TILE_T,
+                _sample(T, 40, rng), _groups32(W2.shape[1], 2, rng))
+
+
+def test_stack_layer_full_six_products():
+    d = W.stack_layer(0, "cuda")
+    Xu, Xd, dYu, dYd, Wu, Wd = (d[k] for k in ("X_up", "X_dn", "dY_up", "dY_dn", "W_up", "W_dn"))
+    T, H = Xu.shape
+    F = Wu.shape[0]
+    say(f"[gemm] stack layer T={T} H={H} F={F}")
+    rng = np.random.default_rng(41)
+    # up projection H -> F
+    qx, sx, qxt, sxt = mx.quant(Xu, "dual")
+    qw, sw, qwt, swt = mx.quant(Wu, "dual")
+    qd, sd, qdt, sdt = mx.quant(dYu, "dual")
+    Y = mx.gemm(qx, sx, qw, sw, "fprop")
+    torch.cuda.synchronize()
+    _end_to_end("stack up fprop", Y, Xu, "row", Wu, "row", oracle.BKIND_ROW,
+                _sample(T, 24, rng), _sample(F, 24, rng))
+    del Y
+    dX = mx.gemm(qd, sd, qwt, swt, "dgrad")
+    torch.cuda.synchronize()
+    _end_to_end("stack up dgrad", dX, dYu, "row", Wu, "col", oracle.BKIND_ROW,
+                _sample(T, 24, rng), _sample(H, 24, rng))
+    del dX
+    dW = mx.gemm(qdt, sdt, qxt, sxt, "wgrad")
+    torch.cuda.synchronize()
+    _end_to_end("stack up wgrad", dW, dYu, "col", Xu, "col", oracle.BKIND_ROW,
+                _sample(F, 12, rng), _sample(H, 12, rng))

@@ -1,0 +1,195 @@
+"""GPU parity of mx_quant against the oracle: payload and scale bytes must be
+bit-identical (every mode, several tiles with ragged tails, every BF16
+magnitude under every scale exponent, special values, the workloads' full
+shapes)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import mxfp8_microscaled_precision_amd as mx
+from mxfp8_microscaled_precision_amd import workloads as W
+from parity import assert_bytes, bits, dev, oracle_quant, say
+
+pytestmark = pytest.mark.gpu
+
+MODES = ["row", "col", "dual", "32x32"]
+
+
+def _check_full(x: torch.Tensor, mode: str, what: str):
+    say(f"[quant] {what} mode={mode} shape={tuple(x.shape)}")
+    outs = mx.quant(x, mode)
+    torch.cuda.synchronize()
+    ref = oracle_quant(bits(x), mode)
+    names = {"row": ("q", "s"), "col": ("q_t", "s_t"), "dual": ("q", "s", "q_t", "s_t"),
+             "32x32": ("q", "s")}[mode]
+    for o, r, n in zip(outs, ref, names):
+        assert_bytes(o, r, f"{what} {mode} {n}")
+
+
+def test_device_is_gfx950():
+    assert mx.mx_device_check(0) == 0, mx.mx_last_error()
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_tiny_config(mode):
+    d = W.tiny("cuda")
+    _check_full(d["A"], mode, "tiny A")
+    _check_full(d["W"], mode, "tiny W")
+
+
+@pytest.mark.parametrize("shape", [(32, 32), (160, 96), (96, 224), (288, 416), (1024, 1056)])
+@pytest.mark.parametrize("mode", MODES)
+def test_ragged_tiles(shape, mode):
+    x = W.normal_bf16(shape, 1.0, 1000 + shape[0] + shape[1], "cuda")
+    _check_full(x, mode, "ragged")
+
+
+@pytest.mark.parametrize("shape", [(1, 32), (3, 64), (7, 4096 + 32)])
+def test_row_only_shapes(shape):
+    x = W.normal_bf16(shape, 1.0, 77, "cuda")
+    _check_full(x, "row", "row-only")
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_scaled_workloads(mode):
+    d = W.dense("cuda", scale=8)                # X with 0.1% outliers x100
+    _check_full(d["X"], mode, "dense/8 X")
+    _check_full(d["dY"], mode, "dense/8 dY")
+    t = W.student_t_bf16((512, 896), 3, 5, "cuda")
+    _check_full(t, mode, "student-t")
+
+
+def test_sweep_every_bf16_under_every_exponent():
+    """All BF16 magnitudes under anchors reaching every exponent -127..120,
+    through the row kernel and (transposed) through the column kernel."""
+    sw = W.sweep_blocks_bits()
+    q_ref, s_ref = oracle.quant_row(sw)
+    x = W.bits_to_bf16(sw, "cuda")
+    say(f"[quant] sweep rows={sw.shape[0]}")
+    q, s = mx.quant(x, "row")
+    assert_bytes(q, q_ref, "sweep row q")
+    assert_bytes(s, s_ref, "sweep row s")
+    n = (sw.shape[0] // 32) * 32
+    xt = W.bits_to_bf16(np.ascontiguousarray(sw[:n].T), "cuda")   # [32, n]
+    qt, st = mx.quant(xt, "col")
+    assert_bytes(qt, q_ref[:n], "sweep col q_t")
+    assert_bytes(st, s_ref[:n], "sweep col s_t")
+
+
+def _special_matrix(R, C, seed):
+    rng = np.random.default_rng(seed)
+    x = W.bf16_bits(W.normal_bf16((R, C), 1.0, seed))
+    x[0:32, 0:32] = 0                                   # zero tile / blocks
+    x[32:64, 0:32] = 0x8000                             # -0 tile
+    x[0, 40] = 0x7FC0                                   # NaN
+    x[5, 70] = 0xFF80                                   # -Inf
+    x[64:96, 32:64] = rng.integers(0, 0x80, size=(32, 32), dtype=np.uint16)  # subnormals
+    x[64:96, 32:64] |= (rng.integers(0, 2, size=(32, 32), dtype=np.uint16) << 15)
+    x[96, 96:128] = 0x4360                              # 224.0 in a row block
+    x[100:132, 130] = 0x7F7F                            # max BF16 down a column
+    x[140, 0:32] = 0x43E0                               # exactly 448
+    return x
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_special_values(mode):
+    xb = _special_matrix(192, 160, 9)
+    x = W.bits_to_bf16(xb, "cuda")
+    _check_full(x, mode, "special")
+
+
+def test_empty_inputs():
+    for mode in MODES:
+        x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+        outs = mx.quant(x, mode)
+        assert all(o.numel() == 0 for o in outs)
+
+
+def test_shape_errors_raise():
+    x = torch.zeros((64, 48), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(mx.MXError) as e:
+        mx.quant(x, "dual")
+    assert e.value.status == 2
+
+
+def test_deterministic():
+    x = W.normal_bf16((1024, 2048), 1.0, 4, "cuda")
+    a = mx.quant(x, "dual")
+    b = mx.quant(x, "dual")
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+
+
+def test_process_quant_result_tuples():
+    w = W.normal_bf16((256, 512), 0.02, 12, "cuda")
+    t4 = mx.process_quant_result(w, "mxfp8")
+    assert len(t4) == 4 and t4[0].shape == (256, 512) and t4[2].shape == (512, 256)
+    q, s, qb, sb = mx.process_quant_result(w, "mxfp8-32x32")
+    assert qb is q and sb is s                 # one FP8 weight shared by both passes
+    rq, rs = oracle.quant_block32(bits(w))
+    assert_bytes(q, rq, "32x32 weight")
+    assert_bytes(s, rs, "32x32 scales")
+
+
+def test_block32_transposes_to_same_bytes():
+    w = W.normal_bf16((2048, 7168 // 4), 0.02, 13, "cuda")
+    q, s = mx.quant(w, "32x32")
+    qT, sT = mx.quant(w.t().contiguous(), "32x32")
+    assert torch.equal(qT, q.t().contiguous()) and torch.equal(sT, s.t().contiguous())
+
+
+# --------------------------------------------------------------------------
+# The workloads at full size (the configurations the bench times)
+# --------------------------------------------------------------------------
+
+def test_dense_full_dual():
+    d = W.dense("cuda")
+    for name in ("X", "W", "dY"):
+        _check_full(d[name], "dual", f"dense {name}")
+
+
+def test_block32_full():
+    d = W.block32("cuda")
+    _check_full(d["W1"], "32x32", "block32 W1")
+    _check_full(d["W2"], "32x32", "block32 W2")
+    _check_full(d["X2"], "row", "block32 X2")
+
+
+def _sampled_dual(x: torch.Tensor, what: str, nrows=64, ncols=64, seed=0):
+    """Full-size dual quantisation checked on seeded rows and columns."""
+    R, C = x.shape
+    say(f"[quant] sampled dual {what} shape={tuple(x.shape)}")
+    q, s, qt, st = mx.quant(x, "dual")
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([[0, R - 1], rng.integers(0, R, nrows)]))
+    cols = np.unique(np.concatenate([[0, C - 1], rng.integers(0, C, ncols)]))
+    ri = torch.from_numpy(rows).cuda()
+    ci = torch.from_numpy(cols).cuda()
+    rq, rs = oracle.quant_row(bits(x.index_select(0, ri)))
+    assert_bytes(q.index_select(0, ri), rq, f"{what} q rows")
+    assert_bytes(s.index_select(0, ri), rs, f"{what} s rows")
+    cq, cs = oracle.quant_col(bits(x.index_select(1, ci)))
+    assert_bytes(qt.index_select(0, ci), cq, f"{what} q_t rows")
+    assert_bytes(st.index_select(0, ci), cs, f"{what} s_t rows")
+
+
+def test_stack_layer_full_sampled():
+    d = W.stack_layer(0, "cuda")
+    for name in ("X_up", "X_dn", "dY_up", "W_up"):
+        _sampled_dual(d[name], f"stack {name}", seed=hash(name) % 1000)
+    del d
+
+
+def test_moe_weights_full_sampled():
+    d = W.moe("cuda")
+    Wg = d["W_gu"].reshape(-1, d["W_gu"].shape[-1])
+    say(f"[quant] moe W_gu row shape={tuple(Wg.shape)}")
+    q, s = mx.quant(Wg, "row")
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    rows = torch.from_numpy(np.unique(rng.integers(0, Wg.shape[0], 256))).cuda()
+    rq, rs = oracle.quant_row(bits(Wg.index_select(0, rows)))
+    assert_bytes(q.index_select(0, rows), rq, "W_gu q rows")
+    assert_bytes(s.index_select(0, rows), rs, "W_gu s rows")
