@@ -35,6 +35,9 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) v2i lds_v2i;
+typedef __attribute__((address_space(3))) v4i lds_v4i;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int BM = 256;
 constexpr int BN = 256;
@@ -47,32 +50,11 @@ constexpr int LDS_BYTES = 2 * STAGE;      // 128 KB
 constexpr int CHUNKS = A_TILE / 16 / NT;  // 16-byte chunks per thread per operand: 8
 constexpr int MAX_GROUPS = 512;
 
-// Scale bytes of blocks kb0 .. kb0+3 of one operand row (blocks at or past
-// nkb read as 0x7F = 2^0; their payload is zero).
-__device__ __forceinline__ uint32_t load_scale4(const uint8_t* __restrict__ p, int64_t kb0,
-                                                int64_t nkb) {
-  if (kb0 + 4 <= nkb && (((uintptr_t)(p + kb0)) & 3) == 0) return *(const uint32_t*)(p + kb0);
-  uint32_t r = 0;
-#pragma unroll
-  for (int i = 0; i < 4; i++) r |= (uint32_t)(kb0 + i < nkb ? p[kb0 + i] : 0x7F) << (8 * i);
-  return r;
-}
-
-// Tile scales of a transposed 32x32 weight: sb[kb][ncol32] for kb0 .. kb0+3.
-__device__ __forceinline__ uint32_t load_scale4_t(const uint8_t* __restrict__ sb, int64_t kb0,
-                                                  int64_t nkb, int64_t ld, int64_t ncol32) {
-  uint32_t r = 0;
-#pragma unroll
-  for (int i = 0; i < 4; i++)
-    r |= (uint32_t)(kb0 + i < nkb ? sb[(kb0 + i) * ld + ncol32] : 0x7F) << (8 * i);
-  return r;
-}
-
 // Fragment of 32 rows x 64 K from a row-major LDS tile (128-byte rows).
-__device__ __forceinline__ v8i read_frag(const uint8_t* tile, int row, int s, int g) {
+__device__ __forceinline__ v8i read_frag(const lds_u8* tile, int row, int s, int g) {
   const int x = row & 7;
-  v4i lo = *(const v4i*)(tile + row * BK + (((2 * s + g) ^ x) << 4));
-  v4i hi = *(const v4i*)(tile + row * BK + (((4 + 2 * s + g) ^ x) << 4));
+  v4i lo = *(const lds_v4i*)(tile + row * BK + (((2 * s + g) ^ x) << 4));
+  v4i hi = *(const lds_v4i*)(tile + row * BK + (((4 + 2 * s + g) ^ x) << 4));
   return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 }
 
@@ -80,115 +62,232 @@ __device__ __forceinline__ v8i read_frag(const uint8_t* tile, int row, int s, in
 // rows), read transposed with ds_read_b64_tr_b8: in each group of 16 lanes,
 // lane 2r+h points at 8 bytes of row k+r and lane i receives byte i of the
 // eight 16-byte rows, i.e. 8 consecutive k of column i.
-__device__ __forceinline__ v8i read_frag_t(const uint8_t* tile, int nb, int s, int lane) {
+__device__ __forceinline__ v8i read_frag_t(const lds_u8* tile, int nb, int s, int lane) {
   const int g = lane >> 5, q = (lane >> 4) & 1, r = (lane & 15) >> 1, hh = lane & 1;
+  // row k = k_const + 16g + r with k_const a multiple of 8, so k & 7 = r and
+  // the swizzled chunk is lane-only; every piece is base + a constant offset
   const int ncol = nb + 16 * q + 8 * hh;
+  const lds_u8* base = tile + (16 * g + r) * 256 + (((ncol >> 4) ^ r) << 4) + (ncol & 15);
   v2i p[4];
 #pragma unroll
   for (int t = 0; t < 4; t++) {
-    const int k = (t >> 1) * 64 + 32 * s + 16 * g + (t & 1) * 8 + r;
-    const uint8_t* a = tile + k * 256 + (((ncol >> 4) ^ (k & 7)) << 4) + (ncol & 15);
-    p[t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)a);
+    const int kc = (t >> 1) * 64 + 32 * s + (t & 1) * 8;
+    p[t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(base + kc * 256));
   }
   return (v8i){p[0].x, p[0].y, p[1].x, p[1].y, p[2].x, p[2].y, p[3].x, p[3].y};
 }
 
-template <int BMODE>
+// Raw buffer descriptor over [base, base + bytes): loads at offsets >= bytes
+// return zero, which fills the tile edges (rows past M or N, K past the end).
+// Every input is uniform across the wave; readfirstlane makes that visible
+// to the compiler so the descriptor lives in scalar registers.
+__device__ __forceinline__ u32x4 make_rsrc(const void* base, int64_t bytes) {
+  const uint64_t p = (uint64_t)base;
+  return (u32x4){(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p),
+                 (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(p >> 32) & 0xFFFFu)),
+                 (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)bytes), 0x00020000u};
+}
+
+// 16 bytes per lane from the buffer at voffset into LDS at lds + 16 * lane
+// (buffer_load_dwordx4 ... lds).  Issued through asm so that the compiler does
+// not order LDS reads of the other stage behind these loads; the kernel waits
+// for them itself (vmcnt(0) before the barrier that publishes the stage).
+__device__ __forceinline__ void dma16(const lds_u8* lds, uint32_t voffset, u32x4 rsrc) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(m0), "v"(voffset), "s"(rsrc)
+               : "memory");
+}
+
+// s_waitcnt vmcnt(0) (expcnt, lgkmcnt left at their maxima), as a builtin so
+// the compiler knows every earlier vector-memory load has completed.
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+constexpr uint32_t OOB = 0x80000000u;  // an offset past every tile buffer
+
+// One workgroup tile.  Pipeline (two LDS stages, one barrier per K step):
+//   phase A of step kt: MFMAs of K half 0 on registers F0, LDS reads of
+//     half 1 into F1 interleaved;
+//   barrier: every wave has read stage kt, and the loads of stage kt+1 and
+//     the scales of step kt+1 have landed (vmcnt(0));
+//   phase B: buffer->LDS loads of stage kt+2 into the buffer just released,
+//     scale loads of step kt+2, MFMAs of half 1 on F1, LDS reads of half 0 of
+//     stage kt+1 into F0 interleaved.
+// The loop body has no branches so the scheduler can interleave freely.
+template <int BMODE, bool FAST>
 struct Tile {
-  // operands
   const uint8_t* __restrict__ a;
   const uint8_t* __restrict__ sa;
   const uint8_t* __restrict__ b;
   const uint8_t* __restrict__ sb;
   uint16_t* __restrict__ c;
   int64_t m0, m_end, n0, N, K, nkb;
-  uint8_t* smem;
+  lds_u8* st0;  // the two LDS stages (distinct arrays, so the compiler can
+  lds_u8* st1;  // tell the loads into one from the reads of the other)
 
-  uint4 ra[CHUNKS], rb[CHUNKS];
+  u32x4 ra, rb;
+  uint32_t voff_a, voff_b;      // per-lane offset of this lane's first chunk
+  uint32_t a_step, b_step;      // offset between this wave's consecutive chunks
+  int64_t srow_a[4], srow_b[4]; // scale row bases
 
-  __device__ __forceinline__ void load_stage(int64_t k0) {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int u = 0; u < CHUNKS; u++) {
-      const int id = u * NT + tid;
-      const int row = id >> 3, cc = id & 7;
-      int64_t m = m0 + row;
-      m = m < m_end ? m : m_end - 1;
-      const int64_t kb = k0 + 16 * cc;
-      ra[u] = kb < K ? *(const uint4*)(a + m * K + kb) : make_uint4(0, 0, 0, 0);
+  __device__ __forceinline__ void setup(int wave, int lane) {
+    const int64_t mrows = m_end - m0;
+    ra = make_rsrc(a + m0 * K, mrows * K);
+    // A: instruction t = wave + 4u covers LDS rows 8t .. 8t+7 (1 KB); lane i
+    // lands in row 8t + i/8 at physical chunk i%8, holding logical chunk
+    // (i%8) ^ (i/8) of that row.
+    voff_a = (uint32_t)((8 * wave + (lane >> 3)) * K + 16 * ((lane & 7) ^ (lane >> 3)));
+    a_step = (uint32_t)(32 * K);
+    if (BMODE == GEMM_B_TILE_T) {
+      // B stored [K][N]; tile columns n0 .. n0+255.  Instruction t covers LDS
+      // rows (k) 4t .. 4t+3 of 256 bytes; lane i -> row 4t + i/16, physical
+      // chunk i%16 holding logical chunk (i%16) ^ (row & 7).
+      // Columns past N feed only outputs that are never stored, and the
+      // buffer ends with the weight, so they need no mask.
+      rb = make_rsrc(b + n0, (K - 1) * N + (N - n0));
+      const int krow = 4 * wave + (lane >> 4);
+      const int lc = (lane & 15) ^ (krow & 7);
+      voff_b = (uint32_t)(krow * N + 16 * lc);
+      b_step = (uint32_t)(16 * N);
+    } else {
+      const int64_t nrows = (N - n0) < BN ? (N - n0) : BN;
+      rb = make_rsrc(b + n0 * K, nrows * K);
+      voff_b = (uint32_t)((8 * wave + (lane >> 3)) * K + 16 * ((lane & 7) ^ (lane >> 3)));
+      b_step = (uint32_t)(32 * K);
     }
-#pragma unroll
-    for (int u = 0; u < CHUNKS; u++) {
-      const int id = u * NT + tid;
-      if (BMODE == GEMM_B_TILE_T) {
-        const int krow = id >> 4, cc = id & 15;
-        const int64_t kk = k0 + krow, nn = n0 + 16 * cc;
-        rb[u] = (kk < K && nn < N) ? *(const uint4*)(b + kk * N + nn) : make_uint4(0, 0, 0, 0);
-      } else {
-        const int row = id >> 3, cc = id & 7;
-        int64_t n = n0 + row;
-        n = n < N ? n : N - 1;
-        const int64_t kb = k0 + 16 * cc;
-        rb[u] = kb < K ? *(const uint4*)(b + n * K + kb) : make_uint4(0, 0, 0, 0);
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store_stage(uint8_t* st) {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int u = 0; u < CHUNKS; u++) {
-      const int id = u * NT + tid;
-      const int row = id >> 3, cc = id & 7;
-      *(uint4*)(st + row * BK + ((cc ^ (row & 7)) << 4)) = ra[u];
-    }
-#pragma unroll
-    for (int u = 0; u < CHUNKS; u++) {
-      const int id = u * NT + tid;
-      if (BMODE == GEMM_B_TILE_T) {
-        const int krow = id >> 4, cc = id & 15;
-        *(uint4*)(st + A_TILE + krow * 256 + ((cc ^ (krow & 7)) << 4)) = rb[u];
-      } else {
-        const int row = id >> 3, cc = id & 7;
-        *(uint4*)(st + A_TILE + row * BK + ((cc ^ (row & 7)) << 4)) = rb[u];
-      }
-    }
-  }
-
-  // Scale registers for K step kb0: sar[fm] for the wave's A fragments and
-  // sbr[fn] for its B fragments, already shifted so that byte s is the
-  // scale of the block this lane half feeds in MFMA step s.
-  __device__ __forceinline__ void load_scales(int64_t kb0, int wm, int wn, int lane,
-                                              uint32_t* sar, uint32_t* sbr) {
-    const int g = lane >> 5, i = lane & 31;
+    const int i = lane & 31;
+    const int wm = wave & 1, wn = wave >> 1;
     const int64_t lda = K >> 5;
 #pragma unroll
     for (int f = 0; f < 4; f++) {
       int64_t m = m0 + 128 * wm + 32 * f + i;
       m = m < m_end ? m : m_end - 1;
-      sar[f] = load_scale4(sa + m * lda, kb0, nkb) >> (16 * g);
-    }
-#pragma unroll
-    for (int f = 0; f < 4; f++) {
+      srow_a[f] = m * lda;
       int64_t n = n0 + 128 * wn + 32 * f + i;
       n = n < N ? n : N - 1;
-      uint32_t v;
-      if (BMODE == GEMM_B_ROW)
-        v = load_scale4(sb + n * lda, kb0, nkb);
-      else if (BMODE == GEMM_B_TILE)
-        v = load_scale4(sb + (n >> 5) * lda, kb0, nkb);
-      else
-        v = load_scale4_t(sb, kb0, nkb, N >> 5, n >> 5);
-      sbr[f] = v >> (16 * g);
+      srow_b[f] = BMODE == GEMM_B_ROW ? n * lda : (BMODE == GEMM_B_TILE ? (n >> 5) * lda : (n >> 5));
+    }
+    if (BMODE == GEMM_B_TILE_T && FAST) {
+      // four consecutive tile columns from an aligned dword; a wave whose
+      // columns lie past N (its results are never stored) reads the last four
+      const int64_t c0 = (n0 + 128 * wn) >> 5, last = (N >> 5) - 4;
+      srow_b[0] = c0 < last ? c0 : last;
+    }
+  }
+
+  // buffer -> LDS loads of the K step starting at byte k0 into stage st:
+  // chunk u of A and of B for this wave (u = 0 .. CHUNKS-1).  Chunks at or
+  // past K read as zero (K is a multiple of 32, so whole 16-byte chunks are
+  // in or out), which also makes the loads of steps past the end harmless.
+  // With FAST (K a multiple of the K step) no real step is partial; the
+  // loads of steps past the end land in a stage that is never read.
+  // Transposed B needs no K check at all: rows at or past K lie beyond the
+  // end of its buffer.
+  __device__ __forceinline__ void dma_a(lds_u8* st, int64_t k0, int u, int wave, int lane) {
+    const int t = wave + 4 * u;
+    uint32_t off = voff_a + (uint32_t)k0 + u * a_step;
+    if (!FAST) {
+      const int lc = (lane & 7) ^ (lane >> 3);
+      off = (k0 + 16 * lc < K) ? off : OOB;
+    }
+    dma16(st + t * 1024, off, ra);
+  }
+
+  __device__ __forceinline__ void dma_b(lds_u8* st, int64_t k0, int u, int wave, int lane) {
+    const int t = wave + 4 * u;
+    if (BMODE == GEMM_B_TILE_T) {
+      const uint32_t off = voff_b + (uint32_t)k0 * (uint32_t)N + u * b_step;
+      dma16(st + A_TILE + t * 1024, off, rb);
+    } else {
+      uint32_t off = voff_b + (uint32_t)k0 + u * b_step;
+      if (!FAST) {
+        const int lc = (lane & 7) ^ (lane >> 3);
+        off = (k0 + 16 * lc < K) ? off : OOB;
+      }
+      dma16(st + A_TILE + t * 1024, off, rb);
+    }
+  }
+
+  __device__ __forceinline__ void issue_stage(lds_u8* st, int64_t k0, int wave, int lane) {
+#pragma unroll
+    for (int u = 0; u < CHUNKS; u++) dma_a(st, k0, u, wave, lane);
+#pragma unroll
+    for (int u = 0; u < CHUNKS; u++) dma_b(st, k0, u, wave, lane);
+  }
+
+  // Scale words of K step kb0 (blocks kb0 .. kb0+3).  load_scales fetches raw
+  // words (for the transposed 32x32 weight: four rows of the tile-scale
+  // array, one dword = the tiles of four consecutive fragments), and
+  // finish_scales turns them into one word per fragment, shifted so that
+  // byte s feeds MFMA half s for this lane's half of the wave.  FAST: K is a
+  // multiple of the K step (and, transposed, N a multiple of 128), so every
+  // word is one aligned dword; steps past the end load a dummy that is never
+  // used.
+  __device__ __forceinline__ uint32_t scale_word(const uint8_t* base, int64_t kb0) {
+    if (FAST) return *(const uint32_t*)(base + (kb0 < nkb ? kb0 : nkb - 4));
+    uint32_t r = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) r |= (uint32_t)(kb0 + i < nkb ? base[kb0 + i] : 0x7F) << (8 * i);
+    return r;
+  }
+
+  __device__ __forceinline__ void load_scales(int64_t kb0, uint32_t* ra_, uint32_t* rb_) {
+#pragma unroll
+    for (int f = 0; f < 4; f++) ra_[f] = scale_word(sa + srow_a[f], kb0);
+    if (BMODE == GEMM_B_TILE_T) {
+      const int64_t ld = N >> 5;
+      if (FAST) {
+        // row kb of the tile scales, tiles of fragments 0..3 (4 bytes)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int64_t kb = kb0 + i < nkb ? kb0 + i : nkb - 1;
+          rb_[i] = *(const uint32_t*)(sb + kb * ld + srow_b[0]);
+        }
+      } else {
+#pragma unroll
+        for (int f = 0; f < 4; f++) {
+          uint32_t v = 0;
+#pragma unroll
+          for (int i = 0; i < 4; i++)
+            v |= (uint32_t)(kb0 + i < nkb ? sb[(kb0 + i) * ld + srow_b[f]] : 0x7F) << (8 * i);
+          rb_[f] = v;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int f = 0; f < 4; f++) rb_[f] = scale_word(sb + srow_b[f], kb0);
+    }
+  }
+
+  __device__ __forceinline__ void finish_scales(int lane, const uint32_t* ra_, const uint32_t* rb_,
+                                                uint32_t* sar, uint32_t* sbr) {
+    const int sh = 16 * (lane >> 5);
+#pragma unroll
+    for (int f = 0; f < 4; f++) sar[f] = ra_[f] >> sh;
+    if (BMODE == GEMM_B_TILE_T && FAST) {
+      // 4x4 byte transpose: word f collects byte f of rows 0..3
+      const uint32_t lo01 = __builtin_amdgcn_perm(rb_[1], rb_[0], 0x05010400u);  // r0b0 r1b0 r0b1 r1b1
+      const uint32_t hi01 = __builtin_amdgcn_perm(rb_[1], rb_[0], 0x07030602u);  // r0b2 r1b2 r0b3 r1b3
+      const uint32_t lo23 = __builtin_amdgcn_perm(rb_[3], rb_[2], 0x05010400u);
+      const uint32_t hi23 = __builtin_amdgcn_perm(rb_[3], rb_[2], 0x07030602u);
+      uint32_t w[4];
+      w[0] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
+      w[1] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
+      w[2] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
+      w[3] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
+#pragma unroll
+      for (int f = 0; f < 4; f++) sbr[f] = w[f] >> sh;
+    } else {
+#pragma unroll
+      for (int f = 0; f < 4; f++) sbr[f] = rb_[f] >> sh;
     }
   }
 
   template <int S>
-  __device__ __forceinline__ void mma_step(const uint8_t* st, int wm, int wn, int lane,
-                                           const uint32_t* sar, const uint32_t* sbr,
-                                           v16f (&acc)[4][4]) {
+  __device__ __forceinline__ void read_frags(const lds_u8* st, int wm, int wn, int lane, v8i* af,
+                                             v8i* bf) {
     const int g = lane >> 5, i = lane & 31;
-    v8i af[4], bf[4];
 #pragma unroll
     for (int f = 0; f < 4; f++) af[f] = read_frag(st, 128 * wm + 32 * f + i, S, g);
 #pragma unroll
@@ -198,6 +297,11 @@ struct Tile {
       else
         bf[f] = read_frag(st + A_TILE, 128 * wn + 32 * f + i, S, g);
     }
+  }
+
+  template <int S>
+  __device__ __forceinline__ void mma(const v8i* af, const v8i* bf, const uint32_t* sar,
+                                      const uint32_t* sbr, v16f (&acc)[4][4]) {
 #pragma unroll
     for (int fn = 0; fn < 4; fn++)
 #pragma unroll
@@ -206,37 +310,91 @@ struct Tile {
             bf[fn], af[fm], acc[fn][fm], 0, 0, S, (int)sbr[fn], S, (int)sar[fm]);
   }
 
+  // LDS fragment reads and vector-memory loads issued per K half
+  static constexpr int DS_READS = BMODE == GEMM_B_TILE_T ? 8 + 16 : 16;
+  static constexpr int SCALE_LOADS = (BMODE == GEMM_B_TILE_T && !FAST) ? 4 + 16 : 8;
+
+  // Ask the scheduler for MFMA, LDS read, vector load, MFMA, ... so the
+  // MFMA pipe always has queued work while the loads are in flight.
+  template <int NDS, int NVM>
+  __device__ __forceinline__ static void interleave() {
+    constexpr int ds_per = (NDS + 15) / 16, vm_per = (NVM + 15) / 16;
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
+      if (ds_per) __builtin_amdgcn_sched_group_barrier(0x100, ds_per, 0);  // DS read
+      if (vm_per) __builtin_amdgcn_sched_group_barrier(0x020, vm_per, 0);  // VMEM read
+    }
+  }
+
+  // One K step on stage `cur`, prefetching into `nxt` (see the pipeline
+  // description above).
+  __device__ __forceinline__ void step(lds_u8* cur, lds_u8* nxt, int64_t kt, int wave, int wm,
+                                       int wn, int lane, uint32_t* sc_a, uint32_t* sc_b,
+                                       uint32_t* nx_a, uint32_t* nx_b, v8i* f0a, v8i* f0b,
+                                       v8i* f1a, v8i* f1b, v16f (&acc)[4][4]) {
+    // phase A: raw scales of step kt+1 land by the barrier
+    load_scales((kt + 1) * (BK / 32), nx_a, nx_b);
+    read_frags<1>(cur, wm, wn, lane, f1a, f1b);
+    mma<0>(f0a, f0b, sc_a, sc_b, acc);
+    interleave<DS_READS, SCALE_LOADS>();
+    wait_vm_all();  // this wave's loads of stage kt+1 have landed ...
+    __syncthreads();  // ... and every wave's; every wave is done reading `cur`
+    // keep the scale arithmetic below the barrier (it would otherwise be
+    // scheduled next to its load and wait on it)
+#pragma unroll
+    for (int f = 0; f < 4; f++) asm volatile("" : "+v"(nx_a[f]), "+v"(nx_b[f]));
+    // phase B: fragment reads of stage kt+1 and loads of stage kt+2 into `cur`
+    const int64_t k2 = (kt + 2) * BK;
+    const int g = lane >> 5, i = lane & 31;
+#pragma unroll
+    for (int f = 0; f < 4; f++) {
+      f0a[f] = read_frag(nxt, 128 * wm + 32 * f + i, 0, g);
+      dma_a(cur, k2, 2 * f, wave, lane);
+      dma_a(cur, k2, 2 * f + 1, wave, lane);
+    }
+#pragma unroll
+    for (int f = 0; f < 4; f++) {
+      if (BMODE == GEMM_B_TILE_T)
+        f0b[f] = read_frag_t(nxt + A_TILE, 128 * wn + 32 * f, 0, lane);
+      else
+        f0b[f] = read_frag(nxt + A_TILE, 128 * wn + 32 * f + i, 0, g);
+      dma_b(cur, k2, 2 * f, wave, lane);
+      dma_b(cur, k2, 2 * f + 1, wave, lane);
+    }
+    mma<1>(f1a, f1b, sc_a, sc_b, acc);
+    interleave<DS_READS, 0>();
+    finish_scales(lane, nx_a, nx_b, sc_a, sc_b);
+  }
+
   __device__ __forceinline__ void run() {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave & 1, wn = wave >> 1;
+    setup(wave, lane);
     v16f acc[4][4];
 #pragma unroll
     for (int x = 0; x < 4; x++)
 #pragma unroll
       for (int y = 0; y < 4; y++) acc[x][y] = (v16f){};
     const int64_t nk = (K + BK - 1) / BK;
-    uint32_t sar[4], sbr[4], sar_n[4], sbr_n[4];
-    load_stage(0);
-    load_scales(0, wm, wn, lane, sar_n, sbr_n);
-    store_stage(smem);
+    uint32_t sc_a[4], sc_b[4], nx_a[4], nx_b[4];
+    v8i f0a[4], f0b[4], f1a[4], f1b[4];
+
+    issue_stage(st0, 0, wave, lane);
+    load_scales(0, nx_a, nx_b);
+    wait_vm_all();
+    finish_scales(lane, nx_a, nx_b, sc_a, sc_b);
     __syncthreads();
-    for (int64_t kt = 0; kt < nk; kt++) {
-#pragma unroll
-      for (int f = 0; f < 4; f++) {
-        sar[f] = sar_n[f];
-        sbr[f] = sbr_n[f];
-      }
-      const bool more = kt + 1 < nk;
-      if (more) {
-        load_stage((kt + 1) * BK);
-        load_scales((kt + 1) * (BK / 32), wm, wn, lane, sar_n, sbr_n);
-      }
-      const uint8_t* st = smem + (kt & 1) * STAGE;
-      mma_step<0>(st, wm, wn, lane, sar, sbr, acc);
-      mma_step<1>(st, wm, wn, lane, sar, sbr, acc);
-      if (more) store_stage(smem + ((kt + 1) & 1) * STAGE);
-      __syncthreads();
+    issue_stage(st1, BK, wave, lane);
+    read_frags<0>(st0, wm, wn, lane, f0a, f0b);
+    int64_t kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      step(st0, st1, kt, wave, wm, wn, lane, sc_a, sc_b, nx_a, nx_b, f0a, f0b, f1a, f1b, acc);
+      step(st1, st0, kt + 1, wave, wm, wn, lane, sc_a, sc_b, nx_a, nx_b, f0a, f0b, f1a, f1b, acc);
     }
+    if (kt < nk)
+      step(st0, st1, kt, wave, wm, wn, lane, sc_a, sc_b, nx_a, nx_b, f0a, f0b, f1a, f1b, acc);
     // epilogue: FP32 -> BF16 (RNE), four consecutive n per lane and row
     const int g = lane >> 5, i = lane & 31;
     const bool vec_ok = (N & 3) == 0;
@@ -285,16 +443,17 @@ __device__ __forceinline__ void tile_of(int64_t bid, int64_t nm, int64_t nn, int
   nt = in / gsz;
 }
 
-template <int BMODE>
+template <int BMODE, bool FAST>
 __global__ void __launch_bounds__(NT)
 gemm_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa,
             const uint8_t* __restrict__ b, const uint8_t* __restrict__ sb, uint16_t* __restrict__ c,
             int64_t M, int64_t N, int64_t K) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t smem0[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t smem1[STAGE];
   const int64_t nm = (M + BM - 1) / BM, nn = (N + BN - 1) / BN;
   int64_t mt, nt;
   tile_of(blockIdx.x, nm, nn, mt, nt);
-  Tile<BMODE> t;
+  Tile<BMODE, FAST> t;
   t.a = a;
   t.sa = sa;
   t.b = b;
@@ -306,7 +465,8 @@ gemm_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa,
   t.N = N;
   t.K = K;
   t.nkb = K >> 5;
-  t.smem = smem;
+  t.st0 = (lds_u8*)smem0;
+  t.st1 = (lds_u8*)smem1;
   t.run();
 }
 
@@ -314,12 +474,14 @@ gemm_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa,
 // device-side offsets (clamped into [0, T] and made non-decreasing, so bad
 // offsets can never address outside the operands) and walks it with a static
 // stride.  Tile t -> (group g, m tile within g, n tile).
+template <bool FAST>
 __global__ void __launch_bounds__(NT)
 grouped_gemm_kernel(int64_t G, const int64_t* __restrict__ offsets, int64_t T, int64_t N,
                     int64_t K, const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa,
                     const uint8_t* __restrict__ b, const uint8_t* __restrict__ sb,
                     uint16_t* __restrict__ c) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t smem0[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t smem1[STAGE];
   __shared__ int64_t s_off[MAX_GROUPS + 1];
   __shared__ int64_t s_pre[MAX_GROUPS + 1];
   const int64_t nn = (N + BN - 1) / BN;
@@ -355,7 +517,7 @@ grouped_gemm_kernel(int64_t G, const int64_t* __restrict__ offsets, int64_t T, i
     const int64_t g = lo;
     const int64_t local = t - s_pre[g];
     const int64_t mt = local / nn, nt = local % nn;
-    Tile<GEMM_B_ROW> tl;
+    Tile<GEMM_B_ROW, FAST> tl;
     tl.a = a;
     tl.sa = sa;
     tl.b = b + g * N * K;
@@ -367,7 +529,8 @@ grouped_gemm_kernel(int64_t G, const int64_t* __restrict__ offsets, int64_t T, i
     tl.N = N;
     tl.K = K;
     tl.nkb = K >> 5;
-    tl.smem = smem;
+    tl.st0 = (lds_u8*)smem0;
+    tl.st1 = (lds_u8*)smem1;
     tl.run();
   }
 }
@@ -388,20 +551,23 @@ hipError_t launch_gemm(int bmode, int64_t M, int64_t N, int64_t K, const void* a
   const uint8_t *A = (const uint8_t*)a, *SA = (const uint8_t*)sa, *B = (const uint8_t*)b,
                 *SB = (const uint8_t*)sb;
   uint16_t* C = (uint16_t*)c;
+  const bool ka = (K % BK) == 0 && (bmode != GEMM_B_TILE_T || N % 128 == 0);
+#define MX_GEMM_LAUNCH(BM_, KA_)                                                              \
+  hipLaunchKernelGGL((gemm_kernel<BM_, KA_>), grid, block, 0, stream, A, SA, B, SB, C, M, N, K)
   switch (bmode) {
     case GEMM_B_ROW:
-      hipLaunchKernelGGL(gemm_kernel<GEMM_B_ROW>, grid, block, 0, stream, A, SA, B, SB, C, M, N, K);
+      if (ka) MX_GEMM_LAUNCH(GEMM_B_ROW, true); else MX_GEMM_LAUNCH(GEMM_B_ROW, false);
       break;
     case GEMM_B_TILE:
-      hipLaunchKernelGGL(gemm_kernel<GEMM_B_TILE>, grid, block, 0, stream, A, SA, B, SB, C, M, N, K);
+      if (ka) MX_GEMM_LAUNCH(GEMM_B_TILE, true); else MX_GEMM_LAUNCH(GEMM_B_TILE, false);
       break;
     case GEMM_B_TILE_T:
-      hipLaunchKernelGGL(gemm_kernel<GEMM_B_TILE_T>, grid, block, 0, stream, A, SA, B, SB, C, M, N,
-                         K);
+      if (ka) MX_GEMM_LAUNCH(GEMM_B_TILE_T, true); else MX_GEMM_LAUNCH(GEMM_B_TILE_T, false);
       break;
     default:
       return hipErrorInvalidValue;
   }
+#undef MX_GEMM_LAUNCH
   return hipGetLastError();
 }
 
@@ -415,9 +581,14 @@ hipError_t launch_grouped_gemm(int64_t G, const int64_t* offsets, int64_t T, int
   wgs = (wgs + 7) / 8 * 8;
   if (upper < wgs) wgs = (upper + 7) / 8 * 8;
   if (wgs < 8) wgs = 8;
-  hipLaunchKernelGGL(grouped_gemm_kernel, dim3((unsigned)wgs), dim3(NT), 0, stream, G, offsets, T,
-                     N, K, (const uint8_t*)a, (const uint8_t*)sa, (const uint8_t*)b,
-                     (const uint8_t*)sb, (uint16_t*)c);
+  if (K % BK == 0)
+    hipLaunchKernelGGL(grouped_gemm_kernel<true>, dim3((unsigned)wgs), dim3(NT), 0, stream, G,
+                       offsets, T, N, K, (const uint8_t*)a, (const uint8_t*)sa, (const uint8_t*)b,
+                       (const uint8_t*)sb, (uint16_t*)c);
+  else
+    hipLaunchKernelGGL(grouped_gemm_kernel<false>, dim3((unsigned)wgs), dim3(NT), 0, stream, G,
+                       offsets, T, N, K, (const uint8_t*)a, (const uint8_t*)sa, (const uint8_t*)b,
+                       (const uint8_t*)sb, (uint16_t*)c);
   return hipGetLastError();
 }
 
