@@ -37,6 +37,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) v2i lds_v2i;
 typedef __attribute__((address_space(3))) v4i lds_v4i;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int BM = 256;
@@ -46,7 +47,7 @@ constexpr int NT = 256;
 constexpr int A_TILE = BM * BK;           // 32 KB
 constexpr int B_TILE = BN * BK;           // 32 KB
 constexpr int STAGE = A_TILE + B_TILE;    // 64 KB
-constexpr int LDS_BYTES = 2 * STAGE;      // 128 KB
+constexpr int SCALE_TILE = 2 * 256 * 16; // A and B scale bytes of four K steps: 8 KB
 constexpr int CHUNKS = A_TILE / 16 / NT;  // 16-byte chunks per thread per operand: 8
 constexpr int MAX_GROUPS = 512;
 
@@ -115,8 +116,17 @@ constexpr uint32_t OOB = 0x80000000u;  // an offset past every tile buffer
 //     scale loads of step kt+2, MFMAs of half 1 on F1, LDS reads of half 0 of
 //     stage kt+1 into F0 interleaved.
 // The loop body has no branches so the scheduler can interleave freely.
+//
+// Scales.  With LDS_SCALES (K a multiple of 512, so the K loop is a whole
+// number of 4-step groups) the per-row scale bytes of four K steps are
+// staged through LDS like the operands: one 16-byte load per row every four
+// steps (rows cost one cache line per four steps instead of one per step),
+// read back per step with ds_read_u16 at the lane half's two blocks.  The
+// 32x32 weight scales are the same for all lanes of a fragment and are read
+// from global memory.  Otherwise every step loads scale words from global.
 template <int BMODE, bool FAST>
 struct Tile {
+  static constexpr bool LDS_SCALES = FAST;
   const uint8_t* __restrict__ a;
   const uint8_t* __restrict__ sa;
   const uint8_t* __restrict__ b;
@@ -125,8 +135,11 @@ struct Tile {
   int64_t m0, m_end, n0, N, K, nkb;
   lds_u8* st0;  // the two LDS stages (distinct arrays, so the compiler can
   lds_u8* st1;  // tell the loads into one from the reads of the other)
+  lds_u8* ss0;  // two scale tiles (LDS_SCALES): [256 rows][16 B] of A, then
+  lds_u8* ss1;  // the same of B, covering four K steps
 
-  u32x4 ra, rb;
+  u32x4 ra, rb, rsa, rsb;
+  uint32_t svoff;               // scale-tile load offset of this lane's row
   uint32_t voff_a, voff_b;      // per-lane offset of this lane's first chunk
   uint32_t a_step, b_step;      // offset between this wave's consecutive chunks
   int64_t srow_a[4], srow_b[4]; // scale row bases
@@ -159,6 +172,14 @@ struct Tile {
     const int i = lane & 31;
     const int wm = wave & 1, wn = wave >> 1;
     const int64_t lda = K >> 5;
+    if (LDS_SCALES) {
+      // scale tiles: wave w loads rows 64w .. 64w+63, one 16-byte chunk
+      // (four K steps) per lane; rows past the edge read as zero
+      rsa = make_rsrc(sa + m0 * lda, mrows * lda);
+      const int64_t nrows = (N - n0) < BN ? (N - n0) : BN;
+      rsb = make_rsrc(sb + n0 * lda, nrows * lda);
+      svoff = (uint32_t)((64 * wave + lane) * lda);
+    }
 #pragma unroll
     for (int f = 0; f < 4; f++) {
       int64_t m = m0 + 128 * wm + 32 * f + i;
@@ -232,9 +253,7 @@ struct Tile {
     return r;
   }
 
-  __device__ __forceinline__ void load_scales(int64_t kb0, uint32_t* ra_, uint32_t* rb_) {
-#pragma unroll
-    for (int f = 0; f < 4; f++) ra_[f] = scale_word(sa + srow_a[f], kb0);
+  __device__ __forceinline__ void load_scales_b(int64_t kb0, uint32_t* rb_) {
     if (BMODE == GEMM_B_TILE_T) {
       const int64_t ld = N >> 5;
       if (FAST) {
@@ -260,11 +279,14 @@ struct Tile {
     }
   }
 
-  __device__ __forceinline__ void finish_scales(int lane, const uint32_t* ra_, const uint32_t* rb_,
-                                                uint32_t* sar, uint32_t* sbr) {
-    const int sh = 16 * (lane >> 5);
+  __device__ __forceinline__ void load_scales(int64_t kb0, uint32_t* ra_, uint32_t* rb_) {
 #pragma unroll
-    for (int f = 0; f < 4; f++) sar[f] = ra_[f] >> sh;
+    for (int f = 0; f < 4; f++) ra_[f] = scale_word(sa + srow_a[f], kb0);
+    load_scales_b(kb0, rb_);
+  }
+
+  __device__ __forceinline__ void finish_scales_b(int lane, const uint32_t* rb_, uint32_t* sbr) {
+    const int sh = 16 * (lane >> 5);
     if (BMODE == GEMM_B_TILE_T && FAST) {
       // 4x4 byte transpose: word f collects byte f of rows 0..3
       const uint32_t lo01 = __builtin_amdgcn_perm(rb_[1], rb_[0], 0x05010400u);  // r0b0 r1b0 r0b1 r1b1
@@ -281,6 +303,34 @@ struct Tile {
     } else {
 #pragma unroll
       for (int f = 0; f < 4; f++) sbr[f] = rb_[f] >> sh;
+    }
+  }
+
+  __device__ __forceinline__ void finish_scales(int lane, const uint32_t* ra_, const uint32_t* rb_,
+                                                uint32_t* sar, uint32_t* sbr) {
+    const int sh = 16 * (lane >> 5);
+#pragma unroll
+    for (int f = 0; f < 4; f++) sar[f] = ra_[f] >> sh;
+    finish_scales_b(lane, rb_, sbr);
+  }
+
+  // LDS_SCALES: scale-tile loads of the 4-step group whose first block is
+  // kb0, and the per-step reads (two blocks per lane: 2g and 2g+1 of step q).
+  __device__ __forceinline__ void dma_scales(lds_u8* buf, int64_t kb0, int wave) {
+    dma16(buf + wave * 1024, svoff + (uint32_t)kb0, rsa);
+    if (BMODE == GEMM_B_ROW) dma16(buf + 4096 + wave * 1024, svoff + (uint32_t)kb0, rsb);
+  }
+
+  __device__ __forceinline__ void read_scales(const lds_u8* buf, int q, int wm, int wn, int lane,
+                                              uint32_t* sar, uint32_t* sbr) {
+    const int g = lane >> 5, i = lane & 31;
+#pragma unroll
+    for (int f = 0; f < 4; f++)
+      sar[f] = *(const lds_u16*)(buf + (128 * wm + 32 * f + i) * 16 + 4 * q + 2 * g);
+    if (BMODE == GEMM_B_ROW) {
+#pragma unroll
+      for (int f = 0; f < 4; f++)
+        sbr[f] = *(const lds_u16*)(buf + 4096 + (128 * wn + 32 * f + i) * 16 + 4 * q + 2 * g);
     }
   }
 
@@ -367,6 +417,59 @@ struct Tile {
     finish_scales(lane, nx_a, nx_b, sc_a, sc_b);
   }
 
+  // One K step with LDS-staged scales; U = kt % 4.  `sread` holds the scale
+  // tile of step kt+1; at U == 0 the tile of the next group is loaded into
+  // `sdma` (its previous contents were last read two barriers earlier).
+  template <int U>
+  __device__ __forceinline__ void step_ls(lds_u8* cur, lds_u8* nxt, const lds_u8* sread,
+                                          lds_u8* sdma, int64_t kt, int wave, int wm, int wn,
+                                          int lane, uint32_t* sc_a, uint32_t* sc_b,
+                                          uint32_t* nx_a, uint32_t* nx_b, v8i* f0a, v8i* f0b,
+                                          v8i* f1a, v8i* f1b, v16f (&acc)[4][4]) {
+    constexpr bool GB = BMODE != GEMM_B_ROW;  // B scales from global memory
+    // phase A
+    if (GB) load_scales_b((kt + 1) * (BK / 32), nx_b);
+    read_frags<1>(cur, wm, wn, lane, f1a, f1b);
+    mma<0>(f0a, f0b, sc_a, sc_b, acc);
+    interleave<DS_READS, GB ? 4 : 0>();
+    wait_vm_all();
+    __syncthreads();
+    if (GB) {
+#pragma unroll
+      for (int f = 0; f < 4; f++) asm volatile("" : "+v"(nx_b[f]));
+    }
+    // phase B
+    if (U == 0) dma_scales(sdma, (kt + 4) * (BK / 32), wave);
+    read_scales(sread, (U + 1) & 3, wm, wn, lane, nx_a, nx_b);
+    const int64_t k2 = (kt + 2) * BK;
+    const int g = lane >> 5, i = lane & 31;
+#pragma unroll
+    for (int f = 0; f < 4; f++) {
+      f0a[f] = read_frag(nxt, 128 * wm + 32 * f + i, 0, g);
+      dma_a(cur, k2, 2 * f, wave, lane);
+      dma_a(cur, k2, 2 * f + 1, wave, lane);
+    }
+#pragma unroll
+    for (int f = 0; f < 4; f++) {
+      if (BMODE == GEMM_B_TILE_T)
+        f0b[f] = read_frag_t(nxt + A_TILE, 128 * wn + 32 * f, 0, lane);
+      else
+        f0b[f] = read_frag(nxt + A_TILE, 128 * wn + 32 * f + i, 0, g);
+      dma_b(cur, k2, 2 * f, wave, lane);
+      dma_b(cur, k2, 2 * f + 1, wave, lane);
+    }
+    mma<1>(f1a, f1b, sc_a, sc_b, acc);
+    interleave<DS_READS + (GB ? 4 : 8), 0>();
+#pragma unroll
+    for (int f = 0; f < 4; f++) sc_a[f] = nx_a[f];
+    if (GB)
+      finish_scales_b(lane, nx_b, sc_b);
+    else {
+#pragma unroll
+      for (int f = 0; f < 4; f++) sc_b[f] = nx_b[f];
+    }
+  }
+
   __device__ __forceinline__ void run() {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -381,20 +484,46 @@ struct Tile {
     uint32_t sc_a[4], sc_b[4], nx_a[4], nx_b[4];
     v8i f0a[4], f0b[4], f1a[4], f1b[4];
 
-    issue_stage(st0, 0, wave, lane);
-    load_scales(0, nx_a, nx_b);
-    wait_vm_all();
-    finish_scales(lane, nx_a, nx_b, sc_a, sc_b);
-    __syncthreads();
-    issue_stage(st1, BK, wave, lane);
-    read_frags<0>(st0, wm, wn, lane, f0a, f0b);
-    int64_t kt = 0;
-    for (; kt + 1 < nk; kt += 2) {
-      step(st0, st1, kt, wave, wm, wn, lane, sc_a, sc_b, nx_a, nx_b, f0a, f0b, f1a, f1b, acc);
-      step(st1, st0, kt + 1, wave, wm, wn, lane, sc_a, sc_b, nx_a, nx_b, f0a, f0b, f1a, f1b, acc);
+    if (LDS_SCALES) {
+      // nk is a multiple of 4
+      issue_stage(st0, 0, wave, lane);
+      dma_scales(ss0, 0, wave);
+      if (BMODE != GEMM_B_ROW) load_scales_b(0, nx_b);
+      wait_vm_all();
+      __syncthreads();
+      read_scales(ss0, 0, wm, wn, lane, sc_a, sc_b);
+      if (BMODE != GEMM_B_ROW) finish_scales_b(lane, nx_b, sc_b);
+      issue_stage(st1, BK, wave, lane);
+      read_frags<0>(st0, wm, wn, lane, f0a, f0b);
+      for (int64_t j = 0; 4 * j < nk; j++) {
+        const int64_t kt = 4 * j;
+        lds_u8* scur = (j & 1) ? ss1 : ss0;
+        lds_u8* snxt = (j & 1) ? ss0 : ss1;
+        step_ls<0>(st0, st1, scur, snxt, kt, wave, wm, wn, lane, sc_a, sc_b, nx_a, nx_b, f0a, f0b,
+                   f1a, f1b, acc);
+        step_ls<1>(st1, st0, scur, snxt, kt + 1, wave, wm, wn, lane, sc_a, sc_b, nx_a, nx_b, f0a,
+                   f0b, f1a, f1b, acc);
+        step_ls<2>(st0, st1, scur, snxt, kt + 2, wave, wm, wn, lane, sc_a, sc_b, nx_a, nx_b, f0a,
+                   f0b, f1a, f1b, acc);
+        step_ls<3>(st1, st0, snxt, snxt, kt + 3, wave, wm, wn, lane, sc_a, sc_b, nx_a, nx_b, f0a,
+                   f0b, f1a, f1b, acc);
+      }
+    } else {
+      issue_stage(st0, 0, wave, lane);
+      load_scales(0, nx_a, nx_b);
+      wait_vm_all();
+      finish_scales(lane, nx_a, nx_b, sc_a, sc_b);
+      __syncthreads();
+      issue_stage(st1, BK, wave, lane);
+      read_frags<0>(st0, wm, wn, lane, f0a, f0b);
+      int64_t kt = 0;
+      for (; kt + 1 < nk; kt += 2) {
+        step(st0, st1, kt, wave, wm, wn, lane, sc_a, sc_b, nx_a, nx_b, f0a, f0b, f1a, f1b, acc);
+        step(st1, st0, kt + 1, wave, wm, wn, lane, sc_a, sc_b, nx_a, nx_b, f0a, f0b, f1a, f1b, acc);
+      }
+      if (kt < nk)
+        step(st0, st1, kt, wave, wm, wn, lane, sc_a, sc_b, nx_a, nx_b, f0a, f0b, f1a, f1b, acc);
     }
-    if (kt < nk)
-      step(st0, st1, kt, wave, wm, wn, lane, sc_a, sc_b, nx_a, nx_b, f0a, f0b, f1a, f1b, acc);
     // epilogue: FP32 -> BF16 (RNE), four consecutive n per lane and row
     const int g = lane >> 5, i = lane & 31;
     const bool vec_ok = (N & 3) == 0;
@@ -450,6 +579,7 @@ gemm_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa,
             int64_t M, int64_t N, int64_t K) {
   __shared__ __attribute__((aligned(16))) uint8_t smem0[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t smem1[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sscale[2 * SCALE_TILE];
   const int64_t nm = (M + BM - 1) / BM, nn = (N + BN - 1) / BN;
   int64_t mt, nt;
   tile_of(blockIdx.x, nm, nn, mt, nt);
@@ -467,6 +597,8 @@ gemm_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa,
   t.nkb = K >> 5;
   t.st0 = (lds_u8*)smem0;
   t.st1 = (lds_u8*)smem1;
+  t.ss0 = (lds_u8*)sscale;
+  t.ss1 = (lds_u8*)sscale + SCALE_TILE;
   t.run();
 }
 
@@ -482,6 +614,7 @@ grouped_gemm_kernel(int64_t G, const int64_t* __restrict__ offsets, int64_t T, i
                     uint16_t* __restrict__ c) {
   __shared__ __attribute__((aligned(16))) uint8_t smem0[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t smem1[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sscale[2 * SCALE_TILE];
   __shared__ int64_t s_off[MAX_GROUPS + 1];
   __shared__ int64_t s_pre[MAX_GROUPS + 1];
   const int64_t nn = (N + BN - 1) / BN;
@@ -531,6 +664,8 @@ grouped_gemm_kernel(int64_t G, const int64_t* __restrict__ offsets, int64_t T, i
     tl.nkb = K >> 5;
     tl.st0 = (lds_u8*)smem0;
     tl.st1 = (lds_u8*)smem1;
+    tl.ss0 = (lds_u8*)sscale;
+    tl.ss1 = (lds_u8*)sscale + SCALE_TILE;
     tl.run();
   }
 }
@@ -551,7 +686,7 @@ hipError_t launch_gemm(int bmode, int64_t M, int64_t N, int64_t K, const void* a
   const uint8_t *A = (const uint8_t*)a, *SA = (const uint8_t*)sa, *B = (const uint8_t*)b,
                 *SB = (const uint8_t*)sb;
   uint16_t* C = (uint16_t*)c;
-  const bool ka = (K % BK) == 0 && (bmode != GEMM_B_TILE_T || N % 128 == 0);
+  const bool ka = (K % (4 * BK)) == 0 && (bmode != GEMM_B_TILE_T || N % 128 == 0);
 #define MX_GEMM_LAUNCH(BM_, KA_)                                                              \
   hipLaunchKernelGGL((gemm_kernel<BM_, KA_>), grid, block, 0, stream, A, SA, B, SB, C, M, N, K)
   switch (bmode) {
@@ -581,7 +716,7 @@ hipError_t launch_grouped_gemm(int64_t G, const int64_t* offsets, int64_t T, int
   wgs = (wgs + 7) / 8 * 8;
   if (upper < wgs) wgs = (upper + 7) / 8 * 8;
   if (wgs < 8) wgs = 8;
-  if (K % BK == 0)
+  if (K % (4 * BK) == 0)
     hipLaunchKernelGGL(grouped_gemm_kernel<true>, dim3((unsigned)wgs), dim3(NT), 0, stream, G,
                        offsets, T, N, K, (const uint8_t*)a, (const uint8_t*)sa, (const uint8_t*)b,
                        (const uint8_t*)sb, (uint16_t*)c);
