@@ -23,8 +23,7 @@
 // Workgroup tile 256 (M) x 256 (N), K step 128 bytes, four waves of 128x128
 // (16 accumulators of 32x32 each).  Both operands are staged through a
 // double-buffered LDS tile whose 16-byte chunks are XOR-swizzled by row, so
-// the fragment reads (8 rows at one column per 128 bytes of LDS bandwidth)
-// are conflict-free.
+// the fragment reads are free of bank conflicts.
 #include "mx_device.h"
 #include "mx_kernels.h"
 
@@ -48,12 +47,21 @@ constexpr int A_TILE = BM * BK;           // 32 KB
 constexpr int B_TILE = BN * BK;           // 32 KB
 constexpr int STAGE = A_TILE + B_TILE;    // 64 KB
 constexpr int SCALE_TILE = 2 * 256 * 16; // A and B scale bytes of four K steps: 8 KB
+constexpr int PF_DIST = 3;                // L2 prefetch distance, in K steps
+constexpr int GM_TILES = 8;               // tile grouping along M (tile_of)
 constexpr int CHUNKS = A_TILE / 16 / NT;  // 16-byte chunks per thread per operand: 8
 constexpr int MAX_GROUPS = 512;
 
+// Row-major LDS tiles with 128-byte rows keep 16-byte chunk c of row r at
+// physical chunk c ^ ((r >> 1) & 7).  gfx950 LDS serves 256 bytes (64
+// banks) per cycle, i.e. 16 lanes of a 16-byte read; the 16 lanes of a
+// fragment read take rows r .. r+15 at one logical chunk, and this swizzle
+// puts them in 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
 // Fragment of 32 rows x 64 K from a row-major LDS tile (128-byte rows).
 __device__ __forceinline__ v8i read_frag(const lds_u8* tile, int row, int s, int g) {
-  const int x = row & 7;
+  const int x = swz(row);
   v4i lo = *(const lds_v4i*)(tile + row * BK + (((2 * s + g) ^ x) << 4));
   v4i hi = *(const lds_v4i*)(tile + row * BK + (((4 + 2 * s + g) ^ x) << 4));
   return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
@@ -66,9 +74,12 @@ __device__ __forceinline__ v8i read_frag(const lds_u8* tile, int row, int s, int
 __device__ __forceinline__ v8i read_frag_t(const lds_u8* tile, int nb, int s, int lane) {
   const int g = lane >> 5, q = (lane >> 4) & 1, r = (lane & 15) >> 1, hh = lane & 1;
   // row k = k_const + 16g + r with k_const a multiple of 8, so k & 7 = r and
-  // the swizzled chunk is lane-only; every piece is base + a constant offset
+  // the swizzled chunk is lane-only; every piece is base + a constant offset.
+  // Chunk c of row k sits at physical chunk c ^ 2(k & 7): the two 16-lane
+  // groups served together read chunks c, c+1 (c even) of the same 8 rows,
+  // which land on 16 distinct 16-byte bank groups.
   const int ncol = nb + 16 * q + 8 * hh;
-  const lds_u8* base = tile + (16 * g + r) * 256 + (((ncol >> 4) ^ r) << 4) + (ncol & 15);
+  const lds_u8* base = tile + (16 * g + r) * 256 + (((ncol >> 4) ^ (2 * r)) << 4) + (ncol & 15);
   v2i p[4];
 #pragma unroll
   for (int t = 0; t < 4; t++) {
@@ -104,6 +115,20 @@ __device__ __forceinline__ void dma16(const lds_u8* lds, uint32_t voffset, u32x4
 // s_waitcnt vmcnt(0) (expcnt, lgkmcnt left at their maxima), as a builtin so
 // the compiler knows every earlier vector-memory load has completed.
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(2): everything but the two most recent vector-memory ops
+// (the L2 prefetches, which nobody waits for) has completed.
+__device__ __forceinline__ void wait_vm_but_prefetch() { __builtin_amdgcn_s_waitcnt(0x0F72); }
+
+// L2 prefetch: one dword per lane (one 128-byte line per row) dropped into a
+// scratch LDS area that is never read.  LDS-DMA has no register destination,
+// so nothing in the kernel can race with the late arrival.
+__device__ __forceinline__ void prefetch_lines(const lds_u8* scratch, uint32_t voffset, u32x4 rsrc) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)scratch);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(m0), "v"(voffset), "s"(rsrc)
+               : "memory");
+}
 
 constexpr uint32_t OOB = 0x80000000u;  // an offset past every tile buffer
 
@@ -140,6 +165,12 @@ struct Tile {
 
   u32x4 ra, rb, rsa, rsb;
   uint32_t svoff;               // scale-tile load offset of this lane's row
+  // L2 prefetch (B_ROW with LDS_SCALES): the first workgroup of each
+  // concurrently running group to need a K slice fetches it PF_DIST steps
+  // ahead of use; pf_a / pf_b are 0 for the operands this workgroup
+  // prefetches and OOB (no memory access) otherwise.
+  lds_u8* pf_scratch;           // 2 KB
+  uint32_t pf_row, pf_a, pf_b;
   uint32_t voff_a, voff_b;      // per-lane offset of this lane's first chunk
   uint32_t a_step, b_step;      // offset between this wave's consecutive chunks
   int64_t srow_a[4], srow_b[4]; // scale row bases
@@ -148,25 +179,26 @@ struct Tile {
     const int64_t mrows = m_end - m0;
     ra = make_rsrc(a + m0 * K, mrows * K);
     // A: instruction t = wave + 4u covers LDS rows 8t .. 8t+7 (1 KB); lane i
-    // lands in row 8t + i/8 at physical chunk i%8, holding logical chunk
-    // (i%8) ^ (i/8) of that row.
-    voff_a = (uint32_t)((8 * wave + (lane >> 3)) * K + 16 * ((lane & 7) ^ (lane >> 3)));
+    // lands in row r = 8t + i/8 at physical chunk i%8, holding logical chunk
+    // (i%8) ^ swz(r); swz(r) = (4 wave + i/16) & 7 does not depend on u.
+    const int sw = (4 * wave + (lane >> 4)) & 7;
+    voff_a = (uint32_t)((8 * wave + (lane >> 3)) * K + 16 * ((lane & 7) ^ sw));
     a_step = (uint32_t)(32 * K);
     if (BMODE == GEMM_B_TILE_T) {
       // B stored [K][N]; tile columns n0 .. n0+255.  Instruction t covers LDS
       // rows (k) 4t .. 4t+3 of 256 bytes; lane i -> row 4t + i/16, physical
-      // chunk i%16 holding logical chunk (i%16) ^ (row & 7).
+      // chunk i%16 holding logical chunk (i%16) ^ 2(row & 7).
       // Columns past N feed only outputs that are never stored, and the
       // buffer ends with the weight, so they need no mask.
       rb = make_rsrc(b + n0, (K - 1) * N + (N - n0));
       const int krow = 4 * wave + (lane >> 4);
-      const int lc = (lane & 15) ^ (krow & 7);
+      const int lc = (lane & 15) ^ (2 * (krow & 7));
       voff_b = (uint32_t)(krow * N + 16 * lc);
       b_step = (uint32_t)(16 * N);
     } else {
       const int64_t nrows = (N - n0) < BN ? (N - n0) : BN;
       rb = make_rsrc(b + n0 * K, nrows * K);
-      voff_b = (uint32_t)((8 * wave + (lane >> 3)) * K + 16 * ((lane & 7) ^ (lane >> 3)));
+      voff_b = (uint32_t)((8 * wave + (lane >> 3)) * K + 16 * ((lane & 7) ^ sw));
       b_step = (uint32_t)(32 * K);
     }
     const int i = lane & 31;
@@ -180,6 +212,7 @@ struct Tile {
       rsb = make_rsrc(sb + n0 * lda, nrows * lda);
       svoff = (uint32_t)((64 * wave + lane) * lda);
     }
+    pf_row = (uint32_t)((64 * wave + lane) * K);
 #pragma unroll
     for (int f = 0; f < 4; f++) {
       int64_t m = m0 + 128 * wm + 32 * f + i;
@@ -209,7 +242,7 @@ struct Tile {
     const int t = wave + 4 * u;
     uint32_t off = voff_a + (uint32_t)k0 + u * a_step;
     if (!FAST) {
-      const int lc = (lane & 7) ^ (lane >> 3);
+      const int lc = (lane & 7) ^ ((4 * wave + (lane >> 4)) & 7);
       off = (k0 + 16 * lc < K) ? off : OOB;
     }
     dma16(st + t * 1024, off, ra);
@@ -223,7 +256,7 @@ struct Tile {
     } else {
       uint32_t off = voff_b + (uint32_t)k0 + u * b_step;
       if (!FAST) {
-        const int lc = (lane & 7) ^ (lane >> 3);
+        const int lc = (lane & 7) ^ ((4 * wave + (lane >> 4)) & 7);
         off = (k0 + 16 * lc < K) ? off : OOB;
       }
       dma16(st + A_TILE + t * 1024, off, rb);
@@ -432,7 +465,10 @@ struct Tile {
     read_frags<1>(cur, wm, wn, lane, f1a, f1b);
     mma<0>(f0a, f0b, sc_a, sc_b, acc);
     interleave<DS_READS, GB ? 4 : 0>();
-    wait_vm_all();
+    if (GB)
+      wait_vm_all();
+    else
+      wait_vm_but_prefetch();
     __syncthreads();
     if (GB) {
 #pragma unroll
@@ -457,6 +493,11 @@ struct Tile {
         f0b[f] = read_frag(nxt + A_TILE, 128 * wn + 32 * f + i, 0, g);
       dma_b(cur, k2, 2 * f, wave, lane);
       dma_b(cur, k2, 2 * f + 1, wave, lane);
+    }
+    if (!GB) {
+      const uint32_t kp = (uint32_t)((kt + PF_DIST) * BK);
+      prefetch_lines(pf_scratch + wave * 512, (pf_row + kp) | pf_a, ra);
+      prefetch_lines(pf_scratch + wave * 512 + 256, (pf_row + kp) | pf_b, rb);
     }
     mma<1>(f1a, f1b, sc_a, sc_b, acc);
     interleave<DS_READS + (GB ? 4 : 8), 0>();
@@ -563,7 +604,7 @@ __device__ __forceinline__ void tile_of(int64_t bid, int64_t nm, int64_t nn, int
   const int64_t x = bid & 7, local = bid >> 3;
   const int64_t per = total >> 3, rem = total & 7;
   const int64_t t = x * per + (x < rem ? x : rem) + local;
-  constexpr int64_t GM = 8;
+  constexpr int64_t GM = GM_TILES;
   const int64_t group = t / (GM * nn);
   const int64_t first = group * GM;
   const int64_t gsz = (nm - first) < GM ? (nm - first) : GM;
@@ -580,6 +621,7 @@ gemm_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa,
   __shared__ __attribute__((aligned(16))) uint8_t smem0[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t smem1[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t sscale[2 * SCALE_TILE];
+  __shared__ __attribute__((aligned(16))) uint8_t spf[2048];
   const int64_t nm = (M + BM - 1) / BM, nn = (N + BN - 1) / BN;
   int64_t mt, nt;
   tile_of(blockIdx.x, nm, nn, mt, nt);
@@ -599,6 +641,12 @@ gemm_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa,
   t.st1 = (lds_u8*)smem1;
   t.ss0 = (lds_u8*)sscale;
   t.ss1 = (lds_u8*)sscale + SCALE_TILE;
+  // tile_of runs GM m-tiles x (32 / GM) n-tiles per XCD at a time: A slices
+  // are first needed by n-tiles at multiples of 32 / GM, B slices by m-tiles
+  // at multiples of GM
+  t.pf_scratch = (lds_u8*)spf;
+  t.pf_a = (nt % (32 / GM_TILES) == 0) ? 0u : OOB;
+  t.pf_b = (mt % GM_TILES == 0) ? 0u : OOB;
   t.run();
 }
 
@@ -615,6 +663,7 @@ grouped_gemm_kernel(int64_t G, const int64_t* __restrict__ offsets, int64_t T, i
   __shared__ __attribute__((aligned(16))) uint8_t smem0[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t smem1[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t sscale[2 * SCALE_TILE];
+  __shared__ __attribute__((aligned(16))) uint8_t spf[2048];
   __shared__ int64_t s_off[MAX_GROUPS + 1];
   __shared__ int64_t s_pre[MAX_GROUPS + 1];
   const int64_t nn = (N + BN - 1) / BN;
@@ -666,6 +715,11 @@ grouped_gemm_kernel(int64_t G, const int64_t* __restrict__ offsets, int64_t T, i
     tl.st1 = (lds_u8*)smem1;
     tl.ss0 = (lds_u8*)sscale;
     tl.ss1 = (lds_u8*)sscale + SCALE_TILE;
+    // 32 consecutive tiles (n fastest) run together on an XCD: A slices are
+    // first needed by n-tile 0, B slices by every other m-tile
+    tl.pf_scratch = (lds_u8*)spf;
+    tl.pf_a = nt == 0 ? 0u : OOB;
+    tl.pf_b = (mt & 1) == 0 ? 0u : OOB;
     tl.run();
   }
 }
