@@ -191,35 +191,41 @@ def run_step(L, stack, b, moe, mb, d):
 
 def cpu_baseline(W, x_dev, w_dev, budget_s):
     """The oracle (untuned) on a bounded sample of the step: dual-axis
-    quantisation of the first 64 token rows of the up-projection input and
-    of leading rows of its weight (the same bytes the GPU step uses), then
-    the binary64 GEMM of those rows (the up-projection fprop, K = hidden)."""
+    quantisation of leading token rows of the up-projection input and of
+    leading rows of its weight (the same bytes the GPU step uses), then the
+    binary64 GEMM of those rows (the up-projection fprop, K = hidden).  The
+    sample is sized from a short calibration run to about `budget_s`."""
     import numpy as np
     import oracle
     oracle.lib()
     nthreads = oracle.num_threads()
+    H = x_dev.shape[1]
+    # calibration: 64 x 512 outputs
     xb = W.bf16_bits(x_dev[:64])
-    wb = W.bf16_bits(w_dev[:2048])
-    H = xb.shape[1]
-    # calibrate on 256 weight rows, then size the sample to the budget
+    wb = W.bf16_bits(w_dev[:512])
     t0 = time.perf_counter()
     qa, sa = oracle.quant_row(xb)
-    qb, sb = oracle.quant_row(wb[:256])
+    qb, sb = oracle.quant_row(wb)
     oracle.gemm(qa, sa, qb, sb)
-    dt = time.perf_counter() - t0
-    ncols = int(min(wb.shape[0], max(256, 256 * budget_s / max(dt, 1e-3))))
-    ncols = (ncols // 32) * 32
+    rate = 64 * 512 / max(time.perf_counter() - t0, 1e-3)      # outputs per second
+    want = rate * budget_s
+    n = int(min(w_dev.shape[0], max(512, want / 256)))
+    n -= n % 32
+    m = int(min(x_dev.shape[0], 4096, max(64, want / n)))
+    m -= m % 32
+    xb = np.ascontiguousarray(W.bf16_bits(x_dev[:m]))
+    wb = np.ascontiguousarray(W.bf16_bits(w_dev[:n]))
     t0 = time.perf_counter()
-    qa, sa, _, _ = oracle.quant_dual(np.ascontiguousarray(xb))
-    qb, sb, _, _ = oracle.quant_dual(np.ascontiguousarray(wb[:ncols]))
+    qa, sa, _, _ = oracle.quant_dual(xb)
+    qb, sb, _, _ = oracle.quant_dual(wb)
     oracle.gemm(qa, sa, qb, sb)
     dt = time.perf_counter() - t0
-    flops = 2.0 * qa.shape[0] * ncols * H
+    flops = 2.0 * m * n * H
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": nthreads,
             "kind": "oracle",
-            "sample": f"dual-axis quantisation of {qa.shape[0]} token rows and {ncols} weight rows "
-                      f"(K={H}) of the up projection, then the binary64 GEMM of the "
-                      f"{qa.shape[0]}x{ncols} fprop outputs; {dt:.1f} s"}
+            "sample": f"dual-axis quantisation of {m} token rows and {n} weight rows (K={H}) of "
+                      f"the up projection, then the binary64 GEMM of the {m}x{n} fprop outputs; "
+                      f"{dt:.1f} s"}
 
 
 def main():
