@@ -111,6 +111,8 @@ mx_status mx_quant(mx_quant_mode mode, const void* x, int64_t rows, int64_t cols
     return fail(MX_ERR_UNSUPPORTED_SHAPE, "cols %lld is not a multiple of 32", (long long)cols);
   if (mode != MX_QUANT_ROW_1x32 && rows % 32 != 0)
     return fail(MX_ERR_UNSUPPORTED_SHAPE, "rows %lld is not a multiple of 32", (long long)rows);
+  if (mode != MX_QUANT_ROW_1x32 && (cols + 127) / 128 > 65535)
+    return fail(MX_ERR_UNSUPPORTED_SHAPE, "cols %lld exceeds the column-tile grid", (long long)cols);
   if (rows == 0 || cols == 0) return MX_OK;
   if (!x) return fail(MX_ERR_INVALID_ARG, "x is NULL");
   if (need_row && (!q || !s)) return fail(MX_ERR_INVALID_ARG, "q and s are required for this mode");

@@ -24,6 +24,7 @@ __device__ __forceinline__ uint32_t pair_absmax(uint32_t w) {
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // 16-byte streaming load (read once, no reuse expected).
 __device__ __forceinline__ uint4 load_stream16(const void* p) {

@@ -65,8 +65,11 @@ quant_row_kernel(const uint4* __restrict__ x, uint2* __restrict__ q, uint8_t* __
 // - a row block (32 columns) spans the 4 lanes h = 4b .. 4b+3 of one quad,
 // - a column block (32 rows) spans lanes h, h+8, ..., h+56 (xor 8, 16, 32),
 // - a 32x32 tile is one half of the wave (h < 4 or h >= 4).
-// Column outputs go to q_t[c][r] as one dword (4 rows of one column) per
-// lane and column; a workgroup writes whole 128-byte rows of q_t.
+// The column and dual modes stage their outputs in LDS (row payload
+// [128 rows][128 B], column payload [128 columns][128 B], 16-byte chunks
+// XOR-swizzled against bank conflicts, and both scale blocks) and then write
+// every output row of the tile as whole 128-byte lines with 16-byte stores
+// and the scales as dwords, instead of 8-, 4- and 1-byte pieces.
 // ---------------------------------------------------------------------------
 constexpr int TILE_THREADS = 512;
 constexpr int TILE_ROWS = 128;
@@ -74,24 +77,32 @@ constexpr int TILE_COLS = 128;
 
 enum TileMode { TILE_COL = 1, TILE_DUAL = 2, TILE_BLOCK32 = 3 };
 
+typedef __attribute__((address_space(3))) uint8_t lds8;
+
+// LDS tiles of 128 rows x 128 bytes; chunk k of row r lives at chunk k ^ sw(r).
+__device__ __forceinline__ int row_chunk(int r, int k) { return k ^ ((r >> 2) & 7); }
+__device__ __forceinline__ int col_chunk(int c, int k) { return k ^ ((c >> 3) & 7); }
+
 template <int MODE>
 __global__ void __launch_bounds__(TILE_THREADS)
 quant_tile_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C, uint8_t* __restrict__ q,
                   uint8_t* __restrict__ s, uint8_t* __restrict__ qt, uint8_t* __restrict__ st) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 3, h = lane & 7;
-  const int64_t r0 = (int64_t)blockIdx.x * TILE_ROWS + 32 * (wave >> 1);
-  const int64_t c0 = (int64_t)blockIdx.y * TILE_COLS + 64 * (wave & 1);
-  if (r0 >= R || c0 >= C) return;  // whole wave out of range (R, C % 32 == 0)
-  const int64_t c = c0 + 8 * h;
-  const bool live = c < C;  // C % 32 == 0: whole quads are live or dead
+  const int wr = wave >> 1, wc = wave & 1;
+  const int64_t R0 = (int64_t)blockIdx.x * TILE_ROWS, C0 = (int64_t)blockIdx.y * TILE_COLS;
+  const int64_t r0 = R0 + 32 * wr;
+  const int64_t c = C0 + 64 * wc + 8 * h;
+  // R, C are multiples of 32: a wave's 32 rows are all in or all out, and
+  // whole quads of columns are in or out
+  const bool live = r0 < R && c < C;
   uint4 v[4];
 #pragma unroll
   for (int i = 0; i < 4; i++)
-    v[i] = live ? load_stream16(x + (r0 + 4 * g + i) * C + c)
-                : make_uint4(0, 0, 0, 0);
+    v[i] = live ? load_stream16(x + (r0 + 4 * g + i) * C + c) : make_uint4(0, 0, 0, 0);
 
   if (MODE == TILE_BLOCK32) {
+    if (r0 >= R) return;  // no barrier below
     uint32_t m = umax(umax(chunk_absmax(v[0]), chunk_absmax(v[1])),
                       umax(chunk_absmax(v[2]), chunk_absmax(v[3])));
     m = quad_max(m);
@@ -107,15 +118,26 @@ quant_tile_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C, uint8_t*
     return;
   }
 
+  __shared__ __attribute__((aligned(16))) uint8_t lq[TILE_ROWS * 128];   // row payload
+  __shared__ __attribute__((aligned(16))) uint8_t lqt[TILE_COLS * 128];  // column payload
+  __shared__ __attribute__((aligned(16))) uint8_t ls[TILE_ROWS * 4];     // row scales
+  __shared__ __attribute__((aligned(16))) uint8_t lst[TILE_COLS * 4];    // column scales
+  lds8* LQ = (lds8*)lq;
+  lds8* LQT = (lds8*)lqt;
+  lds8* LS = (lds8*)ls;
+  lds8* LST = (lds8*)lst;
+  const int rl = 32 * wr + 4 * g;        // local row of this lane's first row
+  const int cl = 64 * wc + 8 * h;        // local column of this lane's first column
+
   if (MODE == TILE_DUAL) {
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      uint32_t sb = scale_byte(quad_max(chunk_absmax(v[i])));
-      if (live) {
-        int64_t r = r0 + 4 * g + i;
-        *(uint2*)(q + r * C + c) = cvt8(v[i], sb);
-        if ((h & 3) == 0) s[r * (C >> 5) + (c >> 5)] = (uint8_t)sb;
-      }
+      const uint32_t sb = scale_byte(quad_max(chunk_absmax(v[i])));
+      const int r = rl + i;
+      const uint2 o = cvt8(v[i], sb);
+      *(__attribute__((address_space(3))) u32x2*)(LQ + r * 128 + row_chunk(r, cl >> 4) * 16 +
+                                                   (cl & 15)) = (u32x2){o.x, o.y};
+      if ((h & 3) == 0) LS[r * 4 + (cl >> 5)] = (uint8_t)sb;
     }
   }
 
@@ -138,25 +160,66 @@ quant_tile_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C, uint8_t*
     sbc[2 * k] = scale_byte(cm[k] & 0xFFFFu);
     sbc[2 * k + 1] = scale_byte(cm[k] >> 16);
   }
-  if (!live) return;
   const uint32_t* w0 = (const uint32_t*)&v[0];
   const uint32_t* w1 = (const uint32_t*)&v[1];
   const uint32_t* w2 = (const uint32_t*)&v[2];
   const uint32_t* w3 = (const uint32_t*)&v[3];
-  const int64_t rq = r0 + 4 * g;
 #pragma unroll
   for (int j = 0; j < 8; j++) {
     const int k = j >> 1;
-    uint32_t p01 = (j & 1) ? pair_hi(w0[k], w1[k]) : pair_lo(w0[k], w1[k]);
-    uint32_t p23 = (j & 1) ? pair_hi(w2[k], w3[k]) : pair_lo(w2[k], w3[k]);
-    uint32_t out = sbc[j] == 0xFFu ? 0x7F7F7F7Fu : cvt4(p01, p23, cvt_scale(sbc[j]));
-    *(uint32_t*)(qt + (c + j) * R + rq) = out;
+    const uint32_t p01 = (j & 1) ? pair_hi(w0[k], w1[k]) : pair_lo(w0[k], w1[k]);
+    const uint32_t p23 = (j & 1) ? pair_hi(w2[k], w3[k]) : pair_lo(w2[k], w3[k]);
+    const uint32_t out = sbc[j] == 0xFFu ? 0x7F7F7F7Fu : cvt4(p01, p23, cvt_scale(sbc[j]));
+    const int cc = cl + j;  // local column; 4 rows rl .. rl+3 of it
+    *(__attribute__((address_space(3))) uint32_t*)(LQT + cc * 128 + col_chunk(cc, rl >> 4) * 16 +
+                                                    (rl & 15)) = out;
   }
-  // lane g stores the scale of column 8h + g
+  // lane g keeps the scale of column cl + g
   uint32_t mine = sbc[0];
 #pragma unroll
   for (int j = 1; j < 8; j++) mine = (g == j) ? sbc[j] : mine;
-  st[(c + g) * (R >> 5) + (r0 >> 5)] = (uint8_t)mine;
+  LST[(cl + g) * 4 + wr] = (uint8_t)mine;
+  __syncthreads();
+
+  // write out: 16-byte chunks, 8 lanes per 128-byte output row
+  const int t = threadIdx.x;
+  const int64_t rows_here = (R - R0) < TILE_ROWS ? (R - R0) : TILE_ROWS;
+  const int64_t cols_here = (C - C0) < TILE_COLS ? (C - C0) : TILE_COLS;
+#pragma unroll
+  for (int u = 0; u < 2; u++) {
+    const int id = t + TILE_THREADS * u;
+    const int row = id >> 3, k = id & 7;
+    if (row < cols_here && 16 * k < rows_here) {  // column payload -> q_t rows
+      const u32x4 d = *(const __attribute__((address_space(3))) u32x4*)(
+          LQT + row * 128 + col_chunk(row, k) * 16);
+      __builtin_nontemporal_store(d, (u32x4*)(qt + (C0 + row) * R + R0 + 16 * k));
+    }
+    if (MODE == TILE_DUAL && row < rows_here && 16 * k < cols_here) {  // row payload -> q rows
+      const u32x4 d = *(const __attribute__((address_space(3))) u32x4*)(
+          LQ + row * 128 + row_chunk(row, k) * 16);
+      __builtin_nontemporal_store(d, (u32x4*)(q + (R0 + row) * C + C0 + 16 * k));
+    }
+  }
+  // scales: four consecutive blocks per row / column
+  if (t < TILE_COLS && t < cols_here) {
+    uint8_t* dst = st + (C0 + t) * (R >> 5) + (R0 >> 5);
+    const int nb = (int)(rows_here >> 5);
+    if (nb == 4 && ((uintptr_t)dst & 3) == 0) {
+      *(uint32_t*)dst = *(const __attribute__((address_space(3))) uint32_t*)(LST + t * 4);
+    } else {
+      for (int b = 0; b < nb; b++) dst[b] = LST[t * 4 + b];
+    }
+  }
+  if (MODE == TILE_DUAL && t >= 256 && t - 256 < rows_here) {
+    const int r = t - 256;
+    uint8_t* dst = s + (R0 + r) * (C >> 5) + (C0 >> 5);
+    const int nb = (int)(cols_here >> 5);
+    if (nb == 4 && ((uintptr_t)dst & 3) == 0) {
+      *(uint32_t*)dst = *(const __attribute__((address_space(3))) uint32_t*)(LS + r * 4);
+    } else {
+      for (int b = 0; b < nb; b++) dst[b] = LS[r * 4 + b];
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
