@@ -23,6 +23,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -41,8 +42,11 @@ def parse():
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--layers", type=int, default=4)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=15.0,
+    p.add_argument("--cpu-seconds", type=float, default=20.0,
                    help="rough budget for the oracle sample")
+    p.add_argument("--calibration-copy", action="store_true",
+                   help="run one plain 1 GiB device-to-device copy before warm-up (untimed), the "
+                        "reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters to bytes")
     return p.parse_args()
 
 
@@ -93,6 +97,26 @@ class Launcher:
 
 def _p(t):
     return 0 if t is None else t.data_ptr()
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemm_row_hbm_traffic.md")
+GEMM_SOURCE = os.path.join(ROOT, "mxfp8_microscaled_precision_amd", "csrc", "gemm.hip")
+
+
+def gemm_traffic():
+    """HBM bytes per launch of the 1x32 GEMM kernel from the committed
+    FETCH_SIZE / WRITE_SIZE counter summary, or (None, None) when that summary
+    is missing or was taken from a different gemm.hip."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+        src = open(GEMM_SOURCE, "rb").read()
+    except OSError:
+        return None, None
+    fields = dict(re.findall(r"^(\w+): (\S+)$", text, re.M))
+    if fields.get("source_sha256") != hashlib.sha256(src).hexdigest():
+        return None, None
+    return int(fields["traffic_bytes_per_launch"]), int(fields["algorithmic_bytes_per_launch"])
 
 
 def build_workload(torch, W, layers):
@@ -200,14 +224,15 @@ def cpu_baseline(W, x_dev, w_dev, budget_s):
     oracle.lib()
     nthreads = oracle.num_threads()
     H = x_dev.shape[1]
-    # calibration: 64 x 512 outputs
-    xb = W.bf16_bits(x_dev[:64])
-    wb = W.bf16_bits(w_dev[:512])
+    # calibration: 256 x 1024 outputs (large enough that thread start-up
+    # does not dominate)
+    xb = W.bf16_bits(x_dev[:256])
+    wb = W.bf16_bits(w_dev[:1024])
     t0 = time.perf_counter()
     qa, sa = oracle.quant_row(xb)
     qb, sb = oracle.quant_row(wb)
     oracle.gemm(qa, sa, qb, sb)
-    rate = 64 * 512 / max(time.perf_counter() - t0, 1e-3)      # outputs per second
+    rate = 256 * 1024 / max(time.perf_counter() - t0, 1e-3)    # outputs per second
     want = rate * budget_s
     n = int(min(w_dev.shape[0], max(512, want / 256)))
     n -= n % 32
@@ -244,6 +269,13 @@ def main():
     print("[bench] generating inputs", file=sys.stderr, flush=True)
     stack, bufs, moe, mbufs, d = build_workload(torch, W, args.layers)
     torch.cuda.synchronize()
+    if args.calibration_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     L = Launcher(torch, mx)
     print("[bench] warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -287,6 +319,7 @@ def main():
     value = gemm_flop / (ms_step * 1e-3) / 1e12
     g = per["gemm"]
     g_rate = g["work"] / (g["ms"] * 1e-3) / 1e12
+    traffic, alg_bytes = gemm_traffic()
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -312,7 +345,9 @@ def main():
         },
         "roofline": {
             "bound": "mfma", "achieved": round(g_rate, 2), "peak": PEAK_FP8_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(g_rate / PEAK_FP8_TFLOPS, 4), "traffic": None,
+            "unit": "TFLOP/s", "frac": round(g_rate / PEAK_FP8_TFLOPS, 4), "traffic": traffic,
+            "traffic_unit": "HBM bytes read + written per launch (mean over the step's launches)",
+            "algorithmic_bytes_per_launch": alg_bytes,
             "kernel": "gemm_kernel<B_ROW> (1x32 fprop/dgrad/wgrad)",
         },
         "quant": {"gbps": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
