@@ -213,6 +213,63 @@ def run_step(L, stack, b, moe, mb, d):
               2.0 * Tm * d["Ndn"] * d["Fm"])
 
 
+def copy_rate(torch, nbytes=1 << 30, reps=5):
+    """Device-to-device copy rate (read + written bytes per second) of torch's
+    copy kernel on `nbytes`, the practical ceiling the quantisers are compared
+    with beside the 8 TB/s nominal peak."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    return 2.0 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+
+def quantisation_error(torch, mx, t, seed=11):
+    """Relative error of the MXFP8 products against the binary64 product of
+    the unquantised BF16 inputs, ||C_mx - C|| / ||C||, for the 1x32 and 32x32
+    weight variants of the up projection (fprop X_up.W_up^T and dgrad
+    dY_up.W_up), on 32 seeded rows x all columns plus 32 seeded columns x all
+    rows of each product.  Reported, not a pass/fail criterion."""
+    X, dY, Wt = t["X_up"], t["dY_up"], t["W_up"]
+    T, H = X.shape
+    F = Wt.shape[0]
+    g = torch.Generator().manual_seed(seed)
+    out = {}
+    qx, sx = mx.quant(X, "row")[:2]
+    qd, sd = mx.quant(dY, "row")[:2]
+    qw, sw, qwt, swt = mx.quant(Wt, "dual")
+    q32, s32 = mx.quant(Wt, "32x32")[:2]
+    Wd = Wt.double()
+    prods = {
+        "fprop": (X, lambda A: A @ Wd.t(), lambda idx: Wd[idx].t(), F,
+                  {"1x32": (qx, sx, qw, sw, "fprop", "1x32"), "32x32": (qx, sx, q32, s32, "fprop", "32x32")}),
+        "dgrad": (dY, lambda A: A @ Wd, lambda idx: Wd[:, idx], H,
+                  {"1x32": (qd, sd, qwt, swt, "dgrad", "1x32"), "32x32": (qd, sd, q32, s32, "dgrad", "32x32")}),
+    }
+    for name, (A, row_ref, col_op, N, variants) in prods.items():
+        rows = torch.randperm(T, generator=g)[:32].cuda()
+        cols = torch.randperm(N, generator=g)[:32].cuda()
+        ref_r = row_ref(A.index_select(0, rows).double())             # [32, N]
+        ref_c = A.double() @ col_op(cols)                               # [T, 32]
+        for var, (a, sa, b, sb, layout, bk) in variants.items():
+            C = mx.gemm(a, sa, b, sb, layout, bk)
+            got_r = C.index_select(0, rows).double()
+            got_c = C.index_select(1, cols).double()
+            num = (got_r - ref_r).pow(2).sum() + (got_c - ref_c).pow(2).sum()
+            den = ref_r.pow(2).sum() + ref_c.pow(2).sum()
+            out[f"{name}_{var}"] = float((num / den).sqrt())
+            del C
+        del ref_r, ref_c
+    torch.cuda.synchronize()
+    return out
+
+
 def cpu_baseline(W, x_dev, w_dev, budget_s):
     """The oracle (untuned) on a bounded sample of the step: dual-axis
     quantisation of leading token rows of the up-projection input and of
@@ -357,6 +414,12 @@ def main():
                     for k, v in kernels.items()},
         "wall_s_timed": round(wall, 3),
     }
+    print("[bench] copy rate, quantisation error", file=sys.stderr, flush=True)
+    cg = copy_rate(torch)
+    out["quant"]["d2d_copy_gbps"] = round(cg, 1)
+    out["quant"]["frac_of_copy"] = round(out["quant"]["gbps"] / cg, 4)
+    out["quantisation_error"] = {k: float(f"{v:.6g}") for k, v in
+                                 quantisation_error(torch, mx, stack[0]).items()}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(W, stack[0]["X_up"], stack[0]["W_up"], args.cpu_seconds)

@@ -17,8 +17,9 @@
 //   the byte (op_sel) of lane i + 32b's scale register.  Result lane l, acc
 //   j: row 8(j/4) + 4(l/32) + j%4, column l%32.
 // The MFMA's first operand is B (our N side) and its second is A (our M
-// side), so each lane ends with four consecutive n of one C row and stores 8
-// bytes at a time.
+// side), so each lane ends with groups of four consecutive n of one C row;
+// lanes l and l + 32 trade groups (v_permlane32_swap) so that every store
+// writes 8 consecutive BF16 (16 bytes).
 //
 // Workgroup tile 256 (M) x 256 (N), K step 128 bytes, four waves of 128x128
 // (16 accumulators of 32x32 each).  Both operands are staged through a
@@ -565,29 +566,46 @@ struct Tile {
       if (kt < nk)
         step(st0, st1, kt, wave, wm, wn, lane, sc_a, sc_b, nx_a, nx_b, f0a, f0b, f1a, f1b, acc);
     }
-    // epilogue: FP32 -> BF16 (RNE), four consecutive n per lane and row
+    // epilogue: FP32 -> BF16 (RNE).  A lane holds four consecutive n of its
+    // row per group r4 (n = 8 r4 + 4 g + 0..3); one v_permlane32_swap per
+    // dword pair trades groups between lanes l and l + 32, after which lane
+    // half g holds the 8 consecutive n at 8 g + 16 h for h = 0, 1 and stores
+    // them as one 16-byte write.  The swaps run on every lane before any
+    // lane drops out at the M edge.
     const int g = lane >> 5, i = lane & 31;
-    const bool vec_ok = (N & 3) == 0;
+    const bool vec_ok = (N & 7) == 0;
 #pragma unroll
     for (int fn = 0; fn < 4; fn++) {
 #pragma unroll
       for (int fm = 0; fm < 4; fm++) {
+        const v16f& v = acc[fn][fm];
+        uint32_t p[4][2];
+#pragma unroll
+        for (int r4 = 0; r4 < 4; r4++) {
+          p[r4][0] = cvt_pk_bf16(v[4 * r4 + 0], v[4 * r4 + 1]);
+          p[r4][1] = cvt_pk_bf16(v[4 * r4 + 2], v[4 * r4 + 3]);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; h++)
+#pragma unroll
+          for (int d = 0; d < 2; d++) {
+            const auto s = __builtin_amdgcn_permlane32_swap(p[2 * h][d], p[2 * h + 1][d], false, false);
+            p[2 * h][d] = s[0];
+            p[2 * h + 1][d] = s[1];
+          }
         const int64_t m = m0 + 128 * wm + 32 * fm + i;
         if (m >= m_end) continue;
 #pragma unroll
-        for (int r4 = 0; r4 < 4; r4++) {
-          const int64_t n = n0 + 128 * wn + 32 * fn + 8 * r4 + 4 * g;
-          const v16f& v = acc[fn][fm];
-          uint32_t h0 = bf16_rne(v[4 * r4 + 0]), h1 = bf16_rne(v[4 * r4 + 1]);
-          uint32_t h2 = bf16_rne(v[4 * r4 + 2]), h3 = bf16_rne(v[4 * r4 + 3]);
+        for (int h = 0; h < 2; h++) {
+          const int64_t n = n0 + 128 * wn + 32 * fn + 16 * h + 8 * g;
+          const uint32_t w[4] = {p[2 * h][0], p[2 * h][1], p[2 * h + 1][0], p[2 * h + 1][1]};
           uint16_t* dst = c + m * N + n;
-          if (vec_ok && n + 4 <= N) {
-            *(uint2*)dst = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+          if (vec_ok && n + 8 <= N) {
+            *(uint4*)dst = make_uint4(w[0], w[1], w[2], w[3]);
           } else {
-            if (n + 0 < N) dst[0] = (uint16_t)h0;
-            if (n + 1 < N) dst[1] = (uint16_t)h1;
-            if (n + 2 < N) dst[2] = (uint16_t)h2;
-            if (n + 3 < N) dst[3] = (uint16_t)h3;
+#pragma unroll
+            for (int e = 0; e < 8; e++)
+              if (n + e < N) dst[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
           }
         }
       }
@@ -697,8 +715,15 @@ grouped_gemm_kernel(int64_t G, const int64_t* __restrict__ offsets, int64_t T, i
       if (s_pre[mid] <= t) lo = mid; else hi = mid;
     }
     const int64_t g = lo;
+    // inside group g, the same grouped order as the dense kernel: runs of
+    // GM_TILES m-tiles, n-tiles outer, so 32 consecutive tiles cover
+    // GM_TILES m-tiles x (32 / GM_TILES) n-tiles
     const int64_t local = t - s_pre[g];
-    const int64_t mt = local / nn, nt = local % nn;
+    const int64_t nmg = (s_off[g + 1] - s_off[g] + BM - 1) / BM;
+    const int64_t first = local / (GM_TILES * nn) * GM_TILES;
+    const int64_t gsz = (nmg - first) < GM_TILES ? (nmg - first) : GM_TILES;
+    const int64_t in = local % (GM_TILES * nn);
+    const int64_t mt = first + in % gsz, nt = in / gsz;
     Tile<GEMM_B_ROW, FAST> tl;
     tl.a = a;
     tl.sa = sa;
@@ -715,11 +740,11 @@ grouped_gemm_kernel(int64_t G, const int64_t* __restrict__ offsets, int64_t T, i
     tl.st1 = (lds_u8*)smem1;
     tl.ss0 = (lds_u8*)sscale;
     tl.ss1 = (lds_u8*)sscale + SCALE_TILE;
-    // 32 consecutive tiles (n fastest) run together on an XCD: A slices are
-    // first needed by n-tile 0, B slices by every other m-tile
+    // as in the dense kernel: A slices are first needed by n-tiles at
+    // multiples of 32 / GM_TILES, B slices by the first m-tile of a run
     tl.pf_scratch = (lds_u8*)spf;
-    tl.pf_a = nt == 0 ? 0u : OOB;
-    tl.pf_b = (mt & 1) == 0 ? 0u : OOB;
+    tl.pf_a = (nt % (32 / GM_TILES) == 0) ? 0u : OOB;
+    tl.pf_b = (mt == first) ? 0u : OOB;
     tl.run();
   }
 }
