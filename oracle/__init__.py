@@ -75,6 +75,17 @@ def lib():
                                        ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p]
+        L.orc_grouped_col_capacity.restype = ctypes.c_int64
+        L.orc_grouped_col_capacity.argtypes = [ctypes.c_int64, ctypes.c_int64]
+        L.orc_quant_col_grouped.restype = ctypes.c_int
+        L.orc_quant_col_grouped.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                            ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_void_p]
+        L.orc_grouped_gemm_wgrad.restype = ctypes.c_int
+        L.orc_grouped_gemm_wgrad.argtypes = [ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                             ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_void_p]
         L.orc_num_threads.restype = ctypes.c_int
         del u8p
         _lib = L
@@ -175,6 +186,44 @@ def quant_dual(x):
     return q, s, qt, st
 
 
+def quant_col_batched(x):
+    """Column quantisation of each matrix of a stack x [B,R,C]:
+    returns (q_t [B,C,R], s_t [B,C,R/32])."""
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.int16:
+        x = x.view(np.uint16)
+    outs = [quant_col(x[i]) for i in range(x.shape[0])]
+    return (np.stack([o[0] for o in outs]), np.stack([o[1] for o in outs]))
+
+
+def grouped_col_capacity(T: int, G: int) -> int:
+    """Columns of the per-group column-quantised output (reading R9)."""
+    return int(lib().orc_grouped_col_capacity(int(T), int(G)))
+
+
+def group_col(g: int, o_g: int) -> int:
+    """First padded column of group g (reading R9): 32 * (o_g // 32 + g)."""
+    return 32 * (int(o_g) // 32 + int(g))
+
+
+def quant_col_grouped(x, offsets):
+    """MoE backward column blocks restarting at each group offset (R9).
+
+    x [T,C] BF16 bits, offsets int64 [G+1] -> (q_t [C,cap] u8, s_t [C,cap/32] u8)
+    with cap = grouped_col_capacity(T, G)."""
+    x = _bits(x)
+    offsets = _c(np.asarray(offsets, dtype=np.int64), np.int64)
+    T, C = x.shape
+    G = offsets.size - 1
+    cap = grouped_col_capacity(T, G)
+    q = np.empty((C, cap), np.uint8)
+    s = np.empty((C, cap // 32), np.uint8)
+    rc = lib().orc_quant_col_grouped(_ptr(x), T, C, G, _ptr(offsets), _ptr(q), _ptr(s))
+    if rc:
+        raise ValueError(f"oracle grouped column quantisation rejected the arguments (rc={rc})")
+    return q, s
+
+
 def quant_block32(x):
     """32x32 tiles: returns (q [R,C] u8, s [R/32,C/32] u8)."""
     x = _bits(x)
@@ -229,6 +278,28 @@ def grouped_gemm(offsets, a, sa, b, sb, want_bound: bool = True):
                                 _ptr(sb), _ptr(ref), _ptr(bound) if bound is not None else None)
     if rc:
         raise ValueError(f"oracle grouped gemm rejected the arguments (rc={rc})")
+    return ref, bound
+
+
+def grouped_gemm_wgrad(offsets, a, sa, b, sb, want_bound: bool = True):
+    """Per-expert weight gradient over each group's tokens (R9 layout).
+
+    offsets int64 [G+1] with offsets[G] = T; a [M,cap] u8 + sa [M,cap/32];
+    b [N,cap] u8 + sb [N,cap/32]; returns ref/bound [G,M,N]."""
+    offsets = _c(np.asarray(offsets, dtype=np.int64), np.int64)
+    a = _c(a, np.uint8)
+    sa = _c(sa, np.uint8)
+    b = _c(b, np.uint8)
+    sb = _c(sb, np.uint8)
+    G = offsets.size - 1
+    T = int(offsets[-1])
+    M, N = a.shape[0], b.shape[0]
+    ref = np.empty((G, M, N), np.float64)
+    bound = np.empty((G, M, N), np.float64) if want_bound else None
+    rc = lib().orc_grouped_gemm_wgrad(G, _ptr(offsets), T, M, N, _ptr(a), _ptr(sa), _ptr(b),
+                                      _ptr(sb), _ptr(ref), _ptr(bound) if bound is not None else None)
+    if rc:
+        raise ValueError(f"oracle grouped wgrad rejected the arguments (rc={rc})")
     return ref, bound
 
 

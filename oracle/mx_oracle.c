@@ -40,6 +40,14 @@
  *   R7  column-axis output is written transposed: q_t[c][r], s_t[c][r/32].
  *   R8  the 32x32 forward and backward scales are two views of one tile
  *       array s[R/32][C/32].
+ *   R9  MoE backward, per-group column blocks: along the token axis, blocks
+ *       of 32 restart at every group offset and a group's last block holds
+ *       only its remaining rows; its amax covers those rows alone.  The
+ *       transposed output gives group g the padded column range starting at
+ *       P_g = 32 * (floor(o_g / 32) + g), i.e. a capacity of
+ *       32 * (floor(T / 32) + G) columns; every column that holds no token
+ *       (the rest of a partial block, the gaps between groups) is an
+ *       all-zero block: payload 0x00 and scale 0x00 (R1).
  *
  * Threading: OpenMP over independent rows / blocks only; no element's
  * arithmetic is split or reordered.
@@ -322,6 +330,100 @@ int orc_grouped_gemm(int64_t G, const int64_t *offsets, int64_t T, int64_t N, in
                           ref ? ref + r0 * N : NULL, bound ? bound + r0 * N : NULL);
         if (rc)
             return rc;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* MoE backward                                                              */
+/* ------------------------------------------------------------------------ */
+
+/* First padded column of group g (R9). */
+static int64_t group_col(int64_t g, int64_t o_g)
+{
+    return 32 * (o_g / 32 + g);
+}
+
+int64_t orc_grouped_col_capacity(int64_t T, int64_t G)
+{
+    return 32 * (T / 32 + G);
+}
+
+static int offsets_ok(int64_t G, const int64_t *offsets, int64_t T)
+{
+    if (G < 0 || offsets[0] != 0 || offsets[G] != T)
+        return 0;
+    for (int64_t g = 0; g < G; g++)
+        if (offsets[g + 1] < offsets[g])
+            return 0;
+    return 1;
+}
+
+/* Column blocks per group (R9): x is BF16 [T][C]; q_t[C][cap] and
+ * s_t[C][cap / 32] with cap = orc_grouped_col_capacity(T, G).  The last block
+ * of a group is quantised from its remaining rows only.  Returns 0, or -1 on
+ * bad offsets or C % 32 != 0. */
+int orc_quant_col_grouped(const uint16_t *x, int64_t T, int64_t C, int64_t G,
+                          const int64_t *offsets, uint8_t *q_t, uint8_t *s_t)
+{
+    if (!offsets_ok(G, offsets, T) || C % 32 != 0)
+        return -1;
+    const int64_t cap = orc_grouped_col_capacity(T, G), nbc = cap / 32;
+    memset(q_t, 0, (size_t)(C * cap));
+    memset(s_t, 0, (size_t)(C * nbc));
+    for (int64_t g = 0; g < G; g++) {
+        const int64_t o = offsets[g], rows = offsets[g + 1] - offsets[g];
+        const int64_t P = group_col(g, o);
+        const int64_t nb = (rows + 31) / 32;
+#pragma omp parallel for schedule(static)
+        for (int64_t c = 0; c < C; c++) {
+            double v[32];
+            uint8_t codes[32];
+            for (int64_t j = 0; j < nb; j++) {
+                const int n = (int)((rows - 32 * j) < 32 ? (rows - 32 * j) : 32);
+                for (int k = 0; k < n; k++)
+                    v[k] = orc_bf16_value(x[(o + 32 * j + k) * C + c]);
+                s_t[c * nbc + P / 32 + j] = quant_block(n, v, codes);
+                memcpy(q_t + c * cap + P + 32 * j, codes, (size_t)n);
+            }
+        }
+    }
+    return 0;
+}
+
+/* Per-expert weight gradient: for every group g,
+ *   ref[g][m][n] = sum over the group's tokens t of A[m][t] * B[n][t]
+ * where A = a [M][cap] (scales [M][cap/32]) and B = b [N][cap] are the
+ * per-group column-quantised copies of (for MoE) the output gradient and the
+ * expert input, token t of group g sitting at column P_g + (t - o_g) (R9).
+ * An empty group gives ref = bound = 0.  ref/bound are [G][M][N]. */
+int orc_grouped_gemm_wgrad(int64_t G, const int64_t *offsets, int64_t T, int64_t M, int64_t N,
+                           const uint8_t *a, const uint8_t *sa, const uint8_t *b,
+                           const uint8_t *sb, double *ref, double *bound)
+{
+    if (!offsets_ok(G, offsets, T) || M < 0 || N < 0)
+        return -1;
+    const int64_t cap = orc_grouped_col_capacity(T, G), nbc = cap / 32;
+    for (int64_t g = 0; g < G; g++) {
+        const int64_t o = offsets[g], rows = offsets[g + 1] - offsets[g];
+        const int64_t P = group_col(g, o);
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t m = 0; m < M; m++) {
+            for (int64_t n = 0; n < N; n++) {
+                double acc = 0.0, mag = 0.0;
+                for (int64_t t = 0; t < rows; t++) {
+                    const int64_t k = P + t;
+                    double p = orc_e4m3_value(a[m * cap + k]) * orc_e8m0_value(sa[m * nbc + k / 32]) *
+                               orc_e4m3_value(b[n * cap + k]) * orc_e8m0_value(sb[n * nbc + k / 32]);
+                    acc += p;
+                    mag += fabs(p);
+                }
+                if (ref)
+                    ref[(g * M + m) * N + n] = acc;
+                if (bound)
+                    bound[(g * M + m) * N + n] = mag;
+            }
+        }
     }
     return 0;
 }

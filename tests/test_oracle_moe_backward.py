@@ -1,0 +1,177 @@
+"""Pins for the oracle's MoE backward pieces (CPU only): per-group column
+quantisation along the token axis (blocks restart at every group offset, a
+group's last block holds only its remaining rows) and the per-expert weight
+gradient over each group's tokens.
+
+The grouped column quantisation is pinned to the (already pinned) plain
+column quantisation of an explicitly zero-padded token matrix built here with
+numpy, and to hand-derived bytes for partial blocks whose neighbours would
+change the scale if they were wrongly included.  The weight gradient is pinned
+to numpy float64 matmuls of operands dequantised through torch's float8 casts.
+"""
+import numpy as np
+import pytest
+import torch
+
+from mxfp8_microscaled_precision_amd import workloads as W
+
+
+def _offsets(sizes):
+    o = np.zeros(len(sizes) + 1, np.int64)
+    np.cumsum(sizes, out=o[1:])
+    return o
+
+
+def _padded(x_bits, off):
+    """Token rows of every group copied to its padded column range: row
+    P_g + k holds token o_g + k; every other row is +0."""
+    G = off.size - 1
+    T, C = x_bits.shape
+    cap = 32 * (T // 32 + G)
+    xp = np.zeros((cap, C), np.uint16)
+    for g in range(G):
+        P = 32 * (int(off[g]) // 32 + g)
+        m = int(off[g + 1] - off[g])
+        xp[P:P + m] = x_bits[off[g]:off[g + 1]]
+    return xp
+
+
+def _deq(q, s):
+    v = torch.from_numpy(np.ascontiguousarray(q)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    sc = torch.from_numpy(np.ascontiguousarray(np.repeat(s, 32, axis=1))).view(
+        torch.float8_e8m0fnu).to(torch.float64).numpy()
+    return v * sc
+
+
+@pytest.mark.parametrize("sizes,C", [
+    ([5, 0, 33, 1, 31, 32, 64, 0, 70], 64),
+    ([0, 0, 7], 32),
+    ([32, 64, 96], 96),
+    ([100], 32),
+])
+def test_grouped_col_equals_col_of_padded_matrix(orc, sizes, C):
+    off = _offsets(sizes)
+    T = int(off[-1])
+    x = W.bf16_bits(W.normal_with_outliers_bf16((T, C), 1.0, 0.01, 100.0, sum(sizes) + C))
+    q, s = orc.quant_col_grouped(x, off)
+    qp, sp = orc.quant_col(_padded(x, off))
+    assert q.shape == qp.shape and s.shape == sp.shape
+    assert np.array_equal(q, qp)
+    assert np.array_equal(s, sp)
+
+
+def test_grouped_col_whole_blocks_equal_per_group_col(orc):
+    """Groups of whole 32-row blocks: each group's columns are the column
+    quantisation of that group's rows alone, at P_g = 32 (o_g / 32 + g)."""
+    sizes = [64, 32, 0, 96]
+    off = _offsets(sizes)
+    x = W.bf16_bits(W.normal_bf16((int(off[-1]), 64), 1.0, 3))
+    q, s = orc.quant_col_grouped(x, off)
+    for g in range(len(sizes)):
+        m = sizes[g]
+        if m == 0:
+            continue
+        P = orc.group_col(g, off[g])
+        qg, sg = orc.quant_col(x[off[g]:off[g + 1]])
+        assert np.array_equal(q[:, P:P + m], qg)
+        assert np.array_equal(s[:, P // 32:(P + m) // 32], sg)
+
+
+def test_partial_blocks_hand_values(orc):
+    """sizes [5, 33, 4], every column the same: group 0 = five 1.0, group 1 =
+    thirty-two 2.0 then one 0.5, group 2 = four 100.0.  By the rceil rule
+    (scale exponent ceil(log2(amax / 448))): 1.0 -> e = -8 (byte 0x77) and
+    payload 256 -> 0x78; 2.0 -> e = -7 (0x78), payload 0x78; the lone 0.5 ->
+    e = -9 (0x76), payload 0x78; 100.0 -> e = -2 (0x7D) and 400, halfway
+    between 384 and 416, rounds to the even mantissa: 384 = 0x7C.  A block
+    that wrongly reached into the next group would see a larger amax."""
+    bf = {1.0: 0x3F80, 2.0: 0x4000, 0.5: 0x3F00, 100.0: 0x42C8}
+    col = [1.0] * 5 + [2.0] * 32 + [0.5] + [100.0] * 4
+    x = np.array([[bf[v]] for v in col], np.uint16).repeat(32, axis=1)
+    off = _offsets([5, 33, 4])
+    q, s = orc.quant_col_grouped(x, off)
+    cap = orc.grouped_col_capacity(42, 3)
+    assert cap == 128 and q.shape == (32, 128) and s.shape == (32, 4)
+    # P_0 = 0, P_1 = 32 (0 + 1) = 32, P_2 = 32 (38 // 32 + 2) = 96
+    want_q = np.zeros(128, np.uint8)
+    want_q[0:5] = 0x78
+    want_q[32:64] = 0x78
+    want_q[64] = 0x78
+    want_q[96:100] = 0x7C
+    want_s = np.array([0x77, 0x78, 0x76, 0x7D], np.uint8)
+    for c in range(32):
+        assert np.array_equal(q[c], want_q), c
+        assert np.array_equal(s[c], want_s), c
+
+
+def test_empty_and_gap_columns_are_zero_blocks(orc):
+    sizes = [0, 3, 0, 0, 40]
+    off = _offsets(sizes)
+    x = W.bf16_bits(W.normal_bf16((43, 32), 1.0, 9))
+    q, s = orc.quant_col_grouped(x, off)
+    used = np.zeros(q.shape[1], bool)
+    for g, m in enumerate(sizes):
+        P = orc.group_col(g, off[g])
+        used[P:P + m] = True
+    assert np.all(q[:, ~used] == 0)
+    blocks_used = used.reshape(-1, 32).any(axis=1)
+    assert np.all(s[:, ~blocks_used] == 0)
+    assert np.all(s[:, blocks_used] != 0)
+
+
+@pytest.mark.parametrize("sizes,M,N", [([5, 0, 33, 64, 1], 20, 12), ([0, 0], 4, 4), ([200], 8, 40)])
+def test_wgrad_matches_numpy_per_group(orc, sizes, M, N):
+    off = _offsets(sizes)
+    T, G = int(off[-1]), len(sizes)
+    cap = orc.grouped_col_capacity(T, G)
+    rng = np.random.default_rng(T + M + N)
+    a = rng.integers(0, 256, size=(M, cap), dtype=np.uint8)
+    b = rng.integers(0, 256, size=(N, cap), dtype=np.uint8)
+    a[(a & 0x7F) == 0x7F] = 0x3C
+    b[(b & 0x7F) == 0x7F] = 0x3C
+    sa = rng.integers(115, 135, size=(M, cap // 32), dtype=np.uint8)
+    sb = rng.integers(115, 135, size=(N, cap // 32), dtype=np.uint8)
+    ref, bound = orc.grouped_gemm_wgrad(off, a, sa, b, sb)
+    A, B = _deq(a, sa), _deq(b, sb)
+    for g in range(G):
+        P, m = orc.group_col(g, off[g]), sizes[g]
+        want = A[:, P:P + m] @ B[:, P:P + m].T
+        mag = np.abs(A[:, P:P + m]) @ np.abs(B[:, P:P + m]).T
+        assert np.all(np.abs(ref[g] - want) <= 2.0 * max(m, 1) * 2.0 ** -53 * mag + 1e-300)
+        assert np.allclose(bound[g], mag, rtol=1e-12, atol=0)
+        if m == 0:
+            assert np.all(ref[g] == 0) and np.all(bound[g] == 0)
+
+
+def test_wgrad_of_quantised_tokens_equals_dense_gemm_on_padded_slices(orc):
+    """With operands from the grouped column quantisation, the padding columns
+    carry zero payload, so each expert's gradient equals the dense oracle GEMM
+    over its whole padded column range."""
+    sizes = [37, 0, 64, 5]
+    off = _offsets(sizes)
+    T = int(off[-1])
+    dy = W.bf16_bits(W.normal_bf16((T, 64), 0.01, 21))
+    xx = W.bf16_bits(W.normal_bf16((T, 96), 1.0, 22))
+    qa, sa = orc.quant_col_grouped(dy, off)
+    qb, sb = orc.quant_col_grouped(xx, off)
+    ref, bound = orc.grouped_gemm_wgrad(off, qa, sa, qb, sb)
+    for g, m in enumerate(sizes):
+        P = orc.group_col(g, off[g])
+        Kg = 32 * ((m + 31) // 32)
+        if Kg == 0:
+            assert np.all(ref[g] == 0)
+            continue
+        d, db = orc.gemm(qa[:, P:P + Kg], sa[:, P // 32:(P + Kg) // 32],
+                         qb[:, P:P + Kg], sb[:, P // 32:(P + Kg) // 32])
+        assert np.all(np.abs(ref[g] - d) <= 2.0 * Kg * 2.0 ** -53 * db + 1e-300)
+
+
+def test_bad_offsets_rejected(orc):
+    x = W.bf16_bits(W.normal_bf16((10, 32), 1.0, 1))
+    with pytest.raises(ValueError):
+        orc.quant_col_grouped(x, np.array([0, 6, 4, 10], np.int64))
+    with pytest.raises(ValueError):
+        orc.quant_col_grouped(x, np.array([0, 4, 9], np.int64))
+    with pytest.raises(ValueError):
+        orc.quant_col_grouped(W.bf16_bits(W.normal_bf16((10, 40), 1.0, 1)),
+                              np.array([0, 10], np.int64))
