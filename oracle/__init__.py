@@ -202,8 +202,8 @@ def grouped_col_capacity(T: int, G: int) -> int:
 
 
 def group_col(g: int, o_g: int) -> int:
-    """First padded column of group g (reading R9): 32 * (o_g // 32 + g)."""
-    return 32 * (int(o_g) // 32 + int(g))
+    """First column of group g (reading R9): 128 * (o_g // 128 + g)."""
+    return 128 * (int(o_g) // 128 + int(g))
 
 
 def quant_col_grouped(x, offsets):

@@ -43,11 +43,12 @@
  *   R9  MoE backward, per-group column blocks: along the token axis, blocks
  *       of 32 restart at every group offset and a group's last block holds
  *       only its remaining rows; its amax covers those rows alone.  The
- *       transposed output gives group g the padded column range starting at
- *       P_g = 32 * (floor(o_g / 32) + g), i.e. a capacity of
- *       32 * (floor(T / 32) + G) columns; every column that holds no token
- *       (the rest of a partial block, the gaps between groups) is an
- *       all-zero block: payload 0x00 and scale 0x00 (R1).
+ *       transposed output gives group g the column range starting at
+ *       P_g = 128 * (floor(o_g / 128) + g), i.e. a capacity of
+ *       128 * (floor(T / 128) + G) columns (every range starts on a whole
+ *       128-byte line, and its scales on a whole 4-byte word); every column
+ *       that holds no token (the rest of a partial block, the gaps between
+ *       groups) belongs to an all-zero block: payload 0x00, scale 0x00 (R1).
  *
  * Threading: OpenMP over independent rows / blocks only; no element's
  * arithmetic is split or reordered.
@@ -338,15 +339,15 @@ int orc_grouped_gemm(int64_t G, const int64_t *offsets, int64_t T, int64_t N, in
 /* MoE backward                                                              */
 /* ------------------------------------------------------------------------ */
 
-/* First padded column of group g (R9). */
+/* First column of group g (R9). */
 static int64_t group_col(int64_t g, int64_t o_g)
 {
-    return 32 * (o_g / 32 + g);
+    return 128 * (o_g / 128 + g);
 }
 
 int64_t orc_grouped_col_capacity(int64_t T, int64_t G)
 {
-    return 32 * (T / 32 + G);
+    return 128 * (T / 128 + G);
 }
 
 static int offsets_ok(int64_t G, const int64_t *offsets, int64_t T)

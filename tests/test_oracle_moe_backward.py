@@ -23,14 +23,14 @@ def _offsets(sizes):
 
 
 def _padded(x_bits, off):
-    """Token rows of every group copied to its padded column range: row
-    P_g + k holds token o_g + k; every other row is +0."""
+    """Token rows of every group copied to its column range: row P_g + k
+    holds token o_g + k, P_g = 128 (o_g // 128 + g); every other row is +0."""
     G = off.size - 1
     T, C = x_bits.shape
-    cap = 32 * (T // 32 + G)
+    cap = 128 * (T // 128 + G)
     xp = np.zeros((cap, C), np.uint16)
     for g in range(G):
-        P = 32 * (int(off[g]) // 32 + g)
+        P = 128 * (int(off[g]) // 128 + g)
         m = int(off[g + 1] - off[g])
         xp[P:P + m] = x_bits[off[g]:off[g + 1]]
     return xp
@@ -62,7 +62,7 @@ def test_grouped_col_equals_col_of_padded_matrix(orc, sizes, C):
 
 def test_grouped_col_whole_blocks_equal_per_group_col(orc):
     """Groups of whole 32-row blocks: each group's columns are the column
-    quantisation of that group's rows alone, at P_g = 32 (o_g / 32 + g)."""
+    quantisation of that group's rows alone, at P_g = 128 (o_g // 128 + g)."""
     sizes = [64, 32, 0, 96]
     off = _offsets(sizes)
     x = W.bf16_bits(W.normal_bf16((int(off[-1]), 64), 1.0, 3))
@@ -91,14 +91,15 @@ def test_partial_blocks_hand_values(orc):
     off = _offsets([5, 33, 4])
     q, s = orc.quant_col_grouped(x, off)
     cap = orc.grouped_col_capacity(42, 3)
-    assert cap == 128 and q.shape == (32, 128) and s.shape == (32, 4)
-    # P_0 = 0, P_1 = 32 (0 + 1) = 32, P_2 = 32 (38 // 32 + 2) = 96
-    want_q = np.zeros(128, np.uint8)
+    assert cap == 384 and q.shape == (32, 384) and s.shape == (32, 12)
+    # P_0 = 0, P_1 = 128 (0 + 1) = 128, P_2 = 128 (38 // 128 + 2) = 256
+    want_q = np.zeros(384, np.uint8)
     want_q[0:5] = 0x78
-    want_q[32:64] = 0x78
-    want_q[64] = 0x78
-    want_q[96:100] = 0x7C
-    want_s = np.array([0x77, 0x78, 0x76, 0x7D], np.uint8)
+    want_q[128:160] = 0x78
+    want_q[160] = 0x78
+    want_q[256:260] = 0x7C
+    want_s = np.zeros(12, np.uint8)
+    want_s[[0, 4, 5, 8]] = [0x77, 0x78, 0x76, 0x7D]
     for c in range(32):
         assert np.array_equal(q[c], want_q), c
         assert np.array_equal(s[c], want_s), c
@@ -157,7 +158,7 @@ def test_wgrad_of_quantised_tokens_equals_dense_gemm_on_padded_slices(orc):
     ref, bound = orc.grouped_gemm_wgrad(off, qa, sa, qb, sb)
     for g, m in enumerate(sizes):
         P = orc.group_col(g, off[g])
-        Kg = 32 * ((m + 31) // 32)
+        Kg = 128 * ((m + 127) // 128)
         if Kg == 0:
             assert np.all(ref[g] == 0)
             continue
