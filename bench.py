@@ -10,8 +10,12 @@ One step = one pass of the whole hot path over one batch of synthetic input:
                    shared FP8 weight; fprop and the transposed-read dgrad use
                    tile scales), same seeds;
   MoE experts, 131072 routed tokens over 64 experts (Zipf(1.1) sizes):
-    1x32 quantisation of tokens and expert weights, then the grouped
-    gate_up (4096 -> 4096) and down (2048 -> 4096) MXFP8 GEMMs.
+    forward: 1x32 quantisation of tokens and expert weights, then the grouped
+    gate_up (4096 -> 4096) and down (2048 -> 4096) MXFP8 GEMMs;
+    backward: 1x32 quantisation of the output gradients, column quantisation
+    of every expert weight (batched) for the grouped dgrad GEMMs, and
+    per-group column quantisation of gradients and inputs along the token
+    axis for the per-expert weight-gradient GEMMs.
 
 Inputs are generated on the GPU and resident in HBM before timing; outputs
 are preallocated.  `value` = GEMM FLOP of the step / step time (TFLOP/s).
@@ -94,6 +98,28 @@ class Launcher:
             G, offs.data_ptr(), T, N, K, a.data_ptr(), sa.data_ptr(), b.data_ptr(),
             sb.data_ptr(), c.data_ptr(), self.stream))
 
+    def quant_batched(self, kind, mode, x, outs):
+        mx = self.mx
+        B, R, C = x.shape
+        q, s, qt, st = outs
+        nbytes = 3.03125 * B * R * C
+        self._wrap(kind, nbytes, "B", lambda: mx.mx_quant_batched(
+            mode, x.data_ptr(), B, R, C, _p(q), _p(s), _p(qt), _p(st), self.stream))
+
+    def quant_grouped_col(self, kind, G, offs, x, outs):
+        mx = self.mx
+        T, C = x.shape
+        qt, st = outs
+        nbytes = 3.03125 * T * C          # the tokens' own bytes; zero padding not counted
+        self._wrap(kind, nbytes, "B", lambda: mx.mx_quant_grouped_col(
+            x.data_ptr(), T, C, G, offs.data_ptr(), qt.data_ptr(), st.data_ptr(), self.stream))
+
+    def grouped_wgrad(self, kind, G, offs, T, M, N, a, sa, b, sb, c):
+        mx = self.mx
+        self._wrap(kind, 2.0 * T * M * N, "FLOP", lambda: mx.mx_grouped_gemm_wgrad(
+            G, offs.data_ptr(), T, M, N, a.data_ptr(), sa.data_ptr(), b.data_ptr(),
+            sb.data_ptr(), c.data_ptr(), self.stream))
+
 
 def _p(t):
     return 0 if t is None else t.data_ptr()
@@ -146,17 +172,31 @@ def build_workload(torch, W, layers):
         "dW_dn": torch.empty((H, F), dtype=bf, device=dev),
     }
     moe = W.moe(dev)
+    moe.update(W.moe_grads(dev))
     off = moe["offsets"]
     Tm = int(off[-1])
     G, Ngu, Hm = moe["W_gu"].shape
     _, Ndn, Fm = moe["W_dn"].shape
+    cap = 128 * (Tm // 128 + G)
     row = lambda R, C: (torch.empty((R, C), dtype=u8, device=dev),
                         torch.empty((R, C // 32), dtype=u8, device=dev), None, None)
+    colb = lambda B, R, C: (None, None, torch.empty((B, C, R), dtype=u8, device=dev),
+                            torch.empty((B, C, R // 32), dtype=u8, device=dev))
+    gcol = lambda C: (torch.empty((C, cap), dtype=u8, device=dev),
+                      torch.empty((C, cap // 32), dtype=u8, device=dev))
     moe_bufs = {
         "offs": torch.from_numpy(off).to(dev),
         "X": row(Tm, Hm), "H": row(Tm, Fm), "W_gu": row(G * Ngu, Hm), "W_dn": row(G * Ndn, Fm),
         "Y_gu": torch.empty((Tm, Ngu), dtype=bf, device=dev),
         "Y_dn": torch.empty((Tm, Ndn), dtype=bf, device=dev),
+        # backward
+        "dY_gu": row(Tm, Ngu), "dY_dn": row(Tm, Ndn),
+        "W_gu_t": colb(G, Ngu, Hm), "W_dn_t": colb(G, Ndn, Fm),
+        "dX": torch.empty((Tm, Hm), dtype=bf, device=dev),
+        "dH": torch.empty((Tm, Fm), dtype=bf, device=dev),
+        "gX": gcol(Hm), "gH": gcol(Fm), "gdY_gu": gcol(Ngu), "gdY_dn": gcol(Ndn),
+        "dW_gu": torch.empty((G, Ngu, Hm), dtype=bf, device=dev),
+        "dW_dn": torch.empty((G, Ndn, Fm), dtype=bf, device=dev),
     }
     dims = dict(T=T, H=H, F=F, Tm=Tm, G=G, Ngu=Ngu, Hm=Hm, Ndn=Ndn, Fm=Fm)
     return stack, bufs, moe, moe_bufs, dims
@@ -211,6 +251,23 @@ def run_step(L, stack, b, moe, mb, d):
     qw, sw = mb["W_dn"][:2]
     L.grouped("grouped_gemm", G, mb["offs"], Tm, d["Ndn"], d["Fm"], qa, sa, qw, sw, mb["Y_dn"],
               2.0 * Tm * d["Ndn"] * d["Fm"])
+    # MoE backward: dgrad through the column-quantised expert weights, wgrad
+    # over each expert's tokens
+    offs = mb["offs"]
+    for dyn, wn, wtn, xn, dxn, gxn, gdyn, dwn, N, K in (
+            ("dY_gu", "W_gu", "W_gu_t", "X", "dX", "gX", "gdY_gu", "dW_gu", d["Ngu"], d["Hm"]),
+            ("dY_dn", "W_dn", "W_dn_t", "H", "dH", "gH", "gdY_dn", "dW_dn", d["Ndn"], d["Fm"])):
+        L.quant("quant_row", 0, moe[dyn], mb[dyn])
+        L.quant_batched("quant_col_batched", 1, moe[wn], mb[wtn])
+        qd, sd = mb[dyn][:2]
+        qwt, swt = mb[wtn][2:]
+        L.grouped("grouped_gemm_dgrad", G, offs, Tm, K, N, qd, sd, qwt, swt, mb[dxn],
+                  2.0 * Tm * N * K)
+        L.quant_grouped_col("quant_grouped_col", G, offs, moe[dyn], mb[gdyn])
+        L.quant_grouped_col("quant_grouped_col", G, offs, moe[xn], mb[gxn])
+        qa, sa = mb[gdyn]
+        qb, sb = mb[gxn]
+        L.grouped_wgrad("grouped_wgrad", G, offs, Tm, N, K, qa, sa, qb, sb, mb[dwn])
 
 
 def copy_rate(torch, nbytes=1 << 30, reps=5):
@@ -393,8 +450,9 @@ def main():
         "config": {
             "workload": (f"MXFP8 linear stack, {args.layers} layers {d['H']}->{d['F']}->{d['H']} at "
                          f"{d['T']} tokens, 1x32 dual-axis and 32x32-weight variants "
-                         f"(quantise + fprop/dgrad/wgrad) + MoE grouped gate_up/down over "
-                         f"{d['Tm']} routed tokens, {d['G']} experts"),
+                         f"(quantise + fprop/dgrad/wgrad) + MoE grouped gate_up/down forward and "
+                         f"backward (dgrad, per-expert wgrad) over {d['Tm']} routed tokens, "
+                         f"{d['G']} experts"),
             "tokens": d["T"], "hidden": d["H"], "ffn": d["F"], "layers": args.layers,
             "moe_tokens": d["Tm"], "experts": d["G"],
             "gemm_tflop_per_step": round(gemm_flop / 1e12, 3),

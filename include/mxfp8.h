@@ -141,6 +141,54 @@ mx_status mx_grouped_gemm(int64_t G, const int64_t* offsets, int64_t T, int64_t 
                           const void* a, const void* sa, const void* b, const void* sb, void* c,
                           hipStream_t stream);
 
+/* mx_quant over a batch of equally shaped matrices, e.g. the per-expert
+ * weights [G, rows, cols] of an MoE layer (the RFC quantises gate_up_proj /
+ * down_proj of every expert, section 2.2).  x holds `batch` contiguous BF16
+ * [rows, cols] matrices; every output is the stack of the per-matrix outputs
+ * of mx_quant in the same mode (q [batch, rows, cols], s [batch, rows,
+ * cols/32], q_t [batch, cols, rows], s_t [batch, cols, rows/32]; 32x32 tiles
+ * s [batch, rows/32, cols/32]).  Shape rules as mx_quant; 1 <= batch <= 65535.
+ * batch == 0 is a no-op. */
+mx_status mx_quant_batched(mx_quant_mode mode, const void* x, int64_t batch, int64_t rows,
+                           int64_t cols, void* q, void* s, void* q_t, void* s_t,
+                           hipStream_t stream);
+
+/* Columns of the per-group column-quantised token matrix: 128 * (T / 128 + G)
+ * (integer division).  Returns -1 for T < 0 or G < 1. */
+int64_t mx_grouped_col_capacity(int64_t T, int64_t G);
+
+/* MoE backward quantisation of a token matrix along the token axis, per
+ * expert group (RFC section 2.2: grouped-matmul quantisation of the MoE
+ * experts; the backward weight-gradient product contracts over each group's
+ * tokens).  x: BF16 [T, C] with the groups' rows in order; offsets: DEVICE
+ * int64 [G+1] as in mx_grouped_gemm.  Blocks of 32 tokens restart at every
+ * group offset; the last block of a group holds only its remaining tokens and
+ * its amax covers those alone.  Output, transposed like the column mode:
+ *   q_t [C, cap], s_t [C, cap / 32], cap = mx_grouped_col_capacity(T, G);
+ *   token o_g + k of group g sits at column P_g + k, P_g = 128 (o_g / 128 + g);
+ *   every column holding no token is part of an all-zero block (payload
+ *   0x00, scale 0x00), so each group's range [P_g, P_g + 128 ceil(m_g / 128))
+ *   is zero past its tokens.
+ * Requires C % 32 == 0, 1 <= G <= 512, 256 * cap < 2^31.  Offsets are read
+ * on the device and clamped into [0, T]; bad offsets give wrong blocks but
+ * never a bad access.  x may be NULL when T == 0 (the outputs are then all
+ * zero blocks).  C == 0 is a no-op. */
+mx_status mx_quant_grouped_col(const void* x, int64_t T, int64_t C, int64_t G,
+                               const int64_t* offsets, void* q_t, void* s_t, hipStream_t stream);
+
+/* Per-expert weight gradient of the MoE backward (RFC section 2.2):
+ *   c[g][m][n] = sum over the tokens t of group g of dY[t][m] * X[t][n]
+ * from the grouped column quantisations a = (q_t, s_t) of dY [T, M] and
+ * b = (q_t, s_t) of X [T, N] (mx_quant_grouped_col with the same offsets):
+ *   a [M, cap] + sa [M, cap/32], b [N, cap] + sb [N, cap/32],
+ *   c: BF16 [G, M, N]; an empty group gets zeros.
+ * FP32 accumulation, BF16 result; the columns of a group's range past its
+ * tokens must hold zero payload (as mx_quant_grouped_col writes them).
+ * Requires 1 <= G <= 512, 256 * cap < 2^31.  M == 0 or N == 0 is a no-op. */
+mx_status mx_grouped_gemm_wgrad(int64_t G, const int64_t* offsets, int64_t T, int64_t M, int64_t N,
+                                const void* a, const void* sa, const void* b, const void* sb,
+                                void* c, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -3,9 +3,10 @@
 Thin Python binding over the C ABI in ``include/mxfp8.h`` (``libmxfp8.so``,
 built in-tree by ``python -m mxfp8_microscaled_precision_amd.build``).  The
 functions named ``mx_*`` take raw device pointers and sizes exactly like the C
-entry points; ``quant``, ``gemm``, ``grouped_gemm`` and
-``process_quant_result`` marshal torch CUDA tensors (device memory and the
-current stream only) into those calls.  Every step of the computation runs in
+entry points; ``quant``, ``quant_batched``, ``quant_grouped_col``, ``gemm``,
+``grouped_gemm``, ``grouped_gemm_wgrad`` and ``process_quant_result`` marshal
+torch CUDA tensors (device memory and the current stream only) into those
+calls.  Every step of the computation runs in
 the HIP kernels; there is no CPU fallback: without the built library, or on a
 device other than gfx950, every call raises.
 """
@@ -16,8 +17,11 @@ import os
 
 __all__ = [
     "MXError", "lib", "mx_device_check", "mx_arch_supported", "mx_status_string",
-    "mx_last_error", "mx_quant", "mx_gemm", "mx_grouped_gemm", "quant", "gemm",
-    "grouped_gemm", "process_quant_result", "QUANT_MODES", "GEMM_LAYOUTS", "BSCALE_KINDS",
+    "mx_last_error", "mx_quant", "mx_gemm", "mx_grouped_gemm", "mx_quant_batched",
+    "mx_grouped_col_capacity", "mx_quant_grouped_col", "mx_grouped_gemm_wgrad", "quant", "gemm",
+    "grouped_gemm", "quant_batched", "quant_grouped_col", "grouped_gemm_wgrad",
+    "grouped_col_capacity", "process_quant_result", "QUANT_MODES", "GEMM_LAYOUTS",
+    "BSCALE_KINDS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxfp8.so")
@@ -61,6 +65,14 @@ def lib() -> ctypes.CDLL:
         L.mx_gemm.argtypes = [c_int, c_int, i64, i64, i64, vp, vp, vp, vp, vp, vp]
         L.mx_grouped_gemm.restype = c_int
         L.mx_grouped_gemm.argtypes = [i64, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp]
+        L.mx_quant_batched.restype = c_int
+        L.mx_quant_batched.argtypes = [c_int, vp, i64, i64, i64, vp, vp, vp, vp, vp]
+        L.mx_grouped_col_capacity.restype = i64
+        L.mx_grouped_col_capacity.argtypes = [i64, i64]
+        L.mx_quant_grouped_col.restype = c_int
+        L.mx_quant_grouped_col.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp]
+        L.mx_grouped_gemm_wgrad.restype = c_int
+        L.mx_grouped_gemm_wgrad.argtypes = [i64, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -95,6 +107,22 @@ def mx_gemm(layout, bkind, M, N, K, a, sa, b, sb, c, stream) -> int:
 
 def mx_grouped_gemm(G, offsets, T, N, K, a, sa, b, sb, c, stream) -> int:
     return lib().mx_grouped_gemm(G, offsets, T, N, K, a, sa, b, sb, c, stream)
+
+
+def mx_quant_batched(mode, x, batch, rows, cols, q, s, q_t, s_t, stream) -> int:
+    return lib().mx_quant_batched(mode, x, batch, rows, cols, q, s, q_t, s_t, stream)
+
+
+def mx_grouped_col_capacity(T, G) -> int:
+    return lib().mx_grouped_col_capacity(T, G)
+
+
+def mx_quant_grouped_col(x, T, C, G, offsets, q_t, s_t, stream) -> int:
+    return lib().mx_quant_grouped_col(x, T, C, G, offsets, q_t, s_t, stream)
+
+
+def mx_grouped_gemm_wgrad(G, offsets, T, M, N, a, sa, b, sb, c, stream) -> int:
+    return lib().mx_grouped_gemm_wgrad(G, offsets, T, M, N, a, sa, b, sb, c, stream)
 
 
 def _check(status: int):
@@ -207,6 +235,82 @@ def grouped_gemm(offsets, a, sa, b, sb, out=None):
     _need(out, torch.bfloat16, "out", 2)
     _check(mx_grouped_gemm(G, _ptr(offsets), T, N, K, _ptr(a), _ptr(sa), _ptr(b), _ptr(sb),
                            _ptr(out), _stream(a.device)))
+    return out
+
+
+def quant_batched(x, mode: str = "row"):
+    """mx_quant on every matrix of a BF16 stack x [B, rows, cols] (e.g. the
+    per-expert weights of an MoE layer); outputs are the stacked per-matrix
+    outputs of ``quant`` in the same mode."""
+    torch = _torch()
+    if mode not in QUANT_MODES:
+        raise ValueError(f"unknown quantisation mode {mode!r}; expected one of {list(QUANT_MODES)}")
+    _need(x, torch.bfloat16, "x", 3)
+    B, R, C = x.shape
+    dev, u8 = x.device, torch.uint8
+    q = s = qt = st = None
+    if mode in ("row", "dual", "32x32"):
+        q = torch.empty((B, R, C), dtype=u8, device=dev)
+        s = torch.empty((B, R // 32, C // 32) if mode == "32x32" else (B, R, C // 32), dtype=u8,
+                        device=dev)
+    if mode in ("col", "dual"):
+        qt = torch.empty((B, C, R), dtype=u8, device=dev)
+        st = torch.empty((B, C, R // 32), dtype=u8, device=dev)
+    _check(mx_quant_batched(QUANT_MODES[mode], _ptr(x), B, R, C, _ptr(q), _ptr(s), _ptr(qt),
+                            _ptr(st), _stream(dev)))
+    if mode == "row" or mode == "32x32":
+        return q, s
+    if mode == "col":
+        return qt, st
+    return q, s, qt, st
+
+
+def grouped_col_capacity(T: int, G: int) -> int:
+    """Columns of the per-group column-quantised token matrix."""
+    cap = mx_grouped_col_capacity(int(T), int(G))
+    if cap < 0:
+        raise ValueError(f"no capacity for T={T}, G={G}")
+    return cap
+
+
+def quant_grouped_col(x, offsets):
+    """Per-expert column quantisation along the token axis (MoE backward):
+    x BF16 [T, C], offsets int64 [G+1] on the device ->
+    (q_t [C, cap] u8, s_t [C, cap/32] u8), cap = grouped_col_capacity(T, G);
+    group g's tokens at columns 128 (offsets[g] // 128 + g) on."""
+    torch = _torch()
+    _need(x, torch.bfloat16, "x", 2)
+    _need(offsets, torch.int64, "offsets", 1)
+    T, C = x.shape
+    G = offsets.numel() - 1
+    cap = grouped_col_capacity(T, G)
+    qt = torch.empty((C, cap), dtype=torch.uint8, device=x.device)
+    st = torch.empty((C, cap // 32), dtype=torch.uint8, device=x.device)
+    _check(mx_quant_grouped_col(_ptr(x), T, C, G, _ptr(offsets), _ptr(qt), _ptr(st),
+                                _stream(x.device)))
+    return qt, st
+
+
+def grouped_gemm_wgrad(offsets, T: int, a, sa, b, sb, out=None):
+    """Per-expert weight gradient: out[g] = A_g * B_g^T over group g's token
+    columns of a [M, cap] and b [N, cap] (both from ``quant_grouped_col`` with
+    the same offsets); returns BF16 [G, M, N]."""
+    torch = _torch()
+    _need(offsets, torch.int64, "offsets", 1)
+    for t, n in ((a, "a"), (sa, "sa"), (b, "b"), (sb, "sb")):
+        _need(t, torch.uint8, n, 2)
+    G = offsets.numel() - 1
+    M, N = a.shape[0], b.shape[0]
+    cap = grouped_col_capacity(T, G)
+    if a.shape[1] != cap or b.shape[1] != cap or sa.shape != (M, cap // 32) or sb.shape != (N, cap // 32):
+        raise ValueError(f"operands must be [rows, {cap}] with scales [rows, {cap // 32}]")
+    if out is None:
+        out = torch.empty((G, M, N), dtype=torch.bfloat16, device=a.device)
+    _need(out, torch.bfloat16, "out", 3)
+    if tuple(out.shape) != (G, M, N):
+        raise ValueError(f"out must be [{G}, {M}, {N}]")
+    _check(mx_grouped_gemm_wgrad(G, _ptr(offsets), T, M, N, _ptr(a), _ptr(sa), _ptr(b), _ptr(sb),
+                                 _ptr(out), _stream(a.device)))
     return out
 
 

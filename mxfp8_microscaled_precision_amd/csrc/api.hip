@@ -62,6 +62,10 @@ mx_status current_device(int* dev) {
 
 bool mul_overflows(int64_t a, int64_t b) { return a != 0 && b > INT64_MAX / a; }
 
+// The GEMM kernels address a 256-row tile with 32-bit offsets (rows * K or
+// rows * cap bytes, out-of-range loads flagged by bit 31).
+constexpr int64_t K_LIMIT = (int64_t(1) << 31) / 256;
+
 }  // namespace
 
 extern "C" {
@@ -124,9 +128,9 @@ mx_status mx_quant(mx_quant_mode mode, const void* x, int64_t rows, int64_t cols
   hipError_t e;
   switch (mode) {
     case MX_QUANT_ROW_1x32: e = mx::launch_quant_row(x, rows * cols, q, s, stream); break;
-    case MX_QUANT_COL_1x32: e = mx::launch_quant_tile(1, x, rows, cols, q, s, q_t, s_t, stream); break;
-    case MX_QUANT_DUAL_AXIS: e = mx::launch_quant_tile(2, x, rows, cols, q, s, q_t, s_t, stream); break;
-    default: e = mx::launch_quant_tile(3, x, rows, cols, q, s, q_t, s_t, stream); break;
+    case MX_QUANT_COL_1x32: e = mx::launch_quant_tile(1, x, rows, cols, q, s, q_t, s_t, 1, stream); break;
+    case MX_QUANT_DUAL_AXIS: e = mx::launch_quant_tile(2, x, rows, cols, q, s, q_t, s_t, 1, stream); break;
+    default: e = mx::launch_quant_tile(3, x, rows, cols, q, s, q_t, s_t, 1, stream); break;
   }
   if (e != hipSuccess) return hip_fail(e, "quantisation kernel launch");
   return MX_OK;
@@ -146,6 +150,11 @@ mx_status mx_gemm(mx_gemm_layout layout, mx_bscale_kind bkind, int64_t M, int64_
   if (mul_overflows(M, K) || mul_overflows(N, K) || mul_overflows(M, N))
     return fail(MX_ERR_INVALID_ARG, "GEMM shape too large");
   if (K % 32 != 0) return fail(MX_ERR_UNSUPPORTED_SHAPE, "K %lld is not a multiple of 32", (long long)K);
+  if (K >= K_LIMIT)
+    return fail(MX_ERR_UNSUPPORTED_SHAPE, "K %lld too large for 32-bit tile offsets", (long long)K);
+  if (bkind == MX_BSCALE_32x32 && layout == MX_GEMM_DGRAD && (K + 256) * N >= (int64_t(1) << 31))
+    return fail(MX_ERR_UNSUPPORTED_SHAPE, "transposed 32x32 weight of %lld x %lld bytes too large",
+                (long long)K, (long long)N);
   if (bkind == MX_BSCALE_32x32 && N % 32 != 0)
     return fail(MX_ERR_UNSUPPORTED_SHAPE, "N %lld is not a multiple of 32 (32x32 weight tiles)",
                 (long long)N);
@@ -176,6 +185,8 @@ mx_status mx_grouped_gemm(int64_t G, const int64_t* offsets, int64_t T, int64_t 
   if (mul_overflows(T, K) || mul_overflows(T, N) || mul_overflows(G, N) || mul_overflows(G * N, K))
     return fail(MX_ERR_INVALID_ARG, "grouped GEMM shape too large");
   if (K % 32 != 0) return fail(MX_ERR_UNSUPPORTED_SHAPE, "K %lld is not a multiple of 32", (long long)K);
+  if (K >= K_LIMIT)
+    return fail(MX_ERR_UNSUPPORTED_SHAPE, "K %lld too large for 32-bit tile offsets", (long long)K);
   if (T == 0 || N == 0) return MX_OK;
   if (!offsets || !c) return fail(MX_ERR_INVALID_ARG, "offsets or c is NULL");
   if (K > 0 && (!a || !sa || !b || !sb)) return fail(MX_ERR_INVALID_ARG, "an operand is NULL");
@@ -194,6 +205,100 @@ mx_status mx_grouped_gemm(int64_t G, const int64_t* offsets, int64_t T, int64_t 
     e = mx::launch_grouped_gemm(G, offsets, T, N, K, a, sa, b, sb, c, cus, stream);
   }
   if (e != hipSuccess) return hip_fail(e, "grouped GEMM kernel launch");
+  return MX_OK;
+}
+
+mx_status mx_quant_batched(mx_quant_mode mode, const void* x, int64_t batch, int64_t rows,
+                           int64_t cols, void* q, void* s, void* q_t, void* s_t,
+                           hipStream_t stream) {
+  g_err[0] = '\0';
+  if (mode < MX_QUANT_ROW_1x32 || mode > MX_QUANT_BLOCK_32x32)
+    return fail(MX_ERR_INVALID_ARG, "unknown quantisation mode %d", (int)mode);
+  if (batch < 0 || batch > 65535) return fail(MX_ERR_INVALID_ARG, "batch %lld not in [0, 65535]", (long long)batch);
+  if (rows < 0 || cols < 0) return fail(MX_ERR_INVALID_ARG, "negative shape [%lld, %lld]",
+                                        (long long)rows, (long long)cols);
+  if (mul_overflows(rows, cols) || mul_overflows(batch, rows * cols) ||
+      batch * rows * cols > (INT64_MAX / 4))
+    return fail(MX_ERR_INVALID_ARG, "shape too large");
+  const bool need_row = mode == MX_QUANT_ROW_1x32 || mode == MX_QUANT_DUAL_AXIS ||
+                        mode == MX_QUANT_BLOCK_32x32;
+  const bool need_col = mode == MX_QUANT_COL_1x32 || mode == MX_QUANT_DUAL_AXIS;
+  if (cols % 32 != 0)
+    return fail(MX_ERR_UNSUPPORTED_SHAPE, "cols %lld is not a multiple of 32", (long long)cols);
+  if (mode != MX_QUANT_ROW_1x32 && rows % 32 != 0)
+    return fail(MX_ERR_UNSUPPORTED_SHAPE, "rows %lld is not a multiple of 32", (long long)rows);
+  if (mode != MX_QUANT_ROW_1x32 && (cols + 127) / 128 > 65535)
+    return fail(MX_ERR_UNSUPPORTED_SHAPE, "cols %lld exceeds the column-tile grid", (long long)cols);
+  if (batch == 0 || rows == 0 || cols == 0) return MX_OK;
+  if (!x) return fail(MX_ERR_INVALID_ARG, "x is NULL");
+  if (need_row && (!q || !s)) return fail(MX_ERR_INVALID_ARG, "q and s are required for this mode");
+  if (need_col && (!q_t || !s_t))
+    return fail(MX_ERR_INVALID_ARG, "q_t and s_t are required for this mode");
+  int dev;
+  mx_status st = current_device(&dev);
+  if (st != MX_OK) return st;
+  hipError_t e;
+  // row blocks and 32x32 tiles never cross a matrix boundary: the stack is
+  // one [batch * rows, cols] matrix for them
+  switch (mode) {
+    case MX_QUANT_ROW_1x32: e = mx::launch_quant_row(x, batch * rows * cols, q, s, stream); break;
+    case MX_QUANT_BLOCK_32x32:
+      e = mx::launch_quant_tile(3, x, batch * rows, cols, q, s, q_t, s_t, 1, stream);
+      break;
+    case MX_QUANT_COL_1x32: e = mx::launch_quant_tile(1, x, rows, cols, q, s, q_t, s_t, batch, stream); break;
+    default: e = mx::launch_quant_tile(2, x, rows, cols, q, s, q_t, s_t, batch, stream); break;
+  }
+  if (e != hipSuccess) return hip_fail(e, "quantisation kernel launch");
+  return MX_OK;
+}
+
+int64_t mx_grouped_col_capacity(int64_t T, int64_t G) {
+  if (T < 0 || G < 1 || G > (INT64_MAX / 128) - T / 128) return -1;
+  return 128 * (T / 128 + G);
+}
+
+mx_status mx_quant_grouped_col(const void* x, int64_t T, int64_t C, int64_t G,
+                               const int64_t* offsets, void* q_t, void* s_t, hipStream_t stream) {
+  g_err[0] = '\0';
+  if (G < 1 || G > 512) return fail(MX_ERR_INVALID_ARG, "group count %lld not in [1, 512]", (long long)G);
+  if (T < 0 || C < 0) return fail(MX_ERR_INVALID_ARG, "negative shape [%lld, %lld]", (long long)T,
+                                  (long long)C);
+  if (C % 32 != 0) return fail(MX_ERR_UNSUPPORTED_SHAPE, "cols %lld is not a multiple of 32", (long long)C);
+  if ((C + 127) / 128 > 65535)
+    return fail(MX_ERR_UNSUPPORTED_SHAPE, "cols %lld exceeds the column-tile grid", (long long)C);
+  const int64_t cap = mx_grouped_col_capacity(T, G);
+  if (cap < 0 || cap >= K_LIMIT)
+    return fail(MX_ERR_UNSUPPORTED_SHAPE, "token capacity %lld too large", (long long)cap);
+  if (mul_overflows(T, C) || mul_overflows(cap, C)) return fail(MX_ERR_INVALID_ARG, "shape too large");
+  if (C == 0) return MX_OK;
+  if (!offsets || !q_t || !s_t) return fail(MX_ERR_INVALID_ARG, "offsets, q_t or s_t is NULL");
+  if (T > 0 && !x) return fail(MX_ERR_INVALID_ARG, "x is NULL");
+  int dev;
+  mx_status st = current_device(&dev);
+  if (st != MX_OK) return st;
+  hipError_t e = mx::launch_quant_grouped_col(x, T, C, G, offsets, cap, q_t, s_t, stream);
+  if (e != hipSuccess) return hip_fail(e, "grouped column quantisation kernel launch");
+  return MX_OK;
+}
+
+mx_status mx_grouped_gemm_wgrad(int64_t G, const int64_t* offsets, int64_t T, int64_t M, int64_t N,
+                                const void* a, const void* sa, const void* b, const void* sb,
+                                void* c, hipStream_t stream) {
+  g_err[0] = '\0';
+  if (G < 1 || G > 512) return fail(MX_ERR_INVALID_ARG, "group count %lld not in [1, 512]", (long long)G);
+  if (T < 0 || M < 0 || N < 0) return fail(MX_ERR_INVALID_ARG, "negative grouped wgrad shape");
+  const int64_t cap = mx_grouped_col_capacity(T, G);
+  if (cap < 0 || cap >= K_LIMIT)
+    return fail(MX_ERR_UNSUPPORTED_SHAPE, "token capacity %lld too large", (long long)cap);
+  if (mul_overflows(M, cap) || mul_overflows(N, cap) || mul_overflows(M, N) || mul_overflows(G, M * N))
+    return fail(MX_ERR_INVALID_ARG, "grouped wgrad shape too large");
+  if (M == 0 || N == 0) return MX_OK;
+  if (!offsets || !c || !a || !sa || !b || !sb) return fail(MX_ERR_INVALID_ARG, "a pointer is NULL");
+  int dev;
+  mx_status st = current_device(&dev);
+  if (st != MX_OK) return st;
+  hipError_t e = mx::launch_grouped_wgrad(G, offsets, T, M, N, cap, a, sa, b, sb, c, stream);
+  if (e != hipSuccess) return hip_fail(e, "grouped wgrad kernel launch");
   return MX_OK;
 }
 

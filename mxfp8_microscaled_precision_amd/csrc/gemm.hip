@@ -8,130 +8,16 @@
 // support to FSDP", section 2.2: gate_up_proj / down_proj of MoE experts).
 // The 32x32 weight variant takes one scale per 32x32 weight tile, and its
 // backward-data product reads the one shared FP8 weight transposed (RFC
-// sections 3.1 and 3.3.3).
-//
-// Hardware mapping (measured on the device):
-//   v_mfma_scale_f32_32x32x64_f8f6f4, wave64.  Operand lane l holds row l%32;
-//   lane half g = l/32 holds K bytes [16g, 16g+16) of scale block 0 and
-//   [32+16g, 32+16g+16) of scale block 1; the scale of block b for row i is
-//   the byte (op_sel) of lane i + 32b's scale register.  Result lane l, acc
-//   j: row 8(j/4) + 4(l/32) + j%4, column l%32.
-// The MFMA's first operand is B (our N side) and its second is A (our M
-// side), so each lane ends with groups of four consecutive n of one C row;
-// lanes l and l + 32 trade groups (v_permlane32_swap) so that every store
-// writes 8 consecutive BF16 (16 bytes).
+// sections 3.1 and 3.3.3).  The MFMA lane layout and the shared helpers are
+// in gemm_common.h.
 //
 // Workgroup tile 256 (M) x 256 (N), K step 128 bytes, four waves of 128x128
 // (16 accumulators of 32x32 each).  Both operands are staged through a
 // double-buffered LDS tile whose 16-byte chunks are XOR-swizzled by row, so
 // the fragment reads are free of bank conflicts.
-#include "mx_device.h"
-#include "mx_kernels.h"
+#include "gemm_common.h"
 
 namespace mx {
-
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v2i __attribute__((ext_vector_type(2)));
-typedef float v16f __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) v2i lds_v2i;
-typedef __attribute__((address_space(3))) v4i lds_v4i;
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
-typedef __attribute__((address_space(3))) uint16_t lds_u16;
-typedef __attribute__((address_space(3))) void lds_void;
-
-constexpr int BM = 256;
-constexpr int BN = 256;
-constexpr int BK = 128;
-constexpr int NT = 256;
-constexpr int A_TILE = BM * BK;           // 32 KB
-constexpr int B_TILE = BN * BK;           // 32 KB
-constexpr int STAGE = A_TILE + B_TILE;    // 64 KB
-constexpr int SCALE_TILE = 2 * 256 * 16; // A and B scale bytes of four K steps: 8 KB
-constexpr int PF_DIST = 3;                // L2 prefetch distance, in K steps
-constexpr int GM_TILES = 8;               // tile grouping along M (tile_of)
-constexpr int CHUNKS = A_TILE / 16 / NT;  // 16-byte chunks per thread per operand: 8
-constexpr int MAX_GROUPS = 512;
-
-// Row-major LDS tiles with 128-byte rows keep 16-byte chunk c of row r at
-// physical chunk c ^ ((r >> 1) & 7).  gfx950 LDS serves 256 bytes (64
-// banks) per cycle, i.e. 16 lanes of a 16-byte read; the 16 lanes of a
-// fragment read take rows r .. r+15 at one logical chunk, and this swizzle
-// puts them in 16 distinct 16-byte bank groups.
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
-
-// Fragment of 32 rows x 64 K from a row-major LDS tile (128-byte rows).
-__device__ __forceinline__ v8i read_frag(const lds_u8* tile, int row, int s, int g) {
-  const int x = swz(row);
-  v4i lo = *(const lds_v4i*)(tile + row * BK + (((2 * s + g) ^ x) << 4));
-  v4i hi = *(const lds_v4i*)(tile + row * BK + (((4 + 2 * s + g) ^ x) << 4));
-  return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-}
-
-// Fragment of 32 columns x 64 K from a [128 k][256 n] LDS tile (256-byte
-// rows), read transposed with ds_read_b64_tr_b8: in each group of 16 lanes,
-// lane 2r+h points at 8 bytes of row k+r and lane i receives byte i of the
-// eight 16-byte rows, i.e. 8 consecutive k of column i.
-__device__ __forceinline__ v8i read_frag_t(const lds_u8* tile, int nb, int s, int lane) {
-  const int g = lane >> 5, q = (lane >> 4) & 1, r = (lane & 15) >> 1, hh = lane & 1;
-  // row k = k_const + 16g + r with k_const a multiple of 8, so k & 7 = r and
-  // the swizzled chunk is lane-only; every piece is base + a constant offset.
-  // Chunk c of row k sits at physical chunk c ^ 2(k & 7): the two 16-lane
-  // groups served together read chunks c, c+1 (c even) of the same 8 rows,
-  // which land on 16 distinct 16-byte bank groups.
-  const int ncol = nb + 16 * q + 8 * hh;
-  const lds_u8* base = tile + (16 * g + r) * 256 + (((ncol >> 4) ^ (2 * r)) << 4) + (ncol & 15);
-  v2i p[4];
-#pragma unroll
-  for (int t = 0; t < 4; t++) {
-    const int kc = (t >> 1) * 64 + 32 * s + (t & 1) * 8;
-    p[t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(base + kc * 256));
-  }
-  return (v8i){p[0].x, p[0].y, p[1].x, p[1].y, p[2].x, p[2].y, p[3].x, p[3].y};
-}
-
-// Raw buffer descriptor over [base, base + bytes): loads at offsets >= bytes
-// return zero, which fills the tile edges (rows past M or N, K past the end).
-// Every input is uniform across the wave; readfirstlane makes that visible
-// to the compiler so the descriptor lives in scalar registers.
-__device__ __forceinline__ u32x4 make_rsrc(const void* base, int64_t bytes) {
-  const uint64_t p = (uint64_t)base;
-  return (u32x4){(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p),
-                 (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(p >> 32) & 0xFFFFu)),
-                 (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)bytes), 0x00020000u};
-}
-
-// 16 bytes per lane from the buffer at voffset into LDS at lds + 16 * lane
-// (buffer_load_dwordx4 ... lds).  Issued through asm so that the compiler does
-// not order LDS reads of the other stage behind these loads; the kernel waits
-// for them itself (vmcnt(0) before the barrier that publishes the stage).
-__device__ __forceinline__ void dma16(const lds_u8* lds, uint32_t voffset, u32x4 rsrc) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(m0), "v"(voffset), "s"(rsrc)
-               : "memory");
-}
-
-// s_waitcnt vmcnt(0) (expcnt, lgkmcnt left at their maxima), as a builtin so
-// the compiler knows every earlier vector-memory load has completed.
-__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-// s_waitcnt vmcnt(2): everything but the two most recent vector-memory ops
-// (the L2 prefetches, which nobody waits for) has completed.
-__device__ __forceinline__ void wait_vm_but_prefetch() { __builtin_amdgcn_s_waitcnt(0x0F72); }
-
-// L2 prefetch: one dword per lane (one 128-byte line per row) dropped into a
-// scratch LDS area that is never read.  LDS-DMA has no register destination,
-// so nothing in the kernel can race with the late arrival.
-__device__ __forceinline__ void prefetch_lines(const lds_u8* scratch, uint32_t voffset, u32x4 rsrc) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)scratch);
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-               :
-               : "s"(m0), "v"(voffset), "s"(rsrc)
-               : "memory");
-}
-
-constexpr uint32_t OOB = 0x80000000u;  // an offset past every tile buffer
 
 // One workgroup tile.  Pipeline (two LDS stages, one barrier per K step):
 //   phase A of step kt: MFMAs of K half 0 on registers F0, LDS reads of
@@ -234,14 +120,21 @@ struct Tile {
   // buffer -> LDS loads of the K step starting at byte k0 into stage st:
   // chunk u of A and of B for this wave (u = 0 .. CHUNKS-1).  Chunks at or
   // past K read as zero (K is a multiple of 32, so whole 16-byte chunks are
-  // in or out), which also makes the loads of steps past the end harmless.
-  // With FAST (K a multiple of the K step) no real step is partial; the
-  // loads of steps past the end land in a stage that is never read.
-  // Transposed B needs no K check at all: rows at or past K lie beyond the
-  // end of its buffer.
-  __device__ __forceinline__ void dma_a(lds_u8* st, int64_t k0, int u, int wave, int lane) {
+  // in or out).  With FAST (K a multiple of the K step) no real step is
+  // partial, and a step past the end gets the base offset OOB: its loads
+  // touch no memory.  step_base() is uniform, one scalar select per step.
+  __device__ __forceinline__ uint32_t step_base_a(int64_t k0) const {
+    return k0 < K ? (uint32_t)k0 : OOB;
+  }
+  __device__ __forceinline__ uint32_t step_base_b(int64_t k0) const {
+    if (BMODE == GEMM_B_TILE_T) return k0 < K ? (uint32_t)k0 * (uint32_t)N : OOB;
+    return k0 < K ? (uint32_t)k0 : OOB;
+  }
+
+  __device__ __forceinline__ void dma_a(lds_u8* st, int64_t k0, uint32_t base, int u, int wave,
+                                        int lane) {
     const int t = wave + 4 * u;
-    uint32_t off = voff_a + (uint32_t)k0 + u * a_step;
+    uint32_t off = voff_a + base + u * a_step;
     if (!FAST) {
       const int lc = (lane & 7) ^ ((4 * wave + (lane >> 4)) & 7);
       off = (k0 + 16 * lc < K) ? off : OOB;
@@ -249,26 +142,24 @@ struct Tile {
     dma16(st + t * 1024, off, ra);
   }
 
-  __device__ __forceinline__ void dma_b(lds_u8* st, int64_t k0, int u, int wave, int lane) {
+  __device__ __forceinline__ void dma_b(lds_u8* st, int64_t k0, uint32_t base, int u, int wave,
+                                        int lane) {
     const int t = wave + 4 * u;
-    if (BMODE == GEMM_B_TILE_T) {
-      const uint32_t off = voff_b + (uint32_t)k0 * (uint32_t)N + u * b_step;
-      dma16(st + A_TILE + t * 1024, off, rb);
-    } else {
-      uint32_t off = voff_b + (uint32_t)k0 + u * b_step;
-      if (!FAST) {
-        const int lc = (lane & 7) ^ ((4 * wave + (lane >> 4)) & 7);
-        off = (k0 + 16 * lc < K) ? off : OOB;
-      }
-      dma16(st + A_TILE + t * 1024, off, rb);
+    uint32_t off = voff_b + base + u * b_step;
+    // transposed B: rows at or past K lie beyond the end of its buffer
+    if (!FAST && BMODE != GEMM_B_TILE_T) {
+      const int lc = (lane & 7) ^ ((4 * wave + (lane >> 4)) & 7);
+      off = (k0 + 16 * lc < K) ? off : OOB;
     }
+    dma16(st + A_TILE + t * 1024, off, rb);
   }
 
   __device__ __forceinline__ void issue_stage(lds_u8* st, int64_t k0, int wave, int lane) {
+    const uint32_t ba = step_base_a(k0), bb = step_base_b(k0);
 #pragma unroll
-    for (int u = 0; u < CHUNKS; u++) dma_a(st, k0, u, wave, lane);
+    for (int u = 0; u < CHUNKS; u++) dma_a(st, k0, ba, u, wave, lane);
 #pragma unroll
-    for (int u = 0; u < CHUNKS; u++) dma_b(st, k0, u, wave, lane);
+    for (int u = 0; u < CHUNKS; u++) dma_b(st, k0, bb, u, wave, lane);
   }
 
   // Scale words of K step kb0 (blocks kb0 .. kb0+3).  load_scales fetches raw
@@ -351,8 +242,9 @@ struct Tile {
   // LDS_SCALES: scale-tile loads of the 4-step group whose first block is
   // kb0, and the per-step reads (two blocks per lane: 2g and 2g+1 of step q).
   __device__ __forceinline__ void dma_scales(lds_u8* buf, int64_t kb0, int wave) {
-    dma16(buf + wave * 1024, svoff + (uint32_t)kb0, rsa);
-    if (BMODE == GEMM_B_ROW) dma16(buf + 4096 + wave * 1024, svoff + (uint32_t)kb0, rsb);
+    const uint32_t off = kb0 < nkb ? svoff + (uint32_t)kb0 : OOB;  // none past the end
+    dma16(buf + wave * 1024, off, rsa);
+    if (BMODE == GEMM_B_ROW) dma16(buf + 4096 + wave * 1024, off, rsb);
   }
 
   __device__ __forceinline__ void read_scales(const lds_u8* buf, int q, int wm, int wn, int lane,
@@ -386,29 +278,16 @@ struct Tile {
   template <int S>
   __device__ __forceinline__ void mma(const v8i* af, const v8i* bf, const uint32_t* sar,
                                       const uint32_t* sbr, v16f (&acc)[4][4]) {
-#pragma unroll
-    for (int fn = 0; fn < 4; fn++)
-#pragma unroll
-      for (int fm = 0; fm < 4; fm++)
-        acc[fn][fm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            bf[fn], af[fm], acc[fn][fm], 0, 0, S, (int)sbr[fn], S, (int)sar[fm]);
+    mma_tile<S>(af, bf, sar, sbr, acc);
   }
 
   // LDS fragment reads and vector-memory loads issued per K half
   static constexpr int DS_READS = BMODE == GEMM_B_TILE_T ? 8 + 16 : 16;
   static constexpr int SCALE_LOADS = (BMODE == GEMM_B_TILE_T && !FAST) ? 4 + 16 : 8;
 
-  // Ask the scheduler for MFMA, LDS read, vector load, MFMA, ... so the
-  // MFMA pipe always has queued work while the loads are in flight.
   template <int NDS, int NVM>
   __device__ __forceinline__ static void interleave() {
-    constexpr int ds_per = (NDS + 15) / 16, vm_per = (NVM + 15) / 16;
-#pragma unroll
-    for (int i = 0; i < 16; i++) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
-      if (ds_per) __builtin_amdgcn_sched_group_barrier(0x100, ds_per, 0);  // DS read
-      if (vm_per) __builtin_amdgcn_sched_group_barrier(0x020, vm_per, 0);  // VMEM read
-    }
+    interleave_ops<NDS, NVM>();
   }
 
   // One K step on stage `cur`, prefetching into `nxt` (see the pipeline
@@ -430,12 +309,13 @@ struct Tile {
     for (int f = 0; f < 4; f++) asm volatile("" : "+v"(nx_a[f]), "+v"(nx_b[f]));
     // phase B: fragment reads of stage kt+1 and loads of stage kt+2 into `cur`
     const int64_t k2 = (kt + 2) * BK;
+    const uint32_t ba = step_base_a(k2), bb = step_base_b(k2);
     const int g = lane >> 5, i = lane & 31;
 #pragma unroll
     for (int f = 0; f < 4; f++) {
       f0a[f] = read_frag(nxt, 128 * wm + 32 * f + i, 0, g);
-      dma_a(cur, k2, 2 * f, wave, lane);
-      dma_a(cur, k2, 2 * f + 1, wave, lane);
+      dma_a(cur, k2, ba, 2 * f, wave, lane);
+      dma_a(cur, k2, ba, 2 * f + 1, wave, lane);
     }
 #pragma unroll
     for (int f = 0; f < 4; f++) {
@@ -443,8 +323,8 @@ struct Tile {
         f0b[f] = read_frag_t(nxt + A_TILE, 128 * wn + 32 * f, 0, lane);
       else
         f0b[f] = read_frag(nxt + A_TILE, 128 * wn + 32 * f + i, 0, g);
-      dma_b(cur, k2, 2 * f, wave, lane);
-      dma_b(cur, k2, 2 * f + 1, wave, lane);
+      dma_b(cur, k2, bb, 2 * f, wave, lane);
+      dma_b(cur, k2, bb, 2 * f + 1, wave, lane);
     }
     mma<1>(f1a, f1b, sc_a, sc_b, acc);
     interleave<DS_READS, 0>();
@@ -479,12 +359,13 @@ struct Tile {
     if (U == 0) dma_scales(sdma, (kt + 4) * (BK / 32), wave);
     read_scales(sread, (U + 1) & 3, wm, wn, lane, nx_a, nx_b);
     const int64_t k2 = (kt + 2) * BK;
+    const uint32_t ba = step_base_a(k2), bb = step_base_b(k2);
     const int g = lane >> 5, i = lane & 31;
 #pragma unroll
     for (int f = 0; f < 4; f++) {
       f0a[f] = read_frag(nxt, 128 * wm + 32 * f + i, 0, g);
-      dma_a(cur, k2, 2 * f, wave, lane);
-      dma_a(cur, k2, 2 * f + 1, wave, lane);
+      dma_a(cur, k2, ba, 2 * f, wave, lane);
+      dma_a(cur, k2, ba, 2 * f + 1, wave, lane);
     }
 #pragma unroll
     for (int f = 0; f < 4; f++) {
@@ -492,13 +373,14 @@ struct Tile {
         f0b[f] = read_frag_t(nxt + A_TILE, 128 * wn + 32 * f, 0, lane);
       else
         f0b[f] = read_frag(nxt + A_TILE, 128 * wn + 32 * f + i, 0, g);
-      dma_b(cur, k2, 2 * f, wave, lane);
-      dma_b(cur, k2, 2 * f + 1, wave, lane);
+      dma_b(cur, k2, bb, 2 * f, wave, lane);
+      dma_b(cur, k2, bb, 2 * f + 1, wave, lane);
     }
     if (!GB) {
-      const uint32_t kp = (uint32_t)((kt + PF_DIST) * BK);
-      prefetch_lines(pf_scratch + wave * 512, (pf_row + kp) | pf_a, ra);
-      prefetch_lines(pf_scratch + wave * 512 + 256, (pf_row + kp) | pf_b, rb);
+      const int64_t kp = (kt + PF_DIST) * BK;
+      const uint32_t live = kp < K ? 0u : OOB;
+      prefetch_lines(pf_scratch + wave * 512, (pf_row + (uint32_t)kp) | pf_a | live, ra);
+      prefetch_lines(pf_scratch + wave * 512 + 256, (pf_row + (uint32_t)kp) | pf_b | live, rb);
     }
     mma<1>(f1a, f1b, sc_a, sc_b, acc);
     interleave<DS_READS + (GB ? 4 : 8), 0>();
@@ -536,6 +418,14 @@ struct Tile {
       read_scales(ss0, 0, wm, wn, lane, sc_a, sc_b);
       if (BMODE != GEMM_B_ROW) finish_scales_b(lane, nx_b, sc_b);
       issue_stage(st1, BK, wave, lane);
+      if (BMODE == GEMM_B_ROW) {
+        // The steps wait with vmcnt(2), which leaves the two most recent
+        // loads in flight: those must be prefetches, never stage loads.  So
+        // the prologue ends with the two prefetches of stage 2.
+        const uint32_t kp = 2 * BK;
+        prefetch_lines(pf_scratch + wave * 512, (pf_row + kp) | pf_a, ra);
+        prefetch_lines(pf_scratch + wave * 512 + 256, (pf_row + kp) | pf_b, rb);
+      }
       read_frags<0>(st0, wm, wn, lane, f0a, f0b);
       for (int64_t j = 0; 4 * j < nk; j++) {
         const int64_t kt = 4 * j;
@@ -566,70 +456,12 @@ struct Tile {
       if (kt < nk)
         step(st0, st1, kt, wave, wm, wn, lane, sc_a, sc_b, nx_a, nx_b, f0a, f0b, f1a, f1b, acc);
     }
-    // epilogue: FP32 -> BF16 (RNE).  A lane holds four consecutive n of its
-    // row per group r4 (n = 8 r4 + 4 g + 0..3); one v_permlane32_swap per
-    // dword pair trades groups between lanes l and l + 32, after which lane
-    // half g holds the 8 consecutive n at 8 g + 16 h for h = 0, 1 and stores
-    // them as one 16-byte write.  The swaps run on every lane before any
-    // lane drops out at the M edge.
-    const int g = lane >> 5, i = lane & 31;
-    const bool vec_ok = (N & 7) == 0;
-#pragma unroll
-    for (int fn = 0; fn < 4; fn++) {
-#pragma unroll
-      for (int fm = 0; fm < 4; fm++) {
-        const v16f& v = acc[fn][fm];
-        uint32_t p[4][2];
-#pragma unroll
-        for (int r4 = 0; r4 < 4; r4++) {
-          p[r4][0] = cvt_pk_bf16(v[4 * r4 + 0], v[4 * r4 + 1]);
-          p[r4][1] = cvt_pk_bf16(v[4 * r4 + 2], v[4 * r4 + 3]);
-        }
-#pragma unroll
-        for (int h = 0; h < 2; h++)
-#pragma unroll
-          for (int d = 0; d < 2; d++) {
-            const auto s = __builtin_amdgcn_permlane32_swap(p[2 * h][d], p[2 * h + 1][d], false, false);
-            p[2 * h][d] = s[0];
-            p[2 * h + 1][d] = s[1];
-          }
-        const int64_t m = m0 + 128 * wm + 32 * fm + i;
-        if (m >= m_end) continue;
-#pragma unroll
-        for (int h = 0; h < 2; h++) {
-          const int64_t n = n0 + 128 * wn + 32 * fn + 16 * h + 8 * g;
-          const uint32_t w[4] = {p[2 * h][0], p[2 * h][1], p[2 * h + 1][0], p[2 * h + 1][1]};
-          uint16_t* dst = c + m * N + n;
-          if (vec_ok && n + 8 <= N) {
-            *(uint4*)dst = make_uint4(w[0], w[1], w[2], w[3]);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; e++)
-              if (n + e < N) dst[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
-          }
-        }
-      }
-    }
+    // no load may still be writing this workgroup's LDS when it ends
+    wait_vm_all();
+    store_tile_bf16(acc, c, N, m0, m_end, n0, N, wm, wn, lane);
   }
 };
 
-// Linear workgroup id -> a contiguous run of tiles per XCD (workgroups are
-// dealt to the 8 XCDs round-robin), then grouped M-major order inside the
-// run so neighbouring tiles share A rows and B rows in that XCD's L2.
-__device__ __forceinline__ void tile_of(int64_t bid, int64_t nm, int64_t nn, int64_t& mt,
-                                        int64_t& nt) {
-  const int64_t total = nm * nn;
-  const int64_t x = bid & 7, local = bid >> 3;
-  const int64_t per = total >> 3, rem = total & 7;
-  const int64_t t = x * per + (x < rem ? x : rem) + local;
-  constexpr int64_t GM = GM_TILES;
-  const int64_t group = t / (GM * nn);
-  const int64_t first = group * GM;
-  const int64_t gsz = (nm - first) < GM ? (nm - first) : GM;
-  const int64_t in = t % (GM * nn);
-  mt = first + in % gsz;
-  nt = in / gsz;
-}
 
 template <int BMODE, bool FAST>
 __global__ void __launch_bounds__(NT)

@@ -1,0 +1,226 @@
+// Device helpers shared by the MXFP8 GEMM kernels for gfx950 (internal).
+//
+// Hardware mapping (measured on the device):
+//   v_mfma_scale_f32_32x32x64_f8f6f4, wave64.  Operand lane l holds row l%32;
+//   lane half g = l/32 holds K bytes [16g, 16g+16) of scale block 0 and
+//   [32+16g, 32+16g+16) of scale block 1; the scale of block b for row i is
+//   the byte (op_sel) of lane i + 32b's scale register.  Result lane l, acc
+//   j: row 8(j/4) + 4(l/32) + j%4, column l%32.
+// The MFMA's first operand is B (the N side) and its second is A (the M
+// side), so each lane ends with groups of four consecutive n of one C row;
+// lanes l and l + 32 trade groups (v_permlane32_swap) so that every store
+// writes 8 consecutive BF16 (16 bytes).
+#pragma once
+#include "mx_device.h"
+#include "mx_kernels.h"
+
+namespace mx {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) v2i lds_v2i;
+typedef __attribute__((address_space(3))) v4i lds_v4i;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int BM = 256;
+constexpr int BN = 256;
+constexpr int BK = 128;
+constexpr int NT = 256;
+constexpr int A_TILE = BM * BK;           // 32 KB
+constexpr int B_TILE = BN * BK;           // 32 KB
+constexpr int STAGE = A_TILE + B_TILE;    // 64 KB
+constexpr int SCALE_TILE = 2 * 256 * 16; // A and B scale bytes of four K steps: 8 KB
+constexpr int PF_DIST = 3;                // L2 prefetch distance, in K steps
+constexpr int GM_TILES = 8;               // tile grouping along M (tile_of)
+constexpr int CHUNKS = A_TILE / 16 / NT;  // 16-byte chunks per thread per operand: 8
+constexpr int MAX_GROUPS = 512;
+
+// Row-major LDS tiles with 128-byte rows keep 16-byte chunk c of row r at
+// physical chunk c ^ ((r >> 1) & 7).  gfx950 LDS serves 256 bytes (64
+// banks) per cycle, i.e. 16 lanes of a 16-byte read; the 16 lanes of a
+// fragment read take rows r .. r+15 at one logical chunk, and this swizzle
+// puts them in 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
+// Fragment of 32 rows x 64 K from a row-major LDS tile (128-byte rows).
+__device__ __forceinline__ v8i read_frag(const lds_u8* tile, int row, int s, int g) {
+  const int x = swz(row);
+  v4i lo = *(const lds_v4i*)(tile + row * BK + (((2 * s + g) ^ x) << 4));
+  v4i hi = *(const lds_v4i*)(tile + row * BK + (((4 + 2 * s + g) ^ x) << 4));
+  return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+}
+
+// Fragment of 32 columns x 64 K from a [128 k][256 n] LDS tile (256-byte
+// rows), read transposed with ds_read_b64_tr_b8: in each group of 16 lanes,
+// lane 2r+h points at 8 bytes of row k+r and lane i receives byte i of the
+// eight 16-byte rows, i.e. 8 consecutive k of column i.
+__device__ __forceinline__ v8i read_frag_t(const lds_u8* tile, int nb, int s, int lane) {
+  const int g = lane >> 5, q = (lane >> 4) & 1, r = (lane & 15) >> 1, hh = lane & 1;
+  // row k = k_const + 16g + r with k_const a multiple of 8, so k & 7 = r and
+  // the swizzled chunk is lane-only; every piece is base + a constant offset.
+  // Chunk c of row k sits at physical chunk c ^ 2(k & 7): the two 16-lane
+  // groups served together read chunks c, c+1 (c even) of the same 8 rows,
+  // which land on 16 distinct 16-byte bank groups.
+  const int ncol = nb + 16 * q + 8 * hh;
+  const lds_u8* base = tile + (16 * g + r) * 256 + (((ncol >> 4) ^ (2 * r)) << 4) + (ncol & 15);
+  v2i p[4];
+#pragma unroll
+  for (int t = 0; t < 4; t++) {
+    const int kc = (t >> 1) * 64 + 32 * s + (t & 1) * 8;
+    p[t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(base + kc * 256));
+  }
+  return (v8i){p[0].x, p[0].y, p[1].x, p[1].y, p[2].x, p[2].y, p[3].x, p[3].y};
+}
+
+// Raw buffer descriptor over [base, base + bytes): loads at offsets >= bytes
+// return zero, which fills the tile edges (rows past M or N, K past the end).
+// Every input is uniform across the wave; readfirstlane makes that visible
+// to the compiler so the descriptor lives in scalar registers.
+__device__ __forceinline__ u32x4 make_rsrc(const void* base, int64_t bytes) {
+  const uint64_t p = (uint64_t)base;
+  return (u32x4){(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p),
+                 (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(p >> 32) & 0xFFFFu)),
+                 (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)bytes), 0x00020000u};
+}
+
+// 16 bytes per lane from the buffer at voffset into LDS at lds + 16 * lane
+// (buffer_load_dwordx4 ... lds).  Issued through asm so that the compiler does
+// not order LDS reads of the other stage behind these loads; the kernel waits
+// for them itself (vmcnt(0) before the barrier that publishes the stage).
+__device__ __forceinline__ void dma16(const lds_u8* lds, uint32_t voffset, u32x4 rsrc) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(m0), "v"(voffset), "s"(rsrc)
+               : "memory");
+}
+
+// s_waitcnt vmcnt(0) (expcnt, lgkmcnt left at their maxima), as a builtin so
+// the compiler knows every earlier vector-memory load has completed.
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(2): everything but the two most recent vector-memory ops
+// (the L2 prefetches, which nobody waits for) has completed.
+__device__ __forceinline__ void wait_vm_but_prefetch() { __builtin_amdgcn_s_waitcnt(0x0F72); }
+
+// L2 prefetch: one dword per lane (one 128-byte line per row) dropped into a
+// scratch LDS area that is never read.  LDS-DMA has no register destination,
+// so nothing in the kernel can race with the late arrival.
+__device__ __forceinline__ void prefetch_lines(const lds_u8* scratch, uint32_t voffset, u32x4 rsrc) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)scratch);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(m0), "v"(voffset), "s"(rsrc)
+               : "memory");
+}
+
+constexpr uint32_t OOB = 0x80000000u;  // an offset past every tile buffer
+
+// 4 bytes per lane from the buffer at voffset into LDS at lds + 4 * lane
+// (buffer_load_dword ... lds), waited for like dma16.
+__device__ __forceinline__ void dma4(const lds_u8* lds, uint32_t voffset, u32x4 rsrc) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(m0), "v"(voffset), "s"(rsrc)
+               : "memory");
+}
+
+// The 16 MFMAs of one 64-K half (S = 0, 1) of a K step for a wave's 128x128
+// sub-tile: B fragments are the first operand, A fragments the second, and
+// op_sel S picks byte S of each lane's scale word.
+template <int S>
+__device__ __forceinline__ void mma_tile(const v8i* af, const v8i* bf, const uint32_t* sar,
+                                         const uint32_t* sbr, v16f (&acc)[4][4]) {
+#pragma unroll
+  for (int fn = 0; fn < 4; fn++)
+#pragma unroll
+    for (int fm = 0; fm < 4; fm++)
+      acc[fn][fm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          bf[fn], af[fm], acc[fn][fm], 0, 0, S, (int)sbr[fn], S, (int)sar[fm]);
+}
+
+// Ask the scheduler for MFMA, LDS read, vector load, MFMA, ... so the MFMA
+// pipe always has queued work while the loads are in flight.
+template <int NDS, int NVM>
+__device__ __forceinline__ void interleave_ops() {
+  constexpr int ds_per = (NDS + 15) / 16, vm_per = (NVM + 15) / 16;
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
+    if (ds_per) __builtin_amdgcn_sched_group_barrier(0x100, ds_per, 0);  // DS read
+    if (vm_per) __builtin_amdgcn_sched_group_barrier(0x020, vm_per, 0);  // VMEM read
+  }
+}
+
+// Epilogue of a 256x256 tile: FP32 -> BF16 (RNE) into C (row stride ldc).
+// A lane holds four consecutive n of its row per group r4 (n = 8 r4 + 4 g +
+// 0..3); one v_permlane32_swap per dword pair trades groups between lanes l
+// and l + 32, after which lane half g holds the 8 consecutive n at 8 g + 16 h
+// for h = 0, 1 and stores them as one 16-byte write.  The swaps run on every
+// lane before any lane drops out at the M edge.
+__device__ __forceinline__ void store_tile_bf16(const v16f (&acc)[4][4], uint16_t* __restrict__ c,
+                                                int64_t ldc, int64_t m0, int64_t m_end, int64_t n0,
+                                                int64_t N, int wm, int wn, int lane) {
+  const int g = lane >> 5, i = lane & 31;
+  const bool vec_ok = (ldc & 7) == 0;
+#pragma unroll
+  for (int fn = 0; fn < 4; fn++) {
+#pragma unroll
+    for (int fm = 0; fm < 4; fm++) {
+      const v16f& v = acc[fn][fm];
+      uint32_t p[4][2];
+#pragma unroll
+      for (int r4 = 0; r4 < 4; r4++) {
+        p[r4][0] = cvt_pk_bf16(v[4 * r4 + 0], v[4 * r4 + 1]);
+        p[r4][1] = cvt_pk_bf16(v[4 * r4 + 2], v[4 * r4 + 3]);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; h++)
+#pragma unroll
+        for (int d = 0; d < 2; d++) {
+          const auto s = __builtin_amdgcn_permlane32_swap(p[2 * h][d], p[2 * h + 1][d], false, false);
+          p[2 * h][d] = s[0];
+          p[2 * h + 1][d] = s[1];
+        }
+      const int64_t m = m0 + 128 * wm + 32 * fm + i;
+      if (m >= m_end) continue;
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+        const int64_t n = n0 + 128 * wn + 32 * fn + 16 * h + 8 * g;
+        const uint32_t w[4] = {p[2 * h][0], p[2 * h][1], p[2 * h + 1][0], p[2 * h + 1][1]};
+        uint16_t* dst = c + m * ldc + n;
+        if (vec_ok && n + 8 <= N) {
+          *(uint4*)dst = make_uint4(w[0], w[1], w[2], w[3]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; e++)
+            if (n + e < N) dst[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+        }
+      }
+    }
+  }
+}
+
+// Linear workgroup id -> a contiguous run of tiles per XCD (workgroups are
+// dealt to the 8 XCDs round-robin), then grouped M-major order inside the
+// run so neighbouring tiles share A rows and B rows in that XCD's L2.
+__device__ __forceinline__ void tile_of(int64_t bid, int64_t nm, int64_t nn, int64_t& mt,
+                                        int64_t& nt) {
+  const int64_t total = nm * nn;
+  const int64_t x = bid & 7, local = bid >> 3;
+  const int64_t per = total >> 3, rem = total & 7;
+  const int64_t t = x * per + (x < rem ? x : rem) + local;
+  constexpr int64_t GM = GM_TILES;
+  const int64_t group = t / (GM * nn);
+  const int64_t first = group * GM;
+  const int64_t gsz = (nm - first) < GM ? (nm - first) : GM;
+  const int64_t in = t % (GM * nn);
+  mt = first + in % gsz;
+  nt = in / gsz;
+}
+
+}  // namespace mx

@@ -8,9 +8,16 @@ namespace mx {
 // 1x32 quantisation of a flat BF16 array of n elements (n % 32 == 0).
 hipError_t launch_quant_row(const void* x, int64_t n, void* q, void* s, hipStream_t stream);
 
-// mode 1 = column (q_t, s_t), 2 = dual (q, s, q_t, s_t), 3 = 32x32 tiles (q, s).
+// mode 1 = column (q_t, s_t), 2 = dual (q, s, q_t, s_t), 3 = 32x32 tiles (q, s);
+// `batch` contiguous [R, C] matrices with contiguous outputs (grid.z).
 hipError_t launch_quant_tile(int mode, const void* x, int64_t R, int64_t C, void* q, void* s,
-                             void* qt, void* st, hipStream_t stream);
+                             void* qt, void* st, int64_t batch, hipStream_t stream);
+
+// Column blocks restarting at every group offset along the token axis of
+// x [T, C]; q_t [C, cap], s_t [C, cap/32] with cap = 128 (T / 128 + G).
+hipError_t launch_quant_grouped_col(const void* x, int64_t T, int64_t C, int64_t G,
+                                    const int64_t* offsets, int64_t cap, void* qt, void* st,
+                                    hipStream_t stream);
 
 // B operand layouts of the GEMM.
 enum GemmB {
@@ -25,6 +32,12 @@ hipError_t launch_gemm(int bmode, int64_t M, int64_t N, int64_t K, const void* a
 hipError_t launch_grouped_gemm(int64_t G, const int64_t* offsets, int64_t T, int64_t N, int64_t K,
                                const void* a, const void* sa, const void* b, const void* sb,
                                void* c, int num_cus, hipStream_t stream);
+
+// Per-expert weight gradient c[g] [M, N] over group g's token columns of
+// a [M, cap] and b [N, cap] (grouped column layout above).
+hipError_t launch_grouped_wgrad(int64_t G, const int64_t* offsets, int64_t T, int64_t M, int64_t N,
+                                int64_t cap, const void* a, const void* sa, const void* b,
+                                const void* sb, void* c, hipStream_t stream);
 
 hipError_t launch_fill_zero_bf16(void* c, int64_t n, hipStream_t stream);
 

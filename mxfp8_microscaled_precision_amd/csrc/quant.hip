@@ -10,6 +10,13 @@
 // step-2 environment table, MXFP8_DUAL_AXIS_FORWARD; RFC section 3.3.3).  The
 // 32x32 variant shares one scale per 32x32 tile (RFC sections 1.1, 3.1).
 //
+// The MoE backward needs column blocks along the token axis of every expert
+// group: blocks restart at each group offset and the last block of a group
+// holds only its remaining rows (MindSpeed RFC section 2.2: grouped-matmul
+// quantisation of gate_up_proj / down_proj).  The grouped column mode writes
+// group g's columns from P_g = 128 (o_g / 128 + g) on and fills every column
+// that holds no token with zero blocks.
+//
 // All kernels are bound by HBM bandwidth: x is read once with 16-byte loads,
 // every output byte is written once.
 #include "mx_device.h"
@@ -75,7 +82,7 @@ constexpr int TILE_THREADS = 512;
 constexpr int TILE_ROWS = 128;
 constexpr int TILE_COLS = 128;
 
-enum TileMode { TILE_COL = 1, TILE_DUAL = 2, TILE_BLOCK32 = 3 };
+enum TileMode { TILE_COL = 1, TILE_DUAL = 2, TILE_BLOCK32 = 3, TILE_GCOL = 4 };
 
 typedef __attribute__((address_space(3))) uint8_t lds8;
 
@@ -83,23 +90,83 @@ typedef __attribute__((address_space(3))) uint8_t lds8;
 __device__ __forceinline__ int row_chunk(int r, int k) { return k ^ ((r >> 2) & 7); }
 __device__ __forceinline__ int col_chunk(int c, int k) { return k ^ ((c >> 3) & 7); }
 
+// Grouped column mode: the wave's 32 output rows r0 .. r0+31 (a block of
+// the padded token axis) -> first source row and number of real rows.  The
+// group is the last g with P_g <= r0, found by counting (one ballot per 64
+// groups, all offsets loaded at once); offsets are clamped into [0, T], so
+// bad offsets give wrong blocks but only rows inside [0, T) are read.
+constexpr int GCOL_MAX_GROUPS = 512;
+
+__device__ __forceinline__ void gcol_block(const int64_t* __restrict__ offsets, int64_t G,
+                                           int64_t T, int64_t r0, int lane, int64_t& src,
+                                           int& nreal) {
+  int64_t o[GCOL_MAX_GROUPS / 64];
+#pragma unroll
+  for (int k = 0; k < GCOL_MAX_GROUPS / 64; k++) {
+    const int64_t gg = 64 * k + lane;
+    o[k] = gg < G ? offsets[gg] : T;
+  }
+  int cnt = 0;
+#pragma unroll
+  for (int k = 0; k < GCOL_MAX_GROUPS / 64; k++) {
+    const int64_t gg = 64 * k + lane;
+    const int64_t oc = o[k] < 0 ? 0 : (o[k] > T ? T : o[k]);
+    cnt += __popcll(__ballot(gg < G && 128 * (oc / 128 + gg) <= r0));
+  }
+  src = 0;
+  nreal = 0;
+  if (cnt == 0) return;
+  const int64_t g = cnt - 1;
+  int64_t lo = offsets[g], hi = offsets[g + 1];
+  lo = lo < 0 ? 0 : (lo > T ? T : lo);
+  hi = hi < lo ? lo : (hi > T ? T : hi);
+  const int64_t first = 128 * (lo / 128 + g);
+  if (r0 < first) return;                       // only with decreasing offsets
+  const int64_t j = (r0 - first) >> 5;          // block of the group's range
+  const int64_t left = (hi - lo) - 32 * j;
+  src = lo + 32 * j;
+  nreal = left <= 0 ? 0 : (left >= 32 ? 32 : (int)left);
+}
+
+// grid.z indexes a batch of equally shaped matrices (contiguous inputs and
+// outputs); the grouped column mode uses G, offsets and T (x has T rows, R is
+// the padded capacity).
 template <int MODE>
 __global__ void __launch_bounds__(TILE_THREADS)
 quant_tile_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C, uint8_t* __restrict__ q,
-                  uint8_t* __restrict__ s, uint8_t* __restrict__ qt, uint8_t* __restrict__ st) {
+                  uint8_t* __restrict__ s, uint8_t* __restrict__ qt, uint8_t* __restrict__ st,
+                  int64_t G, const int64_t* __restrict__ offsets, int64_t T) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 3, h = lane & 7;
   const int wr = wave >> 1, wc = wave & 1;
   const int64_t R0 = (int64_t)blockIdx.x * TILE_ROWS, C0 = (int64_t)blockIdx.y * TILE_COLS;
   const int64_t r0 = R0 + 32 * wr;
   const int64_t c = C0 + 64 * wc + 8 * h;
+  if (blockIdx.z) {
+    const int64_t z = blockIdx.z, n = R * C;
+    x += z * n;
+    q += q ? z * n : 0;
+    s += s ? (MODE == TILE_BLOCK32 ? z * (n >> 10) : z * (n >> 5)) : 0;
+    qt += qt ? z * n : 0;
+    st += st ? z * (n >> 5) : 0;
+  }
   // R, C are multiples of 32: a wave's 32 rows are all in or all out, and
   // whole quads of columns are in or out
   const bool live = r0 < R && c < C;
   uint4 v[4];
+  int nreal = 32;  // grouped column mode: rows 0 .. nreal-1 of the block are tokens
+  if (MODE == TILE_GCOL) {
+    int64_t src = 0;
+    if (r0 < R) gcol_block(offsets, G, T, r0, lane, src, nreal);
 #pragma unroll
-  for (int i = 0; i < 4; i++)
-    v[i] = live ? load_stream16(x + (r0 + 4 * g + i) * C + c) : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < 4; i++)
+      v[i] = (live && 4 * g + i < nreal) ? load_stream16(x + (src + 4 * g + i) * C + c)
+                                         : make_uint4(0, 0, 0, 0);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+      v[i] = live ? load_stream16(x + (r0 + 4 * g + i) * C + c) : make_uint4(0, 0, 0, 0);
+  }
 
   if (MODE == TILE_BLOCK32) {
     if (r0 >= R) return;  // no barrier below
@@ -155,6 +222,9 @@ quant_tile_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C, uint8_t*
     cm[k] = pk_max(cm[k], (uint32_t)__shfl_xor((int)cm[k], 32, 64));
   }
   uint32_t sbc[8];
+  // byte i of a column word is row 4g + i
+  const uint32_t realmask = (4 * g + 0 < nreal ? 0x000000FFu : 0u) | (4 * g + 1 < nreal ? 0x0000FF00u : 0u) |
+                            (4 * g + 2 < nreal ? 0x00FF0000u : 0u) | (4 * g + 3 < nreal ? 0xFF000000u : 0u);
 #pragma unroll
   for (int k = 0; k < 4; k++) {
     sbc[2 * k] = scale_byte(cm[k] & 0xFFFFu);
@@ -169,7 +239,8 @@ quant_tile_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C, uint8_t*
     const int k = j >> 1;
     const uint32_t p01 = (j & 1) ? pair_hi(w0[k], w1[k]) : pair_lo(w0[k], w1[k]);
     const uint32_t p23 = (j & 1) ? pair_hi(w2[k], w3[k]) : pair_lo(w2[k], w3[k]);
-    const uint32_t out = sbc[j] == 0xFFu ? 0x7F7F7F7Fu : cvt4(p01, p23, cvt_scale(sbc[j]));
+    uint32_t out = sbc[j] == 0xFFu ? 0x7F7F7F7Fu : cvt4(p01, p23, cvt_scale(sbc[j]));
+    if (MODE == TILE_GCOL) out &= realmask;  // rows that hold no token stay 0x00
     const int cc = cl + j;  // local column; 4 rows rl .. rl+3 of it
     *(__attribute__((address_space(3))) uint32_t*)(LQT + cc * 128 + col_chunk(cc, rl >> 4) * 16 +
                                                     (rl & 15)) = out;
@@ -237,25 +308,40 @@ hipError_t launch_quant_row(const void* x, int64_t n, void* q, void* s, hipStrea
 }
 
 hipError_t launch_quant_tile(int mode, const void* x, int64_t R, int64_t C, void* q, void* s,
-                             void* qt, void* st, hipStream_t stream) {
-  dim3 grid((unsigned)((R + TILE_ROWS - 1) / TILE_ROWS), (unsigned)((C + TILE_COLS - 1) / TILE_COLS));
+                             void* qt, void* st, int64_t batch, hipStream_t stream) {
+  dim3 grid((unsigned)((R + TILE_ROWS - 1) / TILE_ROWS), (unsigned)((C + TILE_COLS - 1) / TILE_COLS),
+            (unsigned)batch);
   const uint16_t* xx = (const uint16_t*)x;
   switch (mode) {
     case TILE_COL:
       hipLaunchKernelGGL(quant_tile_kernel<TILE_COL>, grid, dim3(TILE_THREADS), 0, stream, xx, R, C,
-                         (uint8_t*)q, (uint8_t*)s, (uint8_t*)qt, (uint8_t*)st);
+                         (uint8_t*)q, (uint8_t*)s, (uint8_t*)qt, (uint8_t*)st, (int64_t)0,
+                         (const int64_t*)nullptr, (int64_t)0);
       break;
     case TILE_DUAL:
       hipLaunchKernelGGL(quant_tile_kernel<TILE_DUAL>, grid, dim3(TILE_THREADS), 0, stream, xx, R, C,
-                         (uint8_t*)q, (uint8_t*)s, (uint8_t*)qt, (uint8_t*)st);
+                         (uint8_t*)q, (uint8_t*)s, (uint8_t*)qt, (uint8_t*)st, (int64_t)0,
+                         (const int64_t*)nullptr, (int64_t)0);
       break;
     case TILE_BLOCK32:
       hipLaunchKernelGGL(quant_tile_kernel<TILE_BLOCK32>, grid, dim3(TILE_THREADS), 0, stream, xx, R,
-                         C, (uint8_t*)q, (uint8_t*)s, (uint8_t*)qt, (uint8_t*)st);
+                         C, (uint8_t*)q, (uint8_t*)s, (uint8_t*)qt, (uint8_t*)st, (int64_t)0,
+                         (const int64_t*)nullptr, (int64_t)0);
       break;
     default:
       return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_grouped_col(const void* x, int64_t T, int64_t C, int64_t G,
+                                    const int64_t* offsets, int64_t cap, void* qt, void* st,
+                                    hipStream_t stream) {
+  if (G < 1 || G > GCOL_MAX_GROUPS) return hipErrorInvalidValue;
+  dim3 grid((unsigned)((cap + TILE_ROWS - 1) / TILE_ROWS), (unsigned)((C + TILE_COLS - 1) / TILE_COLS));
+  hipLaunchKernelGGL(quant_tile_kernel<TILE_GCOL>, grid, dim3(TILE_THREADS), 0, stream,
+                     (const uint16_t*)x, cap, C, (uint8_t*)nullptr, (uint8_t*)nullptr, (uint8_t*)qt,
+                     (uint8_t*)st, G, offsets, T);
   return hipGetLastError();
 }
 

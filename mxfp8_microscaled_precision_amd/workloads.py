@@ -150,6 +150,18 @@ def moe(device="cpu", scale: int = 1, fscale: int = 1, experts: int = 64):
     }
 
 
+def moe_grads(device="cpu", scale: int = 1, fscale: int = 1):
+    """Output gradients of the MoE expert GEMMs for the backward pass: dY of
+    gate_up [T, 2F] and of down [T, H], N(0, 0.01) like the linear stack's
+    gradients (the MoE workload itself gives no backward tensors)."""
+    T = 131072 // scale
+    H, F = 4096 // fscale, 2048 // fscale
+    return {
+        "dY_gu": normal_bf16((T, 2 * F), 0.01, seed_of(4, 4), device),
+        "dY_dn": normal_bf16((T, H), 0.01, seed_of(4, 5), device),
+    }
+
+
 def stack_layer(layer: int, device="cpu", scale: int = 1, fscale: int = 1):
     T = 32768 // scale
     H, F = 7168 // fscale, 18432 // fscale

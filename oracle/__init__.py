@@ -197,17 +197,17 @@ def quant_col_batched(x):
 
 
 def grouped_col_capacity(T: int, G: int) -> int:
-    """Columns of the per-group column-quantised output (reading R9)."""
+    """Columns of the per-group column-quantised output (reading R20)."""
     return int(lib().orc_grouped_col_capacity(int(T), int(G)))
 
 
 def group_col(g: int, o_g: int) -> int:
-    """First column of group g (reading R9): 128 * (o_g // 128 + g)."""
+    """First column of group g (reading R20): 128 * (o_g // 128 + g)."""
     return 128 * (int(o_g) // 128 + int(g))
 
 
 def quant_col_grouped(x, offsets):
-    """MoE backward column blocks restarting at each group offset (R9).
+    """MoE backward column blocks restarting at each group offset (R20).
 
     x [T,C] BF16 bits, offsets int64 [G+1] -> (q_t [C,cap] u8, s_t [C,cap/32] u8)
     with cap = grouped_col_capacity(T, G)."""
@@ -282,7 +282,7 @@ def grouped_gemm(offsets, a, sa, b, sb, want_bound: bool = True):
 
 
 def grouped_gemm_wgrad(offsets, a, sa, b, sb, want_bound: bool = True):
-    """Per-expert weight gradient over each group's tokens (R9 layout).
+    """Per-expert weight gradient over each group's tokens (R20 layout).
 
     offsets int64 [G+1] with offsets[G] = T; a [M,cap] u8 + sa [M,cap/32];
     b [N,cap] u8 + sb [N,cap/32]; returns ref/bound [G,M,N]."""

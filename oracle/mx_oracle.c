@@ -40,7 +40,7 @@
  *   R7  column-axis output is written transposed: q_t[c][r], s_t[c][r/32].
  *   R8  the 32x32 forward and backward scales are two views of one tile
  *       array s[R/32][C/32].
- *   R9  MoE backward, per-group column blocks: along the token axis, blocks
+ *   R20 MoE backward, per-group column blocks: along the token axis, blocks
  *       of 32 restart at every group offset and a group's last block holds
  *       only its remaining rows; its amax covers those rows alone.  The
  *       transposed output gives group g the column range starting at
@@ -339,7 +339,7 @@ int orc_grouped_gemm(int64_t G, const int64_t *offsets, int64_t T, int64_t N, in
 /* MoE backward                                                              */
 /* ------------------------------------------------------------------------ */
 
-/* First column of group g (R9). */
+/* First column of group g (R20). */
 static int64_t group_col(int64_t g, int64_t o_g)
 {
     return 128 * (o_g / 128 + g);
@@ -360,7 +360,7 @@ static int offsets_ok(int64_t G, const int64_t *offsets, int64_t T)
     return 1;
 }
 
-/* Column blocks per group (R9): x is BF16 [T][C]; q_t[C][cap] and
+/* Column blocks per group (R20): x is BF16 [T][C]; q_t[C][cap] and
  * s_t[C][cap / 32] with cap = orc_grouped_col_capacity(T, G).  The last block
  * of a group is quantised from its remaining rows only.  Returns 0, or -1 on
  * bad offsets or C % 32 != 0. */
@@ -396,7 +396,7 @@ int orc_quant_col_grouped(const uint16_t *x, int64_t T, int64_t C, int64_t G,
  *   ref[g][m][n] = sum over the group's tokens t of A[m][t] * B[n][t]
  * where A = a [M][cap] (scales [M][cap/32]) and B = b [N][cap] are the
  * per-group column-quantised copies of (for MoE) the output gradient and the
- * expert input, token t of group g sitting at column P_g + (t - o_g) (R9).
+ * expert input, token t of group g sitting at column P_g + (t - o_g) (R20).
  * An empty group gives ref = bound = 0.  ref/bound are [G][M][N]. */
 int orc_grouped_gemm_wgrad(int64_t G, const int64_t *offsets, int64_t T, int64_t M, int64_t N,
                            const uint8_t *a, const uint8_t *sa, const uint8_t *b,

@@ -110,3 +110,55 @@ def test_process_quant_result_rejects_unknown_recipe():
 def test_quant_rejects_unknown_mode_name():
     with pytest.raises(ValueError):
         mx.quant(None, "1x64")
+
+
+@pytest.mark.parametrize("args,status", [
+    ((7, 1, 2, 32, 32, 1, 1, 0, 0, 0), INVALID),       # unknown mode
+    ((1, 1, -1, 32, 32, 0, 0, 1, 1, 0), INVALID),      # negative batch
+    ((1, 1, 70000, 32, 32, 0, 0, 1, 1, 0), INVALID),   # batch beyond the grid
+    ((1, 1, 2, 33, 32, 0, 0, 1, 1, 0), SHAPE),         # column blocks need rows % 32
+    ((0, 1, 2, 4, 40, 1, 1, 0, 0, 0), SHAPE),          # row blocks need cols % 32
+    ((2, 1, 2, 32, 32, 1, 1, 0, 1, 0), INVALID),       # NULL q_t for dual
+])
+def test_quant_batched_validation(args, status):
+    assert mx.mx_quant_batched(*args) == status
+
+
+def test_quant_batched_empty_is_noop():
+    assert mx.mx_quant_batched(2, 0, 0, 32, 32, 0, 0, 0, 0, 0) == 0
+
+
+@pytest.mark.parametrize("T,G,cap", [(0, 1, 128), (100, 3, 384), (131072, 64, 139264),
+                                     (127, 1, 128), (128, 1, 256), (-1, 1, -1), (5, 0, -1)])
+def test_grouped_col_capacity(T, G, cap):
+    """128 * (T // 128 + G): every group's column range starts on a multiple
+    of 128 (the oracle's layout reading for the per-group column blocks)."""
+    assert mx.mx_grouped_col_capacity(T, G) == cap
+
+
+@pytest.mark.parametrize("args,status", [
+    ((1, 64, 32, 0, 1, 1, 1, 0), INVALID),             # G = 0
+    ((1, 64, 32, 513, 1, 1, 1, 0), INVALID),           # G too large
+    ((1, 64, 40, 2, 1, 1, 1, 0), SHAPE),               # C % 32
+    ((1, -1, 32, 2, 1, 1, 1, 0), INVALID),             # negative T
+    ((1, 64, 32, 2, 0, 1, 1, 0), INVALID),             # NULL offsets
+    ((0, 64, 32, 2, 1, 1, 1, 0), INVALID),             # NULL x with tokens
+    ((1, 1 << 31, 32, 2, 1, 1, 1, 0), SHAPE),          # capacity beyond 32-bit tile offsets
+])
+def test_quant_grouped_col_validation(args, status):
+    assert mx.mx_quant_grouped_col(*args) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 1, 64, 32, 32, 1, 1, 1, 1, 1, 0), INVALID),   # G = 0
+    ((2, 1, -1, 32, 32, 1, 1, 1, 1, 1, 0), INVALID),   # negative T
+    ((2, 0, 64, 32, 32, 1, 1, 1, 1, 1, 0), INVALID),   # NULL offsets
+    ((2, 1, 64, 32, 32, 1, 1, 1, 1, 0, 0), INVALID),   # NULL c
+    ((2, 1, 1 << 31, 32, 32, 1, 1, 1, 1, 1, 0), SHAPE),
+])
+def test_grouped_wgrad_validation(args, status):
+    assert mx.mx_grouped_gemm_wgrad(*args) == status
+
+
+def test_grouped_wgrad_empty_is_noop():
+    assert mx.mx_grouped_gemm_wgrad(2, 1, 64, 0, 32, 0, 0, 0, 0, 0, 0) == 0

@@ -1,0 +1,200 @@
+"""GPU parity of the MoE backward pieces against the oracle: batched
+quantisation of per-expert weights (bytes exact), per-group column
+quantisation along the token axis (bytes exact, ragged and empty groups,
+partial last blocks, whole MoE workload on sampled features) and the
+per-expert weight-gradient GEMM (every element within the GEMM tolerance;
+empty experts give zeros; equal to the dense GEMM over each expert's padded
+column range; the full MoE workload on sampled experts and elements)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import mxfp8_microscaled_precision_amd as mx
+from mxfp8_microscaled_precision_amd import workloads as W
+from parity import assert_bytes, assert_gemm, bits, dev, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _offsets(sizes):
+    o = np.zeros(len(sizes) + 1, np.int64)
+    np.cumsum(sizes, out=o[1:])
+    return o
+
+
+@pytest.mark.parametrize("mode", ["row", "col", "dual", "32x32"])
+def test_quant_batched_equals_per_matrix(mode):
+    B, R, C = 3, 96, 160
+    say(f"[moe-bwd] quant_batched {mode} [{B},{R},{C}]")
+    x = W.normal_with_outliers_bf16((B * R, C), 0.02, 0.01, 100.0, 77).reshape(B, R, C)
+    got = mx.quant_batched(x.cuda(), mode)
+    torch.cuda.synchronize()
+    for i in range(B):
+        want = {"row": oracle.quant_row, "col": oracle.quant_col, "dual": oracle.quant_dual,
+                "32x32": oracle.quant_block32}[mode](bits(x[i]))
+        for k, (g, w) in enumerate(zip(got, want)):
+            assert_bytes(g[i], w, f"batched {mode} matrix {i} output {k}")
+
+
+@pytest.mark.parametrize("sizes,C", [
+    ([5, 0, 33, 1, 31, 32, 64, 0, 70], 64),
+    ([0, 0, 7], 32),
+    ([300, 0, 0, 257, 1, 511, 96], 160),     # C not a multiple of the 128-column tile
+    ([128, 256, 129], 96),
+    ([0], 32),                               # no tokens at all: all zero blocks
+])
+def test_quant_grouped_col_exact(sizes, C):
+    off = _offsets(sizes)
+    T = int(off[-1])
+    say(f"[moe-bwd] grouped col sizes={sizes} C={C}")
+    x = W.normal_with_outliers_bf16((max(T, 1), C), 1.0, 0.01, 100.0, T + C)[:T]
+    q, s = mx.quant_grouped_col(x.cuda(), dev(off))
+    torch.cuda.synchronize()
+    wq, ws = oracle.quant_col_grouped(bits(x) if T else np.zeros((0, C), np.uint16), off)
+    assert_bytes(q, wq, "grouped q_t")
+    assert_bytes(s, ws, "grouped s_t")
+
+
+def test_quant_grouped_col_special_values():
+    """NaN / Inf blocks, zeros and subnormals in ragged groups: the oracle's
+    bytes exactly (a NaN block's padding rows stay 0x00)."""
+    sizes = [3, 40, 0, 29]
+    off = _offsets(sizes)
+    T, C = int(off[-1]), 64
+    rng = np.random.default_rng(4)
+    xb = W.bf16_bits(W.normal_bf16((T, C), 1.0, 5))
+    xb[1, 3] = 0x7FC0           # NaN in group 0
+    xb[20, 7] = 0x7F80          # +Inf in group 1
+    xb[44:46, :] = 0x0001       # subnormals in group 1's partial block
+    xb[50:, 10] = 0x8000        # -0 column piece in group 3
+    xb[rng.integers(0, T, 20), rng.integers(0, C, 20)] = 0
+    q, s = mx.quant_grouped_col(W.bits_to_bf16(xb, "cuda"), dev(off))
+    torch.cuda.synchronize()
+    wq, ws = oracle.quant_col_grouped(xb, off)
+    assert_bytes(q, wq, "special q_t")
+    assert_bytes(s, ws, "special s_t")
+
+
+def test_quant_grouped_col_full_moe_sampled_features():
+    """The MoE tokens [131072, 4096] over 64 Zipf-sized experts: every token
+    of 48 sampled features against the oracle (features are independent)."""
+    d = W.moe("cuda")
+    off = d["offsets"]
+    x = d["X"]
+    say(f"[moe-bwd] grouped col full X {tuple(x.shape)}")
+    q, s = mx.quant_grouped_col(x, dev(off))
+    torch.cuda.synchronize()
+    C = x.shape[1]
+    cols = np.unique(np.concatenate([[0, C - 1], np.random.default_rng(8).choice(
+        np.arange(1, C - 1), 62, replace=False)]))          # 64 features (a multiple of 32)
+    ci = torch.from_numpy(cols).cuda()
+    wq, ws = oracle.quant_col_grouped(bits(x.index_select(1, ci)), off)
+    assert_bytes(q.index_select(0, ci), wq, "full grouped q_t rows")
+    assert_bytes(s.index_select(0, ci), ws, "full grouped s_t rows")
+    del q, s
+
+
+def _wgrad_case(sizes, M, N, seed):
+    off = _offsets(sizes)
+    T = int(off[-1])
+    dy = W.normal_bf16((T, M), 0.01, seed)
+    xx = W.normal_bf16((T, N), 1.0, seed + 1)
+    qa, sa = oracle.quant_col_grouped(bits(dy), off)
+    qb, sb = oracle.quant_col_grouped(bits(xx), off)
+    c = mx.grouped_gemm_wgrad(dev(off), T, dev(qa), dev(sa), dev(qb), dev(sb))
+    torch.cuda.synchronize()
+    return off, T, qa, sa, qb, sb, c
+
+
+@pytest.mark.parametrize("sizes,M,N", [
+    ([5, 0, 33, 64, 1], 64, 96),
+    ([300, 0, 0, 257, 1, 511, 96], 288, 160),   # M, N not multiples of the 256 tile
+    ([0, 0], 64, 64),                            # all experts empty
+    ([1000], 256, 512),
+    ([130, 128, 129, 127], 256, 256),            # odd and even step counts
+])
+def test_wgrad_small_cases(sizes, M, N):
+    say(f"[moe-bwd] wgrad sizes={sizes} M={M} N={N}")
+    off, T, qa, sa, qb, sb, c = _wgrad_case(sizes, M, N, sum(sizes) + M + N)
+    ref, bound = oracle.grouped_gemm_wgrad(off, qa, sa, qb, sb)
+    assert_gemm(c, ref, bound, f"wgrad sizes={sizes}")
+    for g, m in enumerate(sizes):
+        if m == 0:
+            assert torch.count_nonzero(c[g]) == 0, g
+
+
+def test_wgrad_equals_dense_gemm_per_expert():
+    """Each expert's gradient equals the dense GEMM over its padded column
+    range (same K-step order, so the same bits)."""
+    sizes = [200, 0, 384, 45]
+    M, N = 160, 192
+    off, T, qa, sa, qb, sb, c = _wgrad_case(sizes, M, N, 31)
+    for g, m in enumerate(sizes):
+        if m == 0:
+            continue
+        P = oracle.group_col(g, off[g])
+        Kg = 128 * ((m + 127) // 128)
+        dense = mx.gemm(dev(qa[:, P:P + Kg]), dev(sa[:, P // 32:(P + Kg) // 32]),
+                        dev(qb[:, P:P + Kg]), dev(sb[:, P // 32:(P + Kg) // 32]), "wgrad")
+        torch.cuda.synchronize()
+        assert torch.equal(c[g], dense), g
+
+
+def test_moe_backward_full_sampled():
+    """The whole MoE backward at the workload's size: gate_up and down,
+    dgrad through the batched column quantisation of the expert weights and
+    the grouped GEMM, wgrad through the per-group column quantisation and the
+    grouped weight-gradient GEMM; sampled rows / experts / elements against
+    the oracle quantising the same BF16 sources."""
+    d = W.moe("cuda")
+    gr = W.moe_grads("cuda")
+    off = d["offsets"]
+    offd = dev(off)
+    T = int(off[-1])
+    sizes = np.diff(off)
+    rng = np.random.default_rng(61)
+    nonempty = [g for g in range(len(sizes)) if sizes[g] > 0]
+    big, small = int(np.argmax(sizes)), int(min(nonempty, key=lambda g: sizes[g]))
+    empty = [g for g in range(len(sizes)) if sizes[g] == 0]
+    for name, xname, wname, dyname in (("gate_up", "X", "W_gu", "dY_gu"), ("down", "H", "W_dn", "dY_dn")):
+        x, w, dy = d[xname], d[wname], gr[dyname]
+        G, Nout, Kin = w.shape
+        say(f"[moe-bwd] full {name}: T={T} G={G} out={Nout} in={Kin}")
+        # dgrad: dX = dY W_g per expert
+        qd, sd = mx.quant(dy, "row")
+        qwt, swt = mx.quant_batched(w, "col")                 # [G, Kin, Nout]
+        dx = mx.grouped_gemm(offd, qd, sd, qwt, swt)
+        torch.cuda.synchronize()
+        rows = np.unique(np.concatenate([[off[g] for g in nonempty], [off[g + 1] - 1 for g in nonempty],
+                                         rng.integers(0, T, 16)])).astype(np.int64)
+        cols = np.unique(np.concatenate([[0, Kin - 1], rng.integers(0, Kin, 30)])).astype(np.int64)
+        ri, ci = torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()
+        got = dx.index_select(0, ri).index_select(1, ci).float().cpu().numpy().astype(np.float64)
+        ra, rsa = oracle.quant_row(bits(dy.index_select(0, ri)))
+        grp = np.searchsorted(off, rows, side="right") - 1
+        for g in np.unique(grp):
+            sel = np.nonzero(grp == g)[0]
+            wt, swt_o = oracle.quant_col(bits(w[int(g)].index_select(1, ci)))   # [cols, Nout]
+            ref, bound = oracle.gemm(ra[sel], rsa[sel], wt, swt_o)
+            assert_gemm(got[sel], ref, bound, f"{name} dgrad expert {g}")
+        del dx, qd, sd, qwt, swt
+        # wgrad: dW_g = dY_g^T X_g per expert
+        qa, sa = mx.quant_grouped_col(dy, offd)
+        qb, sb = mx.quant_grouped_col(x, offd)
+        dw = mx.grouped_gemm_wgrad(offd, T, qa, sa, qb, sb)
+        torch.cuda.synchronize()
+        # 32 sampled features on each side (the oracle's column blocks need
+        # a multiple of 32 columns)
+        mi = np.unique(np.concatenate([[0, Nout - 1], rng.choice(np.arange(1, Nout - 1), 30,
+                                                                 replace=False)])).astype(np.int64)
+        ni = np.unique(np.concatenate([[0, Kin - 1], rng.choice(np.arange(1, Kin - 1), 30,
+                                                                replace=False)])).astype(np.int64)
+        mt, nt = torch.from_numpy(mi).cuda(), torch.from_numpy(ni).cuda()
+        oa, osa = oracle.quant_col_grouped(bits(dy.index_select(1, mt)), off)
+        ob, osb = oracle.quant_col_grouped(bits(x.index_select(1, nt)), off)
+        ref, bound = oracle.grouped_gemm_wgrad(off, oa, osa, ob, osb)
+        for g in sorted({big, small, *empty[:1], *rng.integers(0, G, 3).tolist()}):
+            got = dw[g].index_select(0, mt).index_select(1, nt)
+            assert_gemm(got, ref[g], bound[g], f"{name} wgrad expert {g} ({sizes[g]} tokens)")
+        del dw, qa, sa, qb, sb
