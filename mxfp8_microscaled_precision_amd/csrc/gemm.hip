@@ -52,6 +52,7 @@ struct Tile {
 
   u32x4 ra, rb, rsa, rsb;
   uint32_t svoff;               // scale-tile load offset of this lane's row
+  uint32_t svoff_b, sb_row;     // the same for B's scales; bytes per block index
   // L2 prefetch (B_ROW with LDS_SCALES): the first workgroup of each
   // concurrently running group to need a K slice fetches it PF_DIST steps
   // ahead of use; pf_a / pf_b are 0 for the operands this workgroup
@@ -95,9 +96,29 @@ struct Tile {
       // scale tiles: wave w loads rows 64w .. 64w+63, one 16-byte chunk
       // (four K steps) per lane; rows past the edge read as zero
       rsa = make_rsrc(sa + m0 * lda, mrows * lda);
-      const int64_t nrows = (N - n0) < BN ? (N - n0) : BN;
-      rsb = make_rsrc(sb + n0 * lda, nrows * lda);
       svoff = (uint32_t)((64 * wave + lane) * lda);
+      if (BMODE == GEMM_B_ROW) {
+        const int64_t nrows = (N - n0) < BN ? (N - n0) : BN;
+        rsb = make_rsrc(sb + n0 * lda, nrows * lda);
+        svoff_b = svoff;
+        sb_row = 1;
+      } else if (BMODE == GEMM_B_TILE) {
+        // the tile's 8 rows of tile scales, 16 bytes (four K steps) each,
+        // loaded by lanes 0..7 of wave 0
+        const int64_t tr0 = n0 >> 5, ntr = ((N - n0) >> 5) < 8 ? ((N - n0) >> 5) : 8;
+        rsb = make_rsrc(sb + tr0 * lda, ntr * lda);
+        svoff_b = lane < 8 ? (uint32_t)(lane * lda) : OOB;
+        sb_row = 1;
+      } else {
+        // transposed weight: tile-scale rows kb (along K) hold the tile
+        // columns of N; a 4-step group needs 16 rows x the tile's 8 columns
+        // (two dwords), loaded by lanes 0..31 of wave 0.  Columns past N
+        // feed only outputs that are never stored.
+        const int64_t c0t = n0 >> 5, ldt = N >> 5;
+        rsb = make_rsrc(sb + c0t, (nkb - 1) * ldt + (ldt - c0t));
+        svoff_b = lane < 32 ? (uint32_t)((lane >> 1) * ldt + 4 * (lane & 1)) : OOB;
+        sb_row = (uint32_t)ldt;
+      }
     }
     pf_row = (uint32_t)((64 * wave + lane) * K);
 #pragma unroll
@@ -241,10 +262,22 @@ struct Tile {
 
   // LDS_SCALES: scale-tile loads of the 4-step group whose first block is
   // kb0, and the per-step reads (two blocks per lane: 2g and 2g+1 of step q).
+  // The scale tile holds A's rows at [0, 4 KB) and B's scales at [4 KB, ...):
+  // per-row words like A's for B_ROW, [8 tile rows][16 B] for B_TILE,
+  // [16 block rows][8 B] for B_TILE_T.  The tile-scale loads are issued by
+  // wave 0 only (one destination for the whole workgroup); the barrier
+  // after wave 0's own vmcnt wait publishes them.
   __device__ __forceinline__ void dma_scales(lds_u8* buf, int64_t kb0, int wave) {
-    const uint32_t off = kb0 < nkb ? svoff + (uint32_t)kb0 : OOB;  // none past the end
-    dma16(buf + wave * 1024, off, rsa);
-    if (BMODE == GEMM_B_ROW) dma16(buf + 4096 + wave * 1024, off, rsb);
+    const bool live = kb0 < nkb;  // none past the end
+    dma16(buf + wave * 1024, live ? svoff + (uint32_t)kb0 : OOB, rsa);
+    const uint32_t offb = live ? svoff_b + (uint32_t)kb0 * sb_row : OOB;
+    if (BMODE == GEMM_B_ROW)
+      dma16(buf + 4096 + wave * 1024, offb, rsb);
+    else if (BMODE == GEMM_B_TILE) {
+      if (wave == 0) dma16(buf + 4096, offb, rsb);
+    } else {
+      if (wave == 0) dma4(buf + 4096, offb, rsb);
+    }
   }
 
   __device__ __forceinline__ void read_scales(const lds_u8* buf, int q, int wm, int wn, int lane,
@@ -257,6 +290,17 @@ struct Tile {
 #pragma unroll
       for (int f = 0; f < 4; f++)
         sbr[f] = *(const lds_u16*)(buf + 4096 + (128 * wn + 32 * f + i) * 16 + 4 * q + 2 * g);
+    } else {
+      // one word per fragment (B_TILE: the tile row's four blocks of step q)
+      // or per block (B_TILE_T: the wave's four tile columns of block 4q+i),
+      // the same for every lane; finish_scales_b shapes them per lane
+      uint32_t w[4];
+#pragma unroll
+      for (int f = 0; f < 4; f++)
+        w[f] = BMODE == GEMM_B_TILE
+                   ? *(const __attribute__((address_space(3))) uint32_t*)(buf + 4096 + (4 * wn + f) * 16 + 4 * q)
+                   : *(const __attribute__((address_space(3))) uint32_t*)(buf + 4096 + (4 * q + f) * 8 + 4 * wn);
+      finish_scales_b(lane, w, sbr);
     }
   }
 
@@ -334,27 +378,20 @@ struct Tile {
   // One K step with LDS-staged scales; U = kt % 4.  `sread` holds the scale
   // tile of step kt+1; at U == 0 the tile of the next group is loaded into
   // `sdma` (its previous contents were last read two barriers earlier).
+  // Every mode waits with vmcnt(2): the two most recent vector-memory ops of
+  // every step are its L2 prefetches, which nothing waits for.
   template <int U>
   __device__ __forceinline__ void step_ls(lds_u8* cur, lds_u8* nxt, const lds_u8* sread,
                                           lds_u8* sdma, int64_t kt, int wave, int wm, int wn,
                                           int lane, uint32_t* sc_a, uint32_t* sc_b,
                                           uint32_t* nx_a, uint32_t* nx_b, v8i* f0a, v8i* f0b,
                                           v8i* f1a, v8i* f1b, v16f (&acc)[4][4]) {
-    constexpr bool GB = BMODE != GEMM_B_ROW;  // B scales from global memory
     // phase A
-    if (GB) load_scales_b((kt + 1) * (BK / 32), nx_b);
     read_frags<1>(cur, wm, wn, lane, f1a, f1b);
     mma<0>(f0a, f0b, sc_a, sc_b, acc);
-    interleave<DS_READS, GB ? 4 : 0>();
-    if (GB)
-      wait_vm_all();
-    else
-      wait_vm_but_prefetch();
+    interleave<DS_READS, 0>();
+    wait_vm_but_prefetch();
     __syncthreads();
-    if (GB) {
-#pragma unroll
-      for (int f = 0; f < 4; f++) asm volatile("" : "+v"(nx_b[f]));
-    }
     // phase B
     if (U == 0) dma_scales(sdma, (kt + 4) * (BK / 32), wave);
     read_scales(sread, (U + 1) & 3, wm, wn, lane, nx_a, nx_b);
@@ -376,22 +413,23 @@ struct Tile {
       dma_b(cur, k2, bb, 2 * f, wave, lane);
       dma_b(cur, k2, bb, 2 * f + 1, wave, lane);
     }
-    if (!GB) {
-      const int64_t kp = (kt + PF_DIST) * BK;
-      const uint32_t live = kp < K ? 0u : OOB;
-      prefetch_lines(pf_scratch + wave * 512, (pf_row + (uint32_t)kp) | pf_a | live, ra);
-      prefetch_lines(pf_scratch + wave * 512 + 256, (pf_row + (uint32_t)kp) | pf_b | live, rb);
-    }
+    prefetch(kt + PF_DIST, wave);
     mma<1>(f1a, f1b, sc_a, sc_b, acc);
-    interleave<DS_READS + (GB ? 4 : 8), 0>();
+    interleave<DS_READS + 8, 0>();
 #pragma unroll
-    for (int f = 0; f < 4; f++) sc_a[f] = nx_a[f];
-    if (GB)
-      finish_scales_b(lane, nx_b, sc_b);
-    else {
-#pragma unroll
-      for (int f = 0; f < 4; f++) sc_b[f] = nx_b[f];
+    for (int f = 0; f < 4; f++) {
+      sc_a[f] = nx_a[f];
+      sc_b[f] = nx_b[f];
     }
+  }
+
+  // L2 prefetch of K step kt (pf_a / pf_b select the workgroups that issue
+  // it; steps past the end touch no memory)
+  __device__ __forceinline__ void prefetch(int64_t kt, int wave) {
+    const int64_t kp = kt * BK;
+    const uint32_t live = kp < K ? 0u : OOB;
+    prefetch_lines(pf_scratch + wave * 512, (pf_row + (uint32_t)kp) | pf_a | live, ra);
+    prefetch_lines(pf_scratch + wave * 512 + 256, (pf_row + (uint32_t)kp) | pf_b | live, rb);
   }
 
   __device__ __forceinline__ void run() {
@@ -412,20 +450,14 @@ struct Tile {
       // nk is a multiple of 4
       issue_stage(st0, 0, wave, lane);
       dma_scales(ss0, 0, wave);
-      if (BMODE != GEMM_B_ROW) load_scales_b(0, nx_b);
       wait_vm_all();
       __syncthreads();
       read_scales(ss0, 0, wm, wn, lane, sc_a, sc_b);
-      if (BMODE != GEMM_B_ROW) finish_scales_b(lane, nx_b, sc_b);
       issue_stage(st1, BK, wave, lane);
-      if (BMODE == GEMM_B_ROW) {
-        // The steps wait with vmcnt(2), which leaves the two most recent
-        // loads in flight: those must be prefetches, never stage loads.  So
-        // the prologue ends with the two prefetches of stage 2.
-        const uint32_t kp = 2 * BK;
-        prefetch_lines(pf_scratch + wave * 512, (pf_row + kp) | pf_a, ra);
-        prefetch_lines(pf_scratch + wave * 512 + 256, (pf_row + kp) | pf_b, rb);
-      }
+      // The steps wait with vmcnt(2), which leaves the two most recent loads
+      // in flight: those must be prefetches, never stage loads.  So the
+      // prologue ends with the two prefetches of stage 2.
+      prefetch(2, wave);
       read_frags<0>(st0, wm, wn, lane, f0a, f0b);
       for (int64_t j = 0; 4 * j < nk; j++) {
         const int64_t kt = 4 * j;
@@ -496,7 +528,8 @@ gemm_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa,
   // at multiples of GM
   t.pf_scratch = (lds_u8*)spf;
   t.pf_a = (nt % (32 / GM_TILES) == 0) ? 0u : OOB;
-  t.pf_b = (mt % GM_TILES == 0) ? 0u : OOB;
+  // (the transposed weight is [K][N]: the row pattern does not apply to it)
+  t.pf_b = (mt % GM_TILES == 0 && BMODE != GEMM_B_TILE_T) ? 0u : OOB;
   t.run();
 }
 

@@ -53,7 +53,8 @@ def test_row_scales_all_layouts(M, N, K, layout):
     _run(qa, sa, qb, sb, layout, "1x32", oracle.BKIND_ROW, f"{layout} {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("M,N,K", [(64, 64, 64), (300, 224, 160), (257, 544, 1056), (512, 256, 4096)])
+@pytest.mark.parametrize("M,N,K", [(64, 64, 64), (300, 224, 160), (257, 544, 1056), (512, 256, 4096),
+                                   (384, 384, 2048), (640, 896, 1536)])
 def test_block32_weight_fprop_and_dgrad(M, N, K):
     # fprop: Y[M, out=N] = X[M, in=K] W[out=N, in=K]^T with W in 32x32 tiles
     qx, sx = oracle.quant_row(bits(W.normal_bf16((M, K), 1.0, M + K)))
