@@ -31,6 +31,10 @@ BKIND_ROW = 0        # B [N][K], scales [N][K/32]
 BKIND_TILE = 1       # B [N][K], 32x32 tile scales [N/32][K/32]
 BKIND_TILE_T = 2     # B [K][N] contracted over rows, tile scales [K/32][N/32]
 
+ELEM_E4M3 = 0        # payload element types
+ELEM_E5M2 = 1
+ELEMS = {"e4m3": ELEM_E4M3, "e5m2": ELEM_E5M2}
+
 
 def build(force: bool = True) -> str:
     """Compile mx_oracle.c into liboracle.so (always, when force)."""
@@ -59,6 +63,22 @@ def lib():
         L.orc_e8m0_value.argtypes = [ctypes.c_uint8]
         L.orc_e4m3_round.restype = ctypes.c_uint8
         L.orc_e4m3_round.argtypes = [ctypes.c_double]
+        L.orc_e5m2_value.restype = ctypes.c_double
+        L.orc_e5m2_value.argtypes = [ctypes.c_uint8]
+        L.orc_e5m2_round.restype = ctypes.c_uint8
+        L.orc_e5m2_round.argtypes = [ctypes.c_double]
+        L.orc_rceil_exponent_e5m2.restype = ctypes.c_int
+        L.orc_rceil_exponent_e5m2.argtypes = [ctypes.c_double]
+        for name in ("orc_quant_row_elem", "orc_quant_col_elem", "orc_quant_block32_elem"):
+            f = getattr(L, name)
+            f.restype = None
+            f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                          ctypes.c_void_p, ctypes.c_void_p]
+        L.orc_gemm_elem.restype = ctypes.c_int
+        L.orc_gemm_elem.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+                                    ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_void_p]
         L.orc_rceil_exponent.restype = ctypes.c_int
         L.orc_rceil_exponent.argtypes = [ctypes.c_double]
         for name in ("orc_quant_row", "orc_quant_col", "orc_quant_block32"):
@@ -125,6 +145,24 @@ def rceil_exponent(amax: float) -> int:
     return int(lib().orc_rceil_exponent(float(amax)))
 
 
+def e5m2_value(code: int) -> float:
+    return lib().orc_e5m2_value(int(code))
+
+
+def e5m2_round(v: float) -> int:
+    return int(lib().orc_e5m2_round(float(v)))
+
+
+def rceil_exponent_e5m2(amax: float) -> int:
+    return int(lib().orc_rceil_exponent_e5m2(float(amax)))
+
+
+def e5m2_decode_table() -> np.ndarray:
+    """binary64 value of each of the 256 E5M2 codes (+-inf, NaN included)."""
+    f = lib().orc_e5m2_value
+    return np.array([f(c) for c in range(256)], dtype=np.float64)
+
+
 def e4m3_round_array(v) -> np.ndarray:
     v = np.asarray(v, dtype=np.float64).ravel()
     f = lib().orc_e4m3_round
@@ -154,7 +192,15 @@ def _bits(x) -> np.ndarray:
     return x
 
 
-def quant_row(x):
+def _elem(elem) -> int:
+    if isinstance(elem, str):
+        elem = ELEMS[elem]
+    if elem not in (ELEM_E4M3, ELEM_E5M2):
+        raise ValueError(f"unknown element type {elem!r}")
+    return int(elem)
+
+
+def quant_row(x, elem=ELEM_E4M3):
     """1x32 quantisation along rows: returns (q [R,C] u8, s [R,C/32] u8)."""
     x = _bits(x)
     R, C = x.shape
@@ -162,11 +208,11 @@ def quant_row(x):
         raise ValueError("cols must be a multiple of 32")
     q = np.empty((R, C), np.uint8)
     s = np.empty((R, C // 32), np.uint8)
-    lib().orc_quant_row(_ptr(x), R, C, _ptr(q), _ptr(s))
+    lib().orc_quant_row_elem(_ptr(x), R, C, _elem(elem), _ptr(q), _ptr(s))
     return q, s
 
 
-def quant_col(x):
+def quant_col(x, elem=ELEM_E4M3):
     """32x1 quantisation down columns, written transposed:
     returns (q_t [C,R] u8, s_t [C,R/32] u8)."""
     x = _bits(x)
@@ -175,14 +221,14 @@ def quant_col(x):
         raise ValueError("rows must be a multiple of 32")
     q = np.empty((C, R), np.uint8)
     s = np.empty((C, R // 32), np.uint8)
-    lib().orc_quant_col(_ptr(x), R, C, _ptr(q), _ptr(s))
+    lib().orc_quant_col_elem(_ptr(x), R, C, _elem(elem), _ptr(q), _ptr(s))
     return q, s
 
 
-def quant_dual(x):
+def quant_dual(x, elem=ELEM_E4M3):
     """Dual-axis: (q, s, q_t, s_t) = quant_row(x) + quant_col(x)."""
-    q, s = quant_row(x)
-    qt, st = quant_col(x)
+    q, s = quant_row(x, elem)
+    qt, st = quant_col(x, elem)
     return q, s, qt, st
 
 
@@ -224,7 +270,7 @@ def quant_col_grouped(x, offsets):
     return q, s
 
 
-def quant_block32(x):
+def quant_block32(x, elem=ELEM_E4M3):
     """32x32 tiles: returns (q [R,C] u8, s [R/32,C/32] u8)."""
     x = _bits(x)
     R, C = x.shape
@@ -232,16 +278,18 @@ def quant_block32(x):
         raise ValueError("rows and cols must be multiples of 32")
     q = np.empty((R, C), np.uint8)
     s = np.empty((R // 32, C // 32), np.uint8)
-    lib().orc_quant_block32(_ptr(x), R, C, _ptr(q), _ptr(s))
+    lib().orc_quant_block32_elem(_ptr(x), R, C, _elem(elem), _ptr(q), _ptr(s))
     return q, s
 
 
 # --- GEMM ---------------------------------------------------------------------
 
-def gemm(a, sa, b, sb, bkind: int = BKIND_ROW, want_bound: bool = True):
+def gemm(a, sa, b, sb, bkind: int = BKIND_ROW, want_bound: bool = True, a_elem=ELEM_E4M3,
+         b_elem=ELEM_E4M3):
     """binary64 reference C = A * B^T of the dequantised operands.
 
-    a [M,K] u8 + sa [M,K/32]; b/sb as described by ``bkind``.
+    a [M,K] u8 + sa [M,K/32]; b/sb as described by ``bkind``; a_elem / b_elem
+    the payload element types.
     Returns (ref [M,N] f64, bound [M,N] f64 or None) where bound = sum_k |a*b|.
     """
     a = _c(a, np.uint8)
@@ -252,8 +300,9 @@ def gemm(a, sa, b, sb, bkind: int = BKIND_ROW, want_bound: bool = True):
     N = b.shape[1] if bkind == BKIND_TILE_T else b.shape[0]
     ref = np.empty((M, N), np.float64)
     bound = np.empty((M, N), np.float64) if want_bound else None
-    rc = lib().orc_gemm(bkind, M, N, K, _ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(ref),
-                        _ptr(bound) if bound is not None else None)
+    rc = lib().orc_gemm_elem(bkind, _elem(a_elem), _elem(b_elem), M, N, K, _ptr(a), _ptr(sa),
+                             _ptr(b), _ptr(sb), _ptr(ref),
+                             _ptr(bound) if bound is not None else None)
     if rc:
         raise ValueError(f"oracle gemm rejected the shapes (rc={rc})")
     return ref, bound

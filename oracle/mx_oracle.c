@@ -40,6 +40,12 @@
  *   R7  column-axis output is written transposed: q_t[c][r], s_t[c][r/32].
  *   R8  the 32x32 forward and backward scales are two views of one tile
  *       array s[R/32][C/32].
+ *   R22 E5M2 payload (an allowed element type besides E4M3): the scale
+ *       keeps the rceil rule with E5M2's largest finite value, the smallest
+ *       e with amax <= 57344 * 2^e; elements round to nearest-even E5M2
+ *       (OCP "E5M2": bias 15, 0x7C = infinity, 0x7D..0x7F = NaN), saturating
+ *       at +-57344 (unreachable for finite blocks); a NaN/Inf block gets
+ *       scale 0xFF and payload 0x7F (an E5M2 NaN) as in R3.
  *   R20 MoE backward, per-group column blocks: along the token axis, blocks
  *       of 32 restart at every group offset and a group's last block holds
  *       only its remaining rows; its amax covers those rows alone.  The
@@ -100,6 +106,23 @@ double orc_e4m3_value(uint8_t code)
     return s ? -mag : mag;
 }
 
+/* OCP E5M2: S.EEEEE.MM, bias 15.  E=0 is subnormal (2^-14 * M/4); E=31 is
+ * infinity (M=0) or NaN (M!=0).  Largest finite value 0x7B = 57344. */
+double orc_e5m2_value(uint8_t code)
+{
+    int s = code >> 7;
+    int E = (code >> 2) & 0x1F;
+    int M = code & 0x3;
+    double mag;
+    if (E == 31)
+        mag = M ? NAN : INFINITY;
+    else if (E == 0)
+        mag = ldexp(M / 4.0, -14);
+    else
+        mag = ldexp(1.0 + M / 4.0, E - 15);
+    return s ? -mag : mag;
+}
+
 /* E8M0: unsigned exponent, value 2^(b-127); 0xFF is NaN. */
 double orc_e8m0_value(uint8_t b)
 {
@@ -141,32 +164,86 @@ uint8_t orc_e4m3_round(double v)
     return sign | (uint8_t)((E << 3) | M);
 }
 
-/* rceil: the smallest integer e with amax <= 448 * 2^e, i.e. the ceiling of
- * log2(amax / 448), clamped to [-127, 127] (R1, R2). */
-int orc_rceil_exponent(double amax)
+/* Round a binary64 value to E5M2 (R22): nearest representable value, ties
+ * to the even mantissa, saturating to +-57344, NaN -> 0x7F, sign of zero
+ * kept.  Grid spacing 2^-16 below 2^-14 (subnormals), 2^(floor(log2|v|) - 2)
+ * above. */
+uint8_t orc_e5m2_round(double v)
+{
+    if (isnan(v))
+        return 0x7F;
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    double a = fabs(v);
+    if (a >= 57344.0)
+        return sign | 0x7B;
+    int p;
+    if (a < 0x1p-14) {
+        p = -16;
+    } else {
+        int ex;
+        frexp(a, &ex);
+        p = (ex - 1) - 2;       /* two fraction bits below the leading one */
+    }
+    double k = nearbyint(ldexp(a, -p));
+    double r = ldexp(k, p);
+    if (r == 0.0)
+        return sign;
+    if (r < 0x1p-14) /* subnormal code: r = M * 2^-16 */
+        return sign | (uint8_t)ldexp(r, 16);
+    int ex;
+    double f = frexp(r, &ex);
+    int E = (ex - 1) + 15;
+    int M = (int)((2.0 * f - 1.0) * 4.0);
+    return sign | (uint8_t)((E << 2) | M);
+}
+
+/* The smallest integer e with amax <= emax_value * 2^e, i.e. the ceiling of
+ * log2(amax / emax_value), clamped to [-127, 127] (R1, R2). */
+static int rceil_for(double amax, double emax_value)
 {
     if (amax == 0.0)
         return -127;
-    int e = (int)ceil(log2(amax / 448.0));
+    int e = (int)ceil(log2(amax / emax_value));
     if (e < -127)
         e = -127;
     if (e > 127)
         e = 127;
     /* make the log2 estimate exactly the definition */
-    while (e > -127 && amax <= ldexp(448.0, e - 1))
+    while (e > -127 && amax <= ldexp(emax_value, e - 1))
         e--;
-    while (e < 127 && amax > ldexp(448.0, e))
+    while (e < 127 && amax > ldexp(emax_value, e))
         e++;
     return e;
+}
+
+/* rceil: the smallest integer e with amax <= 448 * 2^e, i.e. the ceiling of
+ * log2(amax / 448), clamped to [-127, 127] (R1, R2). */
+int orc_rceil_exponent(double amax)
+{
+    return rceil_for(amax, 448.0);
+}
+
+/* The same rule for E5M2 elements (R22): amax <= 57344 * 2^e. */
+int orc_rceil_exponent_e5m2(double amax)
+{
+    return rceil_for(amax, 57344.0);
+}
+
+/* Element types of the payload. */
+enum { ELEM_E4M3 = 0, ELEM_E5M2 = 1 };
+
+static double elem_value(int elem, uint8_t code)
+{
+    return elem == ELEM_E5M2 ? orc_e5m2_value(code) : orc_e4m3_value(code);
 }
 
 /* ------------------------------------------------------------------------ */
 /* One MX block                                                              */
 /* ------------------------------------------------------------------------ */
 
-/* Quantise n values (already decoded to binary64) sharing one scale.
- * Writes n codes and returns the scale byte. */
-static uint8_t quant_block(int n, const double *v, uint8_t *codes)
+/* Quantise n values (already decoded to binary64) sharing one scale into
+ * payload elements of type elem.  Writes n codes, returns the scale byte. */
+static uint8_t quant_block_elem(int elem, int n, const double *v, uint8_t *codes)
 {
     for (int i = 0; i < n; i++) {
         if (!isfinite(v[i])) { /* R3 */
@@ -179,10 +256,18 @@ static uint8_t quant_block(int n, const double *v, uint8_t *codes)
     for (int i = 0; i < n; i++)
         if (fabs(v[i]) > amax)
             amax = fabs(v[i]);
-    int e = orc_rceil_exponent(amax);
-    for (int i = 0; i < n; i++)
-        codes[i] = orc_e4m3_round(ldexp(v[i], -e)); /* exact power-of-two scaling */
+    int e = elem == ELEM_E5M2 ? orc_rceil_exponent_e5m2(amax) : orc_rceil_exponent(amax);
+    for (int i = 0; i < n; i++) {
+        double w = ldexp(v[i], -e); /* exact power-of-two scaling */
+        codes[i] = elem == ELEM_E5M2 ? orc_e5m2_round(w) : orc_e4m3_round(w);
+    }
     return (uint8_t)(e + 127);
+}
+
+/* E4M3 (the default element type). */
+static uint8_t quant_block(int n, const double *v, uint8_t *codes)
+{
+    return quant_block_elem(ELEM_E4M3, n, v, codes);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -190,8 +275,8 @@ static uint8_t quant_block(int n, const double *v, uint8_t *codes)
 /* ------------------------------------------------------------------------ */
 
 /* 1x32 along the row (the contraction axis of a TN GEMM):
- * q[R][C], s[R][C/32].  Requires C % 32 == 0. */
-void orc_quant_row(const uint16_t *x, int64_t R, int64_t C, uint8_t *q, uint8_t *s)
+ * q[R][C], s[R][C/32].  Requires C % 32 == 0.  elem: payload type. */
+void orc_quant_row_elem(const uint16_t *x, int64_t R, int64_t C, int elem, uint8_t *q, uint8_t *s)
 {
     int64_t nb = C / 32;
 #pragma omp parallel for schedule(static)
@@ -200,14 +285,15 @@ void orc_quant_row(const uint16_t *x, int64_t R, int64_t C, uint8_t *q, uint8_t 
         for (int64_t j = 0; j < nb; j++) {
             for (int i = 0; i < 32; i++)
                 v[i] = orc_bf16_value(x[r * C + 32 * j + i]);
-            s[r * nb + j] = quant_block(32, v, q + r * C + 32 * j);
+            s[r * nb + j] = quant_block_elem(elem, 32, v, q + r * C + 32 * j);
         }
     }
 }
 
 /* 32x1 along the column (blocks of 32 consecutive rows of one column),
  * written transposed (R7): q_t[C][R], s_t[C][R/32].  Requires R % 32 == 0. */
-void orc_quant_col(const uint16_t *x, int64_t R, int64_t C, uint8_t *q_t, uint8_t *s_t)
+void orc_quant_col_elem(const uint16_t *x, int64_t R, int64_t C, int elem, uint8_t *q_t,
+                        uint8_t *s_t)
 {
     int64_t nb = R / 32;
 #pragma omp parallel for schedule(static)
@@ -216,14 +302,15 @@ void orc_quant_col(const uint16_t *x, int64_t R, int64_t C, uint8_t *q_t, uint8_
         for (int64_t i = 0; i < nb; i++) {
             for (int k = 0; k < 32; k++)
                 v[k] = orc_bf16_value(x[(32 * i + k) * C + c]);
-            s_t[c * nb + i] = quant_block(32, v, q_t + c * R + 32 * i);
+            s_t[c * nb + i] = quant_block_elem(elem, 32, v, q_t + c * R + 32 * i);
         }
     }
 }
 
 /* 32x32 tiles (RFC block size [1,32,32]): one scale per tile, payload in the
  * original layout: q[R][C], s[R/32][C/32] (R8).  Requires R, C % 32 == 0. */
-void orc_quant_block32(const uint16_t *x, int64_t R, int64_t C, uint8_t *q, uint8_t *s)
+void orc_quant_block32_elem(const uint16_t *x, int64_t R, int64_t C, int elem, uint8_t *q,
+                            uint8_t *s)
 {
     int64_t tr = R / 32, tc = C / 32;
 #pragma omp parallel for schedule(static)
@@ -234,10 +321,25 @@ void orc_quant_block32(const uint16_t *x, int64_t R, int64_t C, uint8_t *q, uint
         for (int a = 0; a < 32; a++)
             for (int b = 0; b < 32; b++)
                 v[32 * a + b] = orc_bf16_value(x[(32 * i + a) * C + 32 * j + b]);
-        s[i * tc + j] = quant_block(1024, v, codes);
+        s[i * tc + j] = quant_block_elem(elem, 1024, v, codes);
         for (int a = 0; a < 32; a++)
             memcpy(q + (32 * i + a) * C + 32 * j, codes + 32 * a, 32);
     }
+}
+
+void orc_quant_row(const uint16_t *x, int64_t R, int64_t C, uint8_t *q, uint8_t *s)
+{
+    orc_quant_row_elem(x, R, C, ELEM_E4M3, q, s);
+}
+
+void orc_quant_col(const uint16_t *x, int64_t R, int64_t C, uint8_t *q_t, uint8_t *s_t)
+{
+    orc_quant_col_elem(x, R, C, ELEM_E4M3, q_t, s_t);
+}
+
+void orc_quant_block32(const uint16_t *x, int64_t R, int64_t C, uint8_t *q, uint8_t *s)
+{
+    orc_quant_block32_elem(x, R, C, ELEM_E4M3, q, s);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -249,25 +351,25 @@ void orc_quant_block32(const uint16_t *x, int64_t R, int64_t C, uint8_t *q, uint
  *   1  B bytes [N][K], tile scales [N/32][K/32]   (32x32 weight, forward)
  *   2  B bytes [K][N], tile scales [K/32][N/32]   (the same 32x32 weight
  *      stored [out=K][in=N], contracted over its rows: backward data) */
-static double b_value(int bkind, int64_t N, int64_t K, const uint8_t *b, const uint8_t *sb,
-                      int64_t n, int64_t k)
+static double b_value(int bkind, int elem, int64_t N, int64_t K, const uint8_t *b,
+                      const uint8_t *sb, int64_t n, int64_t k)
 {
     switch (bkind) {
     case 0:
-        return orc_e4m3_value(b[n * K + k]) * orc_e8m0_value(sb[n * (K / 32) + k / 32]);
+        return elem_value(elem, b[n * K + k]) * orc_e8m0_value(sb[n * (K / 32) + k / 32]);
     case 1:
-        return orc_e4m3_value(b[n * K + k]) * orc_e8m0_value(sb[(n / 32) * (K / 32) + k / 32]);
+        return elem_value(elem, b[n * K + k]) * orc_e8m0_value(sb[(n / 32) * (K / 32) + k / 32]);
     default:
-        return orc_e4m3_value(b[k * N + n]) * orc_e8m0_value(sb[(k / 32) * (N / 32) + n / 32]);
+        return elem_value(elem, b[k * N + n]) * orc_e8m0_value(sb[(k / 32) * (N / 32) + n / 32]);
     }
 }
 
 /* ref[M][N] = sum_k a*b in binary64 and bound[M][N] = sum_k |a*b| (the
  * tolerance scale).  a: bytes [M][K] with scales [M][K/32].  Either output
  * pointer may be NULL.  Returns 0, or -1 on a shape the layout forbids. */
-int orc_gemm(int bkind, int64_t M, int64_t N, int64_t K,
-             const uint8_t *a, const uint8_t *sa, const uint8_t *b, const uint8_t *sb,
-             double *ref, double *bound)
+int orc_gemm_elem(int bkind, int a_elem, int b_elem, int64_t M, int64_t N, int64_t K,
+                  const uint8_t *a, const uint8_t *sa, const uint8_t *b, const uint8_t *sb,
+                  double *ref, double *bound)
 {
     if (K % 32 != 0 || M < 0 || N < 0)
         return -1;
@@ -282,14 +384,14 @@ int orc_gemm(int bkind, int64_t M, int64_t N, int64_t K,
 #pragma omp parallel for schedule(static)
     for (int64_t n = 0; n < N; n++)
         for (int64_t k = 0; k < K; k++)
-            bt[n * K + k] = b_value(bkind, N, K, b, sb, n, k);
+            bt[n * K + k] = b_value(bkind, b_elem, N, K, b, sb, n, k);
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t m = 0; m < M; m++) {
         double *av = (double *)malloc((size_t)(K ? K : 1) * sizeof(double));
         if (!av)
             abort();
         for (int64_t k = 0; k < K; k++)
-            av[k] = orc_e4m3_value(a[m * K + k]) * orc_e8m0_value(sa[m * (K / 32) + k / 32]);
+            av[k] = elem_value(a_elem, a[m * K + k]) * orc_e8m0_value(sa[m * (K / 32) + k / 32]);
         for (int64_t n = 0; n < N; n++) {
             const double *bv = bt + n * K;
             double acc = 0.0, mag = 0.0;
@@ -307,6 +409,14 @@ int orc_gemm(int bkind, int64_t M, int64_t N, int64_t K,
     }
     free(bt);
     return 0;
+}
+
+/* E4M3 operands. */
+int orc_gemm(int bkind, int64_t M, int64_t N, int64_t K,
+             const uint8_t *a, const uint8_t *sa, const uint8_t *b, const uint8_t *sb,
+             double *ref, double *bound)
+{
+    return orc_gemm_elem(bkind, ELEM_E4M3, ELEM_E4M3, M, N, K, a, sa, b, sb, ref, bound);
 }
 
 /* Grouped GEMM for MoE experts: rows offsets[g] .. offsets[g+1]-1 of the
