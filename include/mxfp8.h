@@ -59,6 +59,16 @@ typedef enum mx_quant_mode {
     MX_QUANT_BLOCK_32x32 = 3 /* one scale per 32x32 tile */
 } mx_quant_mode;
 
+/* Payload element type.  E4M3 is the pages' element type for every tensor
+ * (RFC section 3.3.1); E5M2 is the other FP8 dst_type the RFC's recipe
+ * accepts (section 3.5.2.3).  OCP E5M2: bias 15, largest finite 57344,
+ * 0x7C infinity, 0x7D..0x7F NaN.  With E5M2 the scale keeps the rceil rule
+ * against 57344: the smallest e with amax <= 57344 * 2^e. */
+typedef enum mx_elem_type {
+    MX_ELEM_E4M3 = 0,
+    MX_ELEM_E5M2 = 1
+} mx_elem_type;
+
 /* Which product of a linear layer a GEMM call computes (operand roles). */
 typedef enum mx_gemm_layout {
     MX_GEMM_FPROP = 0, /* Y  = X  * W^T : a = X rows,     b = W rows            */
@@ -107,6 +117,13 @@ const char* mx_last_error(void);
 mx_status mx_quant(mx_quant_mode mode, const void* x, int64_t rows, int64_t cols, void* q, void* s,
                    void* q_t, void* s_t, hipStream_t stream);
 
+/* mx_quant with a choice of payload element type (E4M3 or E5M2); every
+ * other rule, layout and shape requirement is that of mx_quant, which is
+ * mx_quant_elem with MX_ELEM_E4M3.  A NaN/Inf block gets scale 0xFF and
+ * payload 0x7F in both types. */
+mx_status mx_quant_elem(mx_quant_mode mode, mx_elem_type elem, const void* x, int64_t rows,
+                        int64_t cols, void* q, void* s, void* q_t, void* s_t, hipStream_t stream);
+
 /* MXFP8 GEMM C = A * B^T with FP32 accumulation and a BF16 result.
  *   a:  E4M3 [M, K] row-major, sa: E8M0 [M, K/32]
  *   b/sb by (layout, bkind):
@@ -123,6 +140,13 @@ mx_status mx_quant(mx_quant_mode mode, const void* x, int64_t rows, int64_t cols
 mx_status mx_gemm(mx_gemm_layout layout, mx_bscale_kind bkind, int64_t M, int64_t N, int64_t K,
                   const void* a, const void* sa, const void* b, const void* sb, void* c,
                   hipStream_t stream);
+
+/* mx_gemm with the payload element type of each operand (E4M3 or E5M2, in
+ * any combination, e.g. E5M2 gradients against an E4M3 weight); layouts,
+ * scales and rules as mx_gemm, which is mx_gemm_elem with E4M3 operands. */
+mx_status mx_gemm_elem(mx_gemm_layout layout, mx_bscale_kind bkind, mx_elem_type a_elem,
+                       mx_elem_type b_elem, int64_t M, int64_t N, int64_t K, const void* a,
+                       const void* sa, const void* b, const void* sb, void* c, hipStream_t stream);
 
 /* MoE grouped MXFP8 GEMM over per-expert token groups (tutorial, "MXFP8 /
  * HiF8 architecture overview": MoE expert layers run as grouped matmul; RFC

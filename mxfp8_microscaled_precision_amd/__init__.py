@@ -17,7 +17,8 @@ import os
 
 __all__ = [
     "MXError", "lib", "mx_device_check", "mx_arch_supported", "mx_status_string",
-    "mx_last_error", "mx_quant", "mx_gemm", "mx_grouped_gemm", "mx_quant_batched",
+    "mx_last_error", "mx_quant", "mx_gemm", "mx_grouped_gemm", "mx_quant_elem", "mx_gemm_elem",
+    "mx_quant_batched",
     "mx_grouped_col_capacity", "mx_quant_grouped_col", "mx_grouped_gemm_wgrad", "quant", "gemm",
     "grouped_gemm", "quant_batched", "quant_grouped_col", "grouped_gemm_wgrad",
     "grouped_col_capacity", "process_quant_result", "QUANT_MODES", "GEMM_LAYOUTS",
@@ -30,6 +31,7 @@ MX_OK = 0
 QUANT_MODES = {"row": 0, "col": 1, "dual": 2, "32x32": 3}
 GEMM_LAYOUTS = {"fprop": 0, "dgrad": 1, "wgrad": 2}
 BSCALE_KINDS = {"1x32": 0, "32x32": 1}
+ELEM_TYPES = {"e4m3": 0, "e5m2": 1}
 
 
 class MXError(RuntimeError):
@@ -65,6 +67,10 @@ def lib() -> ctypes.CDLL:
         L.mx_gemm.argtypes = [c_int, c_int, i64, i64, i64, vp, vp, vp, vp, vp, vp]
         L.mx_grouped_gemm.restype = c_int
         L.mx_grouped_gemm.argtypes = [i64, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp]
+        L.mx_quant_elem.restype = c_int
+        L.mx_quant_elem.argtypes = [c_int, c_int, vp, i64, i64, vp, vp, vp, vp, vp]
+        L.mx_gemm_elem.restype = c_int
+        L.mx_gemm_elem.argtypes = [c_int, c_int, c_int, c_int, i64, i64, i64, vp, vp, vp, vp, vp, vp]
         L.mx_quant_batched.restype = c_int
         L.mx_quant_batched.argtypes = [c_int, vp, i64, i64, i64, vp, vp, vp, vp, vp]
         L.mx_grouped_col_capacity.restype = i64
@@ -107,6 +113,14 @@ def mx_gemm(layout, bkind, M, N, K, a, sa, b, sb, c, stream) -> int:
 
 def mx_grouped_gemm(G, offsets, T, N, K, a, sa, b, sb, c, stream) -> int:
     return lib().mx_grouped_gemm(G, offsets, T, N, K, a, sa, b, sb, c, stream)
+
+
+def mx_quant_elem(mode, elem, x, rows, cols, q, s, q_t, s_t, stream) -> int:
+    return lib().mx_quant_elem(mode, elem, x, rows, cols, q, s, q_t, s_t, stream)
+
+
+def mx_gemm_elem(layout, bkind, a_elem, b_elem, M, N, K, a, sa, b, sb, c, stream) -> int:
+    return lib().mx_gemm_elem(layout, bkind, a_elem, b_elem, M, N, K, a, sa, b, sb, c, stream)
 
 
 def mx_quant_batched(mode, x, batch, rows, cols, q, s, q_t, s_t, stream) -> int:
@@ -160,18 +174,21 @@ def _need(t, dtype, name, ndim=None):
         raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
 
 
-def quant(x, mode: str = "row"):
+def quant(x, mode: str = "row", elem: str = "e4m3"):
     """Dynamic MX quantisation of a BF16 [rows, cols] tensor.
 
     mode "row"   -> (q [rows,cols], s [rows,cols/32])
          "col"   -> (q_t [cols,rows], s_t [cols,rows/32])
          "dual"  -> (q, s, q_t, s_t)
          "32x32" -> (q [rows,cols], s [rows/32,cols/32])
-    Payloads are uint8 E4M3 bytes, scales uint8 E8M0 bytes.
+    Payloads are uint8 E4M3 (or, with elem="e5m2", E5M2) bytes, scales
+    uint8 E8M0 bytes.
     """
     torch = _torch()
     if mode not in QUANT_MODES:
         raise ValueError(f"unknown quantisation mode {mode!r}; expected one of {list(QUANT_MODES)}")
+    if elem not in ELEM_TYPES:
+        raise ValueError(f"unknown element type {elem!r}; expected one of {list(ELEM_TYPES)}")
     _need(x, torch.bfloat16, "x", 2)
     R, C = x.shape
     dev, u8 = x.device, torch.uint8
@@ -182,8 +199,8 @@ def quant(x, mode: str = "row"):
     if mode in ("col", "dual"):
         qt = torch.empty((C, R), dtype=u8, device=dev)
         st = torch.empty((C, R // 32), dtype=u8, device=dev)
-    _check(mx_quant(QUANT_MODES[mode], _ptr(x), R, C, _ptr(q), _ptr(s), _ptr(qt), _ptr(st),
-                    _stream(dev)))
+    _check(mx_quant_elem(QUANT_MODES[mode], ELEM_TYPES[elem], _ptr(x), R, C, _ptr(q), _ptr(s),
+                         _ptr(qt), _ptr(st), _stream(dev)))
     if mode == "row" or mode == "32x32":
         return q, s
     if mode == "col":
@@ -191,16 +208,20 @@ def quant(x, mode: str = "row"):
     return q, s, qt, st
 
 
-def gemm(a, sa, b, sb, layout: str = "fprop", bscale: str = "1x32", out=None):
+def gemm(a, sa, b, sb, layout: str = "fprop", bscale: str = "1x32", out=None,
+         a_elem: str = "e4m3", b_elem: str = "e4m3"):
     """MXFP8 GEMM C = A * B^T (FP32 accumulation, BF16 result).
 
     a [M,K] u8 + sa [M,K/32]; b [N,K] u8 + sb [N,K/32] for 1x32 scales;
     with bscale "32x32": fprop b [N,K] + tiles [N/32,K/32], dgrad b [K,N]
     (the shared weight, contracted over rows) + tiles [K/32,N/32].
+    a_elem / b_elem: payload element types ("e4m3" or "e5m2").
     """
     torch = _torch()
     if layout not in GEMM_LAYOUTS or bscale not in BSCALE_KINDS:
         raise ValueError(f"unknown layout {layout!r} or B scale kind {bscale!r}")
+    if a_elem not in ELEM_TYPES or b_elem not in ELEM_TYPES:
+        raise ValueError(f"unknown element types {a_elem!r}, {b_elem!r}")
     for t, n in ((a, "a"), (sa, "sa"), (b, "b"), (sb, "sb")):
         _need(t, torch.uint8, n, 2)
     M, K = a.shape
@@ -210,8 +231,9 @@ def gemm(a, sa, b, sb, layout: str = "fprop", bscale: str = "1x32", out=None):
     _need(out, torch.bfloat16, "out", 2)
     if tuple(out.shape) != (M, N):
         raise ValueError(f"out must be [{M}, {N}]")
-    _check(mx_gemm(GEMM_LAYOUTS[layout], BSCALE_KINDS[bscale], M, N, K, _ptr(a), _ptr(sa), _ptr(b),
-                   _ptr(sb), _ptr(out), _stream(a.device)))
+    _check(mx_gemm_elem(GEMM_LAYOUTS[layout], BSCALE_KINDS[bscale], ELEM_TYPES[a_elem],
+                        ELEM_TYPES[b_elem], M, N, K, _ptr(a), _ptr(sa), _ptr(b), _ptr(sb),
+                        _ptr(out), _stream(a.device)))
     return out
 
 

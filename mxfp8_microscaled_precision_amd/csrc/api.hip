@@ -98,11 +98,13 @@ mx_status mx_device_check(int device) {
   return check_device(device);
 }
 
-mx_status mx_quant(mx_quant_mode mode, const void* x, int64_t rows, int64_t cols, void* q, void* s,
-                   void* q_t, void* s_t, hipStream_t stream) {
+mx_status mx_quant_elem(mx_quant_mode mode, mx_elem_type elem, const void* x, int64_t rows,
+                        int64_t cols, void* q, void* s, void* q_t, void* s_t, hipStream_t stream) {
   g_err[0] = '\0';
   if (mode < MX_QUANT_ROW_1x32 || mode > MX_QUANT_BLOCK_32x32)
     return fail(MX_ERR_INVALID_ARG, "unknown quantisation mode %d", (int)mode);
+  if (elem != MX_ELEM_E4M3 && elem != MX_ELEM_E5M2)
+    return fail(MX_ERR_INVALID_ARG, "unknown element type %d", (int)elem);
   if (rows < 0 || cols < 0) return fail(MX_ERR_INVALID_ARG, "negative shape [%lld, %lld]",
                                         (long long)rows, (long long)cols);
   if (mul_overflows(rows, cols) || (rows * cols) > (INT64_MAX / 4))
@@ -126,20 +128,29 @@ mx_status mx_quant(mx_quant_mode mode, const void* x, int64_t rows, int64_t cols
   mx_status st = current_device(&dev);
   if (st != MX_OK) return st;
   hipError_t e;
+  const int el = (int)elem;
   switch (mode) {
-    case MX_QUANT_ROW_1x32: e = mx::launch_quant_row(x, rows * cols, q, s, stream); break;
-    case MX_QUANT_COL_1x32: e = mx::launch_quant_tile(1, x, rows, cols, q, s, q_t, s_t, 1, stream); break;
-    case MX_QUANT_DUAL_AXIS: e = mx::launch_quant_tile(2, x, rows, cols, q, s, q_t, s_t, 1, stream); break;
-    default: e = mx::launch_quant_tile(3, x, rows, cols, q, s, q_t, s_t, 1, stream); break;
+    case MX_QUANT_ROW_1x32: e = mx::launch_quant_row(x, rows * cols, q, s, el, stream); break;
+    case MX_QUANT_COL_1x32: e = mx::launch_quant_tile(1, x, rows, cols, q, s, q_t, s_t, 1, el, stream); break;
+    case MX_QUANT_DUAL_AXIS: e = mx::launch_quant_tile(2, x, rows, cols, q, s, q_t, s_t, 1, el, stream); break;
+    default: e = mx::launch_quant_tile(3, x, rows, cols, q, s, q_t, s_t, 1, el, stream); break;
   }
   if (e != hipSuccess) return hip_fail(e, "quantisation kernel launch");
   return MX_OK;
 }
 
-mx_status mx_gemm(mx_gemm_layout layout, mx_bscale_kind bkind, int64_t M, int64_t N, int64_t K,
-                  const void* a, const void* sa, const void* b, const void* sb, void* c,
-                  hipStream_t stream) {
+mx_status mx_quant(mx_quant_mode mode, const void* x, int64_t rows, int64_t cols, void* q, void* s,
+                   void* q_t, void* s_t, hipStream_t stream) {
+  return mx_quant_elem(mode, MX_ELEM_E4M3, x, rows, cols, q, s, q_t, s_t, stream);
+}
+
+mx_status mx_gemm_elem(mx_gemm_layout layout, mx_bscale_kind bkind, mx_elem_type a_elem,
+                       mx_elem_type b_elem, int64_t M, int64_t N, int64_t K, const void* a,
+                       const void* sa, const void* b, const void* sb, void* c, hipStream_t stream) {
   g_err[0] = '\0';
+  if ((a_elem != MX_ELEM_E4M3 && a_elem != MX_ELEM_E5M2) ||
+      (b_elem != MX_ELEM_E4M3 && b_elem != MX_ELEM_E5M2))
+    return fail(MX_ERR_INVALID_ARG, "unknown element type (a %d, b %d)", (int)a_elem, (int)b_elem);
   if (layout < MX_GEMM_FPROP || layout > MX_GEMM_WGRAD)
     return fail(MX_ERR_INVALID_ARG, "unknown GEMM layout %d", (int)layout);
   if (bkind != MX_BSCALE_1x32 && bkind != MX_BSCALE_32x32)
@@ -170,10 +181,16 @@ mx_status mx_gemm(mx_gemm_layout layout, mx_bscale_kind bkind, int64_t M, int64_
   } else {
     int bmode = mx::GEMM_B_ROW;
     if (bkind == MX_BSCALE_32x32) bmode = layout == MX_GEMM_DGRAD ? mx::GEMM_B_TILE_T : mx::GEMM_B_TILE;
-    e = mx::launch_gemm(bmode, M, N, K, a, sa, b, sb, c, stream);
+    e = mx::launch_gemm(bmode, (int)a_elem, (int)b_elem, M, N, K, a, sa, b, sb, c, stream);
   }
   if (e != hipSuccess) return hip_fail(e, "GEMM kernel launch");
   return MX_OK;
+}
+
+mx_status mx_gemm(mx_gemm_layout layout, mx_bscale_kind bkind, int64_t M, int64_t N, int64_t K,
+                  const void* a, const void* sa, const void* b, const void* sb, void* c,
+                  hipStream_t stream) {
+  return mx_gemm_elem(layout, bkind, MX_ELEM_E4M3, MX_ELEM_E4M3, M, N, K, a, sa, b, sb, c, stream);
 }
 
 mx_status mx_grouped_gemm(int64_t G, const int64_t* offsets, int64_t T, int64_t N, int64_t K,
@@ -241,12 +258,12 @@ mx_status mx_quant_batched(mx_quant_mode mode, const void* x, int64_t batch, int
   // row blocks and 32x32 tiles never cross a matrix boundary: the stack is
   // one [batch * rows, cols] matrix for them
   switch (mode) {
-    case MX_QUANT_ROW_1x32: e = mx::launch_quant_row(x, batch * rows * cols, q, s, stream); break;
+    case MX_QUANT_ROW_1x32: e = mx::launch_quant_row(x, batch * rows * cols, q, s, 0, stream); break;
     case MX_QUANT_BLOCK_32x32:
-      e = mx::launch_quant_tile(3, x, batch * rows, cols, q, s, q_t, s_t, 1, stream);
+      e = mx::launch_quant_tile(3, x, batch * rows, cols, q, s, q_t, s_t, 1, 0, stream);
       break;
-    case MX_QUANT_COL_1x32: e = mx::launch_quant_tile(1, x, rows, cols, q, s, q_t, s_t, batch, stream); break;
-    default: e = mx::launch_quant_tile(2, x, rows, cols, q, s, q_t, s_t, batch, stream); break;
+    case MX_QUANT_COL_1x32: e = mx::launch_quant_tile(1, x, rows, cols, q, s, q_t, s_t, batch, 0, stream); break;
+    default: e = mx::launch_quant_tile(2, x, rows, cols, q, s, q_t, s_t, batch, 0, stream); break;
   }
   if (e != hipSuccess) return hip_fail(e, "quantisation kernel launch");
   return MX_OK;

@@ -36,7 +36,7 @@ namespace mx {
 // read back per step with ds_read_u16 at the lane half's two blocks.  The
 // 32x32 weight scales are the same for all lanes of a fragment and are read
 // from global memory.  Otherwise every step loads scale words from global.
-template <int BMODE, bool FAST>
+template <int BMODE, bool FAST, int FA = 0, int FB = 0>
 struct Tile {
   static constexpr bool LDS_SCALES = FAST;
   const uint8_t* __restrict__ a;
@@ -322,7 +322,7 @@ struct Tile {
   template <int S>
   __device__ __forceinline__ void mma(const v8i* af, const v8i* bf, const uint32_t* sar,
                                       const uint32_t* sbr, v16f (&acc)[4][4]) {
-    mma_tile<S>(af, bf, sar, sbr, acc);
+    mma_tile<S, FA, FB>(af, bf, sar, sbr, acc);
   }
 
   // LDS fragment reads and vector-memory loads issued per K half
@@ -495,7 +495,7 @@ struct Tile {
 };
 
 
-template <int BMODE, bool FAST>
+template <int BMODE, bool FAST, int FA, int FB>
 __global__ void __launch_bounds__(NT)
 gemm_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa,
             const uint8_t* __restrict__ b, const uint8_t* __restrict__ sb, uint16_t* __restrict__ c,
@@ -507,7 +507,7 @@ gemm_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa,
   const int64_t nm = (M + BM - 1) / BM, nn = (N + BN - 1) / BN;
   int64_t mt, nt;
   tile_of(blockIdx.x, nm, nn, mt, nt);
-  Tile<BMODE, FAST> t;
+  Tile<BMODE, FAST, FA, FB> t;
   t.a = a;
   t.sa = sa;
   t.b = b;
@@ -623,30 +623,46 @@ __global__ void fill_zero_kernel(uint4* __restrict__ p, int64_t n16, uint16_t* _
     for (int64_t i = threadIdx.x; i < ntail; i += blockDim.x) tail[i] = 0;
 }
 
-hipError_t launch_gemm(int bmode, int64_t M, int64_t N, int64_t K, const void* a, const void* sa,
-                       const void* b, const void* sb, void* c, hipStream_t stream) {
+template <int BMODE, bool FAST>
+static void launch_gemm_fmt(int a_elem, int b_elem, dim3 grid, const uint8_t* A, const uint8_t* SA,
+                            const uint8_t* B, const uint8_t* SB, uint16_t* C, int64_t M, int64_t N,
+                            int64_t K, hipStream_t stream) {
+#define MX_GEMM_LAUNCH(FA_, FB_)                                                                  \
+  hipLaunchKernelGGL((gemm_kernel<BMODE, FAST, FA_, FB_>), grid, dim3(NT), 0, stream, A, SA, B, SB, \
+                     C, M, N, K)
+  if (a_elem == 0 && b_elem == 0) MX_GEMM_LAUNCH(0, 0);
+  else if (a_elem == 1 && b_elem == 0) MX_GEMM_LAUNCH(1, 0);
+  else if (a_elem == 0 && b_elem == 1) MX_GEMM_LAUNCH(0, 1);
+  else MX_GEMM_LAUNCH(1, 1);
+#undef MX_GEMM_LAUNCH
+}
+
+hipError_t launch_gemm(int bmode, int a_elem, int b_elem, int64_t M, int64_t N, int64_t K,
+                       const void* a, const void* sa, const void* b, const void* sb, void* c,
+                       hipStream_t stream) {
+  if ((a_elem != 0 && a_elem != 1) || (b_elem != 0 && b_elem != 1)) return hipErrorInvalidValue;
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  dim3 grid((unsigned)tiles), block(NT);
+  dim3 grid((unsigned)tiles);
   const uint8_t *A = (const uint8_t*)a, *SA = (const uint8_t*)sa, *B = (const uint8_t*)b,
                 *SB = (const uint8_t*)sb;
   uint16_t* C = (uint16_t*)c;
   const bool ka = (K % (4 * BK)) == 0 && (bmode != GEMM_B_TILE_T || N % 128 == 0);
-#define MX_GEMM_LAUNCH(BM_, KA_)                                                              \
-  hipLaunchKernelGGL((gemm_kernel<BM_, KA_>), grid, block, 0, stream, A, SA, B, SB, C, M, N, K)
   switch (bmode) {
     case GEMM_B_ROW:
-      if (ka) MX_GEMM_LAUNCH(GEMM_B_ROW, true); else MX_GEMM_LAUNCH(GEMM_B_ROW, false);
+      if (ka) launch_gemm_fmt<GEMM_B_ROW, true>(a_elem, b_elem, grid, A, SA, B, SB, C, M, N, K, stream);
+      else launch_gemm_fmt<GEMM_B_ROW, false>(a_elem, b_elem, grid, A, SA, B, SB, C, M, N, K, stream);
       break;
     case GEMM_B_TILE:
-      if (ka) MX_GEMM_LAUNCH(GEMM_B_TILE, true); else MX_GEMM_LAUNCH(GEMM_B_TILE, false);
+      if (ka) launch_gemm_fmt<GEMM_B_TILE, true>(a_elem, b_elem, grid, A, SA, B, SB, C, M, N, K, stream);
+      else launch_gemm_fmt<GEMM_B_TILE, false>(a_elem, b_elem, grid, A, SA, B, SB, C, M, N, K, stream);
       break;
     case GEMM_B_TILE_T:
-      if (ka) MX_GEMM_LAUNCH(GEMM_B_TILE_T, true); else MX_GEMM_LAUNCH(GEMM_B_TILE_T, false);
+      if (ka) launch_gemm_fmt<GEMM_B_TILE_T, true>(a_elem, b_elem, grid, A, SA, B, SB, C, M, N, K, stream);
+      else launch_gemm_fmt<GEMM_B_TILE_T, false>(a_elem, b_elem, grid, A, SA, B, SB, C, M, N, K, stream);
       break;
     default:
       return hipErrorInvalidValue;
   }
-#undef MX_GEMM_LAUNCH
   return hipGetLastError();
 }
 

@@ -131,8 +131,10 @@ __device__ __forceinline__ void dma4(const lds_u8* lds, uint32_t voffset, u32x4 
 
 // The 16 MFMAs of one 64-K half (S = 0, 1) of a K step for a wave's 128x128
 // sub-tile: B fragments are the first operand, A fragments the second, and
-// op_sel S picks byte S of each lane's scale word.
-template <int S>
+// op_sel S picks byte S of each lane's scale word.  FA / FB are the element
+// formats of A and B in the MFMA's encoding (0 = E4M3, 1 = E5M2), passed as
+// the formats of the instruction's first (B) and second (A) operand.
+template <int S, int FA = 0, int FB = 0>
 __device__ __forceinline__ void mma_tile(const v8i* af, const v8i* bf, const uint32_t* sar,
                                          const uint32_t* sbr, v16f (&acc)[4][4]) {
 #pragma unroll
@@ -140,7 +142,7 @@ __device__ __forceinline__ void mma_tile(const v8i* af, const v8i* bf, const uin
 #pragma unroll
     for (int fm = 0; fm < 4; fm++)
       acc[fn][fm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          bf[fn], af[fm], acc[fn][fm], 0, 0, S, (int)sbr[fn], S, (int)sar[fm]);
+          bf[fn], af[fm], acc[fn][fm], FB, FA, S, (int)sbr[fn], S, (int)sar[fm]);
 }
 
 // Ask the scheduler for MFMA, LDS read, vector load, MFMA, ... so the MFMA

@@ -1,8 +1,9 @@
 // Device helpers shared by the gfx950 kernels of the MXFP8 library.
 //
-// Formats: BF16 in, OCP E4M3 payload bytes and E8M0 scale bytes out (one
-// scale per 32 elements, or per 32x32 weight tile).  The scale exponent is
-// the smallest e with amax <= 448 * 2^e ("rceil"), clamped to [-127, 127];
+// Formats: BF16 in, OCP E4M3 (or E5M2) payload bytes and E8M0 scale bytes
+// out (one scale per 32 elements, or per 32x32 weight tile).  The scale
+// exponent is the smallest e with amax <= 448 * 2^e ("rceil"; 57344 for
+// E5M2), clamped to [-127, 127];
 // on BF16 bits that is e = E - 135 + [mantissa > 96] for a normal amax
 // (448 = 1.75 * 2^8 and 1.75 = 1 + 96/128), and -127 for zero or subnormal
 // amax.  A block holding NaN or Inf gets scale 0xFF and payload 0x7F.
@@ -50,36 +51,57 @@ __device__ __forceinline__ uint32_t xor_max(uint32_t v, int mask) {
   return umax(v, (uint32_t)__shfl_xor((int)v, mask, 64));
 }
 
-// E8M0 scale byte for a block whose largest magnitude has BF16 bits `amax`.
-__device__ __forceinline__ uint32_t scale_byte(uint32_t amax) {
+// Payload element types: OCP E4M3 (largest finite 448) and E5M2 (largest
+// finite 57344 = 1.75 * 2^15).
+enum Elem { ELEM_E4M3 = 0, ELEM_E5M2 = 1 };
+
+// E8M0 scale byte for a block whose largest magnitude has BF16 bits `amax`:
+// e = E - 135 + [m > 96] for E4M3 (448 = 1.75 * 2^8) and E - 142 + [m > 96]
+// for E5M2 (57344 = 1.75 * 2^15), at least -127.
+template <int EL>
+__device__ __forceinline__ uint32_t scale_byte_t(uint32_t amax) {
   if (amax >= 0x7F80u) return 0xFFu;  // Inf or NaN in the block
-  int e = (int)(amax >> 7) - 135 + ((amax & 0x7Fu) > 96u ? 1 : 0);
+  constexpr int off = EL == ELEM_E5M2 ? 142 : 135;
+  int e = (int)(amax >> 7) - off + ((amax & 0x7Fu) > 96u ? 1 : 0);
   e = e < -127 ? -127 : e;
   return (uint32_t)(e + 127);
 }
+__device__ __forceinline__ uint32_t scale_byte(uint32_t amax) { return scale_byte_t<ELEM_E4M3>(amax); }
 
-// The scale operand of v_cvt_scalef32_pk_fp8_bf16: a float whose value is
-// 2^(byte - 127); byte 0 is the subnormal float 2^-127.
+// The scale operand of v_cvt_scalef32_pk_{fp8,bf8}_bf16: a float whose value
+// is 2^(byte - 127); byte 0 is the subnormal float 2^-127.
 __device__ __forceinline__ float cvt_scale(uint32_t byte) {
   return __uint_as_float(byte ? (byte << 23) : 0x00400000u);
 }
 
-// Four BF16 (two packed words) -> four E4M3 bytes of one dword, dividing by
-// the block scale with round-to-nearest-even (v_cvt_scalef32_pk_fp8_bf16).
-__device__ __forceinline__ uint32_t cvt4(uint32_t w0, uint32_t w1, float scale) {
+// Four BF16 (two packed words) -> four payload bytes of one dword, dividing
+// by the block scale with round-to-nearest-even (v_cvt_scalef32_pk_fp8_bf16
+// for E4M3, v_cvt_scalef32_pk_bf8_bf16 for E5M2).
+template <int EL>
+__device__ __forceinline__ uint32_t cvt4_t(uint32_t w0, uint32_t w1, float scale) {
   v2s acc = {0, 0};
-  acc = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(acc, __builtin_bit_cast(v2bf, w0), scale, false);
-  acc = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(acc, __builtin_bit_cast(v2bf, w1), scale, true);
+  if (EL == ELEM_E5M2) {
+    acc = __builtin_amdgcn_cvt_scalef32_pk_bf8_bf16(acc, __builtin_bit_cast(v2bf, w0), scale, false);
+    acc = __builtin_amdgcn_cvt_scalef32_pk_bf8_bf16(acc, __builtin_bit_cast(v2bf, w1), scale, true);
+  } else {
+    acc = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(acc, __builtin_bit_cast(v2bf, w0), scale, false);
+    acc = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(acc, __builtin_bit_cast(v2bf, w1), scale, true);
+  }
   return __builtin_bit_cast(uint32_t, acc);
 }
+__device__ __forceinline__ uint32_t cvt4(uint32_t w0, uint32_t w1, float scale) {
+  return cvt4_t<ELEM_E4M3>(w0, w1, scale);
+}
 
-// Eight BF16 of a chunk -> eight E4M3 bytes.  A non-finite block (scale byte
-// 0xFF) gives all-NaN payload bytes.
-__device__ __forceinline__ uint2 cvt8(uint4 v, uint32_t sbyte) {
+// Eight BF16 of a chunk -> eight payload bytes.  A non-finite block (scale
+// byte 0xFF) gives all-NaN payload bytes (0x7F is NaN in both formats).
+template <int EL>
+__device__ __forceinline__ uint2 cvt8_t(uint4 v, uint32_t sbyte) {
   if (sbyte == 0xFFu) return make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
   float sc = cvt_scale(sbyte);
-  return make_uint2(cvt4(v.x, v.y, sc), cvt4(v.z, v.w, sc));
+  return make_uint2(cvt4_t<EL>(v.x, v.y, sc), cvt4_t<EL>(v.z, v.w, sc));
 }
+__device__ __forceinline__ uint2 cvt8(uint4 v, uint32_t sbyte) { return cvt8_t<ELEM_E4M3>(v, sbyte); }
 
 // BF16 pairs built from the same half of two packed words: (lo of a, lo of
 // b) and (hi of a, hi of b).  Used to pair two rows of one column.

@@ -5,13 +5,16 @@
 
 namespace mx {
 
+// Payload element type codes (mx_elem_type): 0 = E4M3, 1 = E5M2.
+
 // 1x32 quantisation of a flat BF16 array of n elements (n % 32 == 0).
-hipError_t launch_quant_row(const void* x, int64_t n, void* q, void* s, hipStream_t stream);
+hipError_t launch_quant_row(const void* x, int64_t n, void* q, void* s, int elem,
+                            hipStream_t stream);
 
 // mode 1 = column (q_t, s_t), 2 = dual (q, s, q_t, s_t), 3 = 32x32 tiles (q, s);
 // `batch` contiguous [R, C] matrices with contiguous outputs (grid.z).
 hipError_t launch_quant_tile(int mode, const void* x, int64_t R, int64_t C, void* q, void* s,
-                             void* qt, void* st, int64_t batch, hipStream_t stream);
+                             void* qt, void* st, int64_t batch, int elem, hipStream_t stream);
 
 // Column blocks restarting at every group offset along the token axis of
 // x [T, C]; q_t [C, cap], s_t [C, cap/32] with cap = 128 (T / 128 + G).
@@ -26,8 +29,10 @@ enum GemmB {
   GEMM_B_TILE_T = 2,  // b [K][N] contracted over its rows, sb tiles [K/32][N/32]
 };
 
-hipError_t launch_gemm(int bmode, int64_t M, int64_t N, int64_t K, const void* a, const void* sa,
-                       const void* b, const void* sb, void* c, hipStream_t stream);
+// a_elem / b_elem: payload element types of A and B.
+hipError_t launch_gemm(int bmode, int a_elem, int b_elem, int64_t M, int64_t N, int64_t K,
+                       const void* a, const void* sa, const void* b, const void* sb, void* c,
+                       hipStream_t stream);
 
 hipError_t launch_grouped_gemm(int64_t G, const int64_t* offsets, int64_t T, int64_t N, int64_t K,
                                const void* a, const void* sa, const void* b, const void* sb,

@@ -39,6 +39,7 @@ __device__ __forceinline__ uint32_t pk_max(uint32_t a, uint32_t b) {
 constexpr int ROW_THREADS = 256;
 constexpr int ROW_UNROLL = 4;
 
+template <int EL>
 __global__ void __launch_bounds__(ROW_THREADS)
 quant_row_kernel(const uint4* __restrict__ x, uint2* __restrict__ q, uint8_t* __restrict__ s,
                  int64_t nchunks) {
@@ -54,9 +55,9 @@ quant_row_kernel(const uint4* __restrict__ x, uint2* __restrict__ q, uint8_t* __
     for (int u = 0; u < ROW_UNROLL; u++) {
       int64_t c = base + u * ROW_THREADS + threadIdx.x;
       // quads are either wholly in range or wholly out (nchunks % 4 == 0)
-      uint32_t sb = scale_byte(quad_max(chunk_absmax(v[u])));
+      uint32_t sb = scale_byte_t<EL>(quad_max(chunk_absmax(v[u])));
       if (c < nchunks) {
-        q[c] = cvt8(v[u], sb);
+        q[c] = cvt8_t<EL>(v[u], sb);
         if ((threadIdx.x & 3) == 0) s[c >> 2] = (uint8_t)sb;
       }
     }
@@ -131,7 +132,7 @@ __device__ __forceinline__ void gcol_block(const int64_t* __restrict__ offsets, 
 // grid.z indexes a batch of equally shaped matrices (contiguous inputs and
 // outputs); the grouped column mode uses G, offsets and T (x has T rows, R is
 // the padded capacity).
-template <int MODE>
+template <int MODE, int EL>
 __global__ void __launch_bounds__(TILE_THREADS)
 quant_tile_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C, uint8_t* __restrict__ q,
                   uint8_t* __restrict__ s, uint8_t* __restrict__ qt, uint8_t* __restrict__ st,
@@ -176,10 +177,10 @@ quant_tile_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C, uint8_t*
     m = xor_max(m, 8);
     m = xor_max(m, 16);
     m = xor_max(m, 32);
-    uint32_t sb = scale_byte(m);
+    uint32_t sb = scale_byte_t<EL>(m);
     if (live) {
 #pragma unroll
-      for (int i = 0; i < 4; i++) *(uint2*)(q + (r0 + 4 * g + i) * C + c) = cvt8(v[i], sb);
+      for (int i = 0; i < 4; i++) *(uint2*)(q + (r0 + 4 * g + i) * C + c) = cvt8_t<EL>(v[i], sb);
       if (g == 0 && (h & 3) == 0) s[(r0 >> 5) * (C >> 5) + (c >> 5)] = (uint8_t)sb;
     }
     return;
@@ -199,9 +200,9 @@ quant_tile_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C, uint8_t*
   if (MODE == TILE_DUAL) {
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      const uint32_t sb = scale_byte(quad_max(chunk_absmax(v[i])));
+      const uint32_t sb = scale_byte_t<EL>(quad_max(chunk_absmax(v[i])));
       const int r = rl + i;
-      const uint2 o = cvt8(v[i], sb);
+      const uint2 o = cvt8_t<EL>(v[i], sb);
       *(__attribute__((address_space(3))) u32x2*)(LQ + r * 128 + row_chunk(r, cl >> 4) * 16 +
                                                    (cl & 15)) = (u32x2){o.x, o.y};
       if ((h & 3) == 0) LS[r * 4 + (cl >> 5)] = (uint8_t)sb;
@@ -227,8 +228,8 @@ quant_tile_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C, uint8_t*
                             (4 * g + 2 < nreal ? 0x00FF0000u : 0u) | (4 * g + 3 < nreal ? 0xFF000000u : 0u);
 #pragma unroll
   for (int k = 0; k < 4; k++) {
-    sbc[2 * k] = scale_byte(cm[k] & 0xFFFFu);
-    sbc[2 * k + 1] = scale_byte(cm[k] >> 16);
+    sbc[2 * k] = scale_byte_t<EL>(cm[k] & 0xFFFFu);
+    sbc[2 * k + 1] = scale_byte_t<EL>(cm[k] >> 16);
   }
   const uint32_t* w0 = (const uint32_t*)&v[0];
   const uint32_t* w1 = (const uint32_t*)&v[1];
@@ -239,7 +240,7 @@ quant_tile_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C, uint8_t*
     const int k = j >> 1;
     const uint32_t p01 = (j & 1) ? pair_hi(w0[k], w1[k]) : pair_lo(w0[k], w1[k]);
     const uint32_t p23 = (j & 1) ? pair_hi(w2[k], w3[k]) : pair_lo(w2[k], w3[k]);
-    uint32_t out = sbc[j] == 0xFFu ? 0x7F7F7F7Fu : cvt4(p01, p23, cvt_scale(sbc[j]));
+    uint32_t out = sbc[j] == 0xFFu ? 0x7F7F7F7Fu : cvt4_t<EL>(p01, p23, cvt_scale(sbc[j]));
     if (MODE == TILE_GCOL) out &= realmask;  // rows that hold no token stay 0x00
     const int cc = cl + j;  // local column; 4 rows rl .. rl+3 of it
     *(__attribute__((address_space(3))) uint32_t*)(LQT + cc * 128 + col_chunk(cc, rl >> 4) * 16 +
@@ -296,37 +297,53 @@ quant_tile_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C, uint8_t*
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-hipError_t launch_quant_row(const void* x, int64_t n, void* q, void* s, hipStream_t stream) {
+hipError_t launch_quant_row(const void* x, int64_t n, void* q, void* s, int elem,
+                            hipStream_t stream) {
   int64_t nchunks = n / 8;
   int64_t span = (int64_t)ROW_THREADS * ROW_UNROLL;
   int64_t blocks = (nchunks + span - 1) / span;
   if (blocks > 65536) blocks = 65536;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(quant_row_kernel, dim3((unsigned)blocks), dim3(ROW_THREADS), 0, stream,
-                     (const uint4*)x, (uint2*)q, (uint8_t*)s, nchunks);
+  if (elem == ELEM_E5M2)
+    hipLaunchKernelGGL(quant_row_kernel<ELEM_E5M2>, dim3((unsigned)blocks), dim3(ROW_THREADS), 0,
+                       stream, (const uint4*)x, (uint2*)q, (uint8_t*)s, nchunks);
+  else
+    hipLaunchKernelGGL(quant_row_kernel<ELEM_E4M3>, dim3((unsigned)blocks), dim3(ROW_THREADS), 0,
+                       stream, (const uint4*)x, (uint2*)q, (uint8_t*)s, nchunks);
   return hipGetLastError();
 }
 
+template <int MODE, int EL>
+static void launch_tile(dim3 grid, const void* x, int64_t R, int64_t C, void* q, void* s, void* qt,
+                        void* st, int64_t G, const int64_t* offsets, int64_t T, hipStream_t stream) {
+  hipLaunchKernelGGL((quant_tile_kernel<MODE, EL>), grid, dim3(TILE_THREADS), 0, stream,
+                     (const uint16_t*)x, R, C, (uint8_t*)q, (uint8_t*)s, (uint8_t*)qt, (uint8_t*)st,
+                     G, offsets, T);
+}
+
+template <int MODE>
+static void launch_tile_elem(int elem, dim3 grid, const void* x, int64_t R, int64_t C, void* q,
+                             void* s, void* qt, void* st, int64_t G, const int64_t* offsets,
+                             int64_t T, hipStream_t stream) {
+  if (elem == ELEM_E5M2)
+    launch_tile<MODE, ELEM_E5M2>(grid, x, R, C, q, s, qt, st, G, offsets, T, stream);
+  else
+    launch_tile<MODE, ELEM_E4M3>(grid, x, R, C, q, s, qt, st, G, offsets, T, stream);
+}
+
 hipError_t launch_quant_tile(int mode, const void* x, int64_t R, int64_t C, void* q, void* s,
-                             void* qt, void* st, int64_t batch, hipStream_t stream) {
+                             void* qt, void* st, int64_t batch, int elem, hipStream_t stream) {
   dim3 grid((unsigned)((R + TILE_ROWS - 1) / TILE_ROWS), (unsigned)((C + TILE_COLS - 1) / TILE_COLS),
             (unsigned)batch);
-  const uint16_t* xx = (const uint16_t*)x;
   switch (mode) {
     case TILE_COL:
-      hipLaunchKernelGGL(quant_tile_kernel<TILE_COL>, grid, dim3(TILE_THREADS), 0, stream, xx, R, C,
-                         (uint8_t*)q, (uint8_t*)s, (uint8_t*)qt, (uint8_t*)st, (int64_t)0,
-                         (const int64_t*)nullptr, (int64_t)0);
+      launch_tile_elem<TILE_COL>(elem, grid, x, R, C, q, s, qt, st, 0, nullptr, 0, stream);
       break;
     case TILE_DUAL:
-      hipLaunchKernelGGL(quant_tile_kernel<TILE_DUAL>, grid, dim3(TILE_THREADS), 0, stream, xx, R, C,
-                         (uint8_t*)q, (uint8_t*)s, (uint8_t*)qt, (uint8_t*)st, (int64_t)0,
-                         (const int64_t*)nullptr, (int64_t)0);
+      launch_tile_elem<TILE_DUAL>(elem, grid, x, R, C, q, s, qt, st, 0, nullptr, 0, stream);
       break;
     case TILE_BLOCK32:
-      hipLaunchKernelGGL(quant_tile_kernel<TILE_BLOCK32>, grid, dim3(TILE_THREADS), 0, stream, xx, R,
-                         C, (uint8_t*)q, (uint8_t*)s, (uint8_t*)qt, (uint8_t*)st, (int64_t)0,
-                         (const int64_t*)nullptr, (int64_t)0);
+      launch_tile_elem<TILE_BLOCK32>(elem, grid, x, R, C, q, s, qt, st, 0, nullptr, 0, stream);
       break;
     default:
       return hipErrorInvalidValue;
@@ -339,9 +356,7 @@ hipError_t launch_quant_grouped_col(const void* x, int64_t T, int64_t C, int64_t
                                     hipStream_t stream) {
   if (G < 1 || G > GCOL_MAX_GROUPS) return hipErrorInvalidValue;
   dim3 grid((unsigned)((cap + TILE_ROWS - 1) / TILE_ROWS), (unsigned)((C + TILE_COLS - 1) / TILE_COLS));
-  hipLaunchKernelGGL(quant_tile_kernel<TILE_GCOL>, grid, dim3(TILE_THREADS), 0, stream,
-                     (const uint16_t*)x, cap, C, (uint8_t*)nullptr, (uint8_t*)nullptr, (uint8_t*)qt,
-                     (uint8_t*)st, G, offsets, T);
+  launch_tile<TILE_GCOL, ELEM_E4M3>(grid, x, cap, C, nullptr, nullptr, qt, st, G, offsets, T, stream);
   return hipGetLastError();
 }
 

@@ -162,3 +162,21 @@ def test_grouped_wgrad_validation(args, status):
 
 def test_grouped_wgrad_empty_is_noop():
     assert mx.mx_grouped_gemm_wgrad(2, 1, 64, 0, 32, 0, 0, 0, 0, 0, 0) == 0
+
+
+def test_elem_validation():
+    # unknown element type, before any device call
+    assert mx.mx_quant_elem(0, 2, 1, 4, 32, 1, 1, 0, 0, 0) == INVALID
+    assert mx.mx_gemm_elem(0, 0, 0, 5, 4, 4, 32, 1, 1, 1, 1, 1, 0) == INVALID
+    assert mx.mx_gemm_elem(0, 0, 3, 0, 4, 4, 32, 1, 1, 1, 1, 1, 0) == INVALID
+    # the shape rules of the E4M3 entry points hold for E5M2
+    assert mx.mx_quant_elem(0, 1, 1, 4, 33, 1, 1, 0, 0, 0) == SHAPE
+    assert mx.mx_gemm_elem(0, 0, 1, 1, 4, 4, 48, 1, 1, 1, 1, 1, 0) == SHAPE
+    assert mx.mx_quant_elem(2, 1, 0, 64, 0, 0, 0, 0, 0, 0) == 0     # empty
+
+
+def test_binding_rejects_unknown_elem_names():
+    with pytest.raises(ValueError):
+        mx.quant(None, "row", "e3m4")
+    with pytest.raises(ValueError):
+        mx.gemm(None, None, None, None, "fprop", "1x32", None, "fp8", "e4m3")
