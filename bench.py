@@ -327,6 +327,44 @@ def quantisation_error(torch, mx, t, seed=11):
     return out
 
 
+def fused_producer(torch, mx, t, reps=5):
+    """The up projection with its output quantised for a following layer
+    (1x32 along N), as one fused GEMM (mx_gemm_quant) and as the GEMM's BF16
+    output followed by the row quantiser; median HIP-event time of each."""
+    qx, sx = mx.quant(t["X_up"], "row")
+    qw, sw = mx.quant(t["W_up"], "row")
+    M, N, K = qx.shape[0], qw.shape[0], qx.shape[1]
+    c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    q = torch.empty((M, N), dtype=torch.uint8, device="cuda")
+    s = torch.empty((M, N // 32), dtype=torch.uint8, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    P = lambda x: x.data_ptr()
+
+    def fused():
+        return mx.mx_gemm_quant(0, 0, 0, M, N, K, P(qx), P(sx), P(qw), P(sw), P(q), P(s), st)
+
+    def unfused():
+        r = mx.mx_gemm(0, 0, M, N, K, P(qx), P(sx), P(qw), P(sw), P(c), st)
+        return r or mx.mx_quant(0, P(c), M, N, P(q), P(s), 0, 0, st)
+
+    out = {}
+    for name, fn in (("fused", fused), ("unfused", unfused)):
+        times = []
+        for _ in range(reps + 1):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            if fn() != 0:
+                raise RuntimeError(mx.mx_last_error())
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        out[name + "_ms"] = round(sorted(times[1:])[reps // 2], 4)
+    out["gemm_shape"] = [M, N, K]
+    out["saving"] = round(1.0 - out["fused_ms"] / out["unfused_ms"], 4)
+    return out
+
+
 def cpu_baseline(W, x_dev, w_dev, budget_s):
     """The oracle (untuned) on a bounded sample of the step: dual-axis
     quantisation of leading token rows of the up-projection input and of
@@ -478,6 +516,7 @@ def main():
     out["quant"]["frac_of_copy"] = round(out["quant"]["gbps"] / cg, 4)
     out["quantisation_error"] = {k: float(f"{v:.6g}") for k, v in
                                  quantisation_error(torch, mx, stack[0]).items()}
+    out["fused_producer"] = fused_producer(torch, mx, stack[0])
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(W, stack[0]["X_up"], stack[0]["W_up"], args.cpu_seconds)

@@ -148,6 +148,20 @@ mx_status mx_gemm_elem(mx_gemm_layout layout, mx_bscale_kind bkind, mx_elem_type
                        mx_elem_type b_elem, int64_t M, int64_t N, int64_t K, const void* a,
                        const void* sa, const void* b, const void* sb, void* c, hipStream_t stream);
 
+/* Fused producer: mx_gemm (E4M3 operands) whose BF16 result is quantised
+ * in the epilogue, in 1x32 blocks along N, instead of being written: the
+ * next GEMM's row-quantised operand straight from this one, without the
+ * BF16 round trip through memory (the pages stress fusing the memory-bound
+ * steps around the matmuls: torchtitan-npu practice page, AutoFuse).
+ *   q: [M, N] payload of out_elem (E4M3 or E5M2), s: E8M0 [M, N/32];
+ *   the bytes equal mx_quant_elem(MX_QUANT_ROW_1x32, out_elem) applied to
+ *   the BF16 result mx_gemm would write (same rounding to BF16, same rule).
+ * Layouts and operand rules as mx_gemm; requires N % 32 == 0 as well.
+ * M == 0 or N == 0 is a no-op; K == 0 gives zero payload and scales. */
+mx_status mx_gemm_quant(mx_gemm_layout layout, mx_bscale_kind bkind, mx_elem_type out_elem,
+                        int64_t M, int64_t N, int64_t K, const void* a, const void* sa,
+                        const void* b, const void* sb, void* q, void* s, hipStream_t stream);
+
 /* MoE grouped MXFP8 GEMM over per-expert token groups (tutorial, "MXFP8 /
  * HiF8 architecture overview": MoE expert layers run as grouped matmul; RFC
  * section 2.2, gate_up_proj / down_proj).

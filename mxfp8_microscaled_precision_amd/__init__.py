@@ -18,6 +18,7 @@ import os
 __all__ = [
     "MXError", "lib", "mx_device_check", "mx_arch_supported", "mx_status_string",
     "mx_last_error", "mx_quant", "mx_gemm", "mx_grouped_gemm", "mx_quant_elem", "mx_gemm_elem",
+    "mx_gemm_quant", "gemm_quant",
     "mx_quant_batched",
     "mx_grouped_col_capacity", "mx_quant_grouped_col", "mx_grouped_gemm_wgrad", "quant", "gemm",
     "grouped_gemm", "quant_batched", "quant_grouped_col", "grouped_gemm_wgrad",
@@ -71,6 +72,8 @@ def lib() -> ctypes.CDLL:
         L.mx_quant_elem.argtypes = [c_int, c_int, vp, i64, i64, vp, vp, vp, vp, vp]
         L.mx_gemm_elem.restype = c_int
         L.mx_gemm_elem.argtypes = [c_int, c_int, c_int, c_int, i64, i64, i64, vp, vp, vp, vp, vp, vp]
+        L.mx_gemm_quant.restype = c_int
+        L.mx_gemm_quant.argtypes = [c_int, c_int, c_int, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
         L.mx_quant_batched.restype = c_int
         L.mx_quant_batched.argtypes = [c_int, vp, i64, i64, i64, vp, vp, vp, vp, vp]
         L.mx_grouped_col_capacity.restype = i64
@@ -121,6 +124,10 @@ def mx_quant_elem(mode, elem, x, rows, cols, q, s, q_t, s_t, stream) -> int:
 
 def mx_gemm_elem(layout, bkind, a_elem, b_elem, M, N, K, a, sa, b, sb, c, stream) -> int:
     return lib().mx_gemm_elem(layout, bkind, a_elem, b_elem, M, N, K, a, sa, b, sb, c, stream)
+
+
+def mx_gemm_quant(layout, bkind, out_elem, M, N, K, a, sa, b, sb, q, s, stream) -> int:
+    return lib().mx_gemm_quant(layout, bkind, out_elem, M, N, K, a, sa, b, sb, q, s, stream)
 
 
 def mx_quant_batched(mode, x, batch, rows, cols, q, s, q_t, s_t, stream) -> int:
@@ -235,6 +242,24 @@ def gemm(a, sa, b, sb, layout: str = "fprop", bscale: str = "1x32", out=None,
                         ELEM_TYPES[b_elem], M, N, K, _ptr(a), _ptr(sa), _ptr(b), _ptr(sb),
                         _ptr(out), _stream(a.device)))
     return out
+
+
+def gemm_quant(a, sa, b, sb, layout: str = "fprop", bscale: str = "1x32", out_elem: str = "e4m3"):
+    """Fused producer: the GEMM's BF16 result quantised in 1x32 blocks along N
+    in the epilogue -> (q [M,N] u8, s [M,N/32] u8), equal to
+    quant(gemm(...), "row", out_elem)."""
+    torch = _torch()
+    if layout not in GEMM_LAYOUTS or bscale not in BSCALE_KINDS or out_elem not in ELEM_TYPES:
+        raise ValueError(f"unknown layout {layout!r}, B scale kind {bscale!r} or element {out_elem!r}")
+    for t, n in ((a, "a"), (sa, "sa"), (b, "b"), (sb, "sb")):
+        _need(t, torch.uint8, n, 2)
+    M, K = a.shape
+    N = b.shape[1] if (bscale == "32x32" and layout == "dgrad") else b.shape[0]
+    q = torch.empty((M, N), dtype=torch.uint8, device=a.device)
+    s = torch.empty((M, N // 32), dtype=torch.uint8, device=a.device)
+    _check(mx_gemm_quant(GEMM_LAYOUTS[layout], BSCALE_KINDS[bscale], ELEM_TYPES[out_elem], M, N, K,
+                         _ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(q), _ptr(s), _stream(a.device)))
+    return q, s
 
 
 def grouped_gemm(offsets, a, sa, b, sb, out=None):

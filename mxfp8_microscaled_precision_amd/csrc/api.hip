@@ -193,6 +193,43 @@ mx_status mx_gemm(mx_gemm_layout layout, mx_bscale_kind bkind, int64_t M, int64_
   return mx_gemm_elem(layout, bkind, MX_ELEM_E4M3, MX_ELEM_E4M3, M, N, K, a, sa, b, sb, c, stream);
 }
 
+mx_status mx_gemm_quant(mx_gemm_layout layout, mx_bscale_kind bkind, mx_elem_type out_elem,
+                        int64_t M, int64_t N, int64_t K, const void* a, const void* sa,
+                        const void* b, const void* sb, void* q, void* s, hipStream_t stream) {
+  g_err[0] = '\0';
+  if (layout < MX_GEMM_FPROP || layout > MX_GEMM_WGRAD)
+    return fail(MX_ERR_INVALID_ARG, "unknown GEMM layout %d", (int)layout);
+  if (bkind != MX_BSCALE_1x32 && bkind != MX_BSCALE_32x32)
+    return fail(MX_ERR_INVALID_ARG, "unknown B scale kind %d", (int)bkind);
+  if (out_elem != MX_ELEM_E4M3 && out_elem != MX_ELEM_E5M2)
+    return fail(MX_ERR_INVALID_ARG, "unknown element type %d", (int)out_elem);
+  if (bkind == MX_BSCALE_32x32 && layout == MX_GEMM_WGRAD)
+    return fail(MX_ERR_INVALID_ARG, "the weight-gradient GEMM has no 32x32 weight operand");
+  if (M < 0 || N < 0 || K < 0) return fail(MX_ERR_INVALID_ARG, "negative GEMM shape");
+  if (mul_overflows(M, K) || mul_overflows(N, K) || mul_overflows(M, N))
+    return fail(MX_ERR_INVALID_ARG, "GEMM shape too large");
+  if (K % 32 != 0) return fail(MX_ERR_UNSUPPORTED_SHAPE, "K %lld is not a multiple of 32", (long long)K);
+  if (N % 32 != 0)
+    return fail(MX_ERR_UNSUPPORTED_SHAPE, "N %lld is not a multiple of 32 (1x32 output blocks)",
+                (long long)N);
+  if (K >= K_LIMIT)
+    return fail(MX_ERR_UNSUPPORTED_SHAPE, "K %lld too large for 32-bit tile offsets", (long long)K);
+  if (bkind == MX_BSCALE_32x32 && layout == MX_GEMM_DGRAD && (K + 256) * N >= (int64_t(1) << 31))
+    return fail(MX_ERR_UNSUPPORTED_SHAPE, "transposed 32x32 weight of %lld x %lld bytes too large",
+                (long long)K, (long long)N);
+  if (M == 0 || N == 0) return MX_OK;
+  if (!q || !s) return fail(MX_ERR_INVALID_ARG, "q or s is NULL");
+  if (K > 0 && (!a || !sa || !b || !sb)) return fail(MX_ERR_INVALID_ARG, "an operand is NULL");
+  int dev;
+  mx_status st = current_device(&dev);
+  if (st != MX_OK) return st;
+  int bmode = mx::GEMM_B_ROW;
+  if (bkind == MX_BSCALE_32x32) bmode = layout == MX_GEMM_DGRAD ? mx::GEMM_B_TILE_T : mx::GEMM_B_TILE;
+  hipError_t e = mx::launch_gemm_q(bmode, (int)out_elem, M, N, K, a, sa, b, sb, q, s, stream);
+  if (e != hipSuccess) return hip_fail(e, "fused GEMM kernel launch");
+  return MX_OK;
+}
+
 mx_status mx_grouped_gemm(int64_t G, const int64_t* offsets, int64_t T, int64_t N, int64_t K,
                           const void* a, const void* sa, const void* b, const void* sb, void* c,
                           hipStream_t stream) {

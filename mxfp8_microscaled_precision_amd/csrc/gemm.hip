@@ -36,7 +36,7 @@ namespace mx {
 // read back per step with ds_read_u16 at the lane half's two blocks.  The
 // 32x32 weight scales are the same for all lanes of a fragment and are read
 // from global memory.  Otherwise every step loads scale words from global.
-template <int BMODE, bool FAST, int FA = 0, int FB = 0>
+template <int BMODE, bool FAST, int FA = 0, int FB = 0, int OUT = 0>
 struct Tile {
   static constexpr bool LDS_SCALES = FAST;
   const uint8_t* __restrict__ a;
@@ -44,6 +44,8 @@ struct Tile {
   const uint8_t* __restrict__ b;
   const uint8_t* __restrict__ sb;
   uint16_t* __restrict__ c;
+  uint8_t* __restrict__ q_out;  // OUT != 0: row-quantised result (payload, scales)
+  uint8_t* __restrict__ s_out;
   int64_t m0, m_end, n0, N, K, nkb;
   lds_u8* st0;  // the two LDS stages (distinct arrays, so the compiler can
   lds_u8* st1;  // tell the loads into one from the reads of the other)
@@ -490,16 +492,21 @@ struct Tile {
     }
     // no load may still be writing this workgroup's LDS when it ends
     wait_vm_all();
-    store_tile_bf16(acc, c, N, m0, m_end, n0, N, wm, wn, lane);
+    if (OUT == 0)
+      store_tile_bf16(acc, c, N, m0, m_end, n0, N, wm, wn, lane);
+    else
+      store_tile_q<OUT - 1>(acc, q_out, s_out, N, m0, m_end, n0, N, wm, wn, lane);
   }
 };
 
 
-template <int BMODE, bool FAST, int FA, int FB>
+// OUT: 0 = BF16 result in c; 1 / 2 = the result quantised in 1x32 blocks
+// along N with E4M3 / E5M2 payload into q, s (fused producer).
+template <int BMODE, bool FAST, int FA, int FB, int OUT>
 __global__ void __launch_bounds__(NT)
 gemm_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa,
             const uint8_t* __restrict__ b, const uint8_t* __restrict__ sb, uint16_t* __restrict__ c,
-            int64_t M, int64_t N, int64_t K) {
+            uint8_t* __restrict__ q, uint8_t* __restrict__ s, int64_t M, int64_t N, int64_t K) {
   __shared__ __attribute__((aligned(16))) uint8_t smem0[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t smem1[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t sscale[2 * SCALE_TILE];
@@ -507,12 +514,14 @@ gemm_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa,
   const int64_t nm = (M + BM - 1) / BM, nn = (N + BN - 1) / BN;
   int64_t mt, nt;
   tile_of(blockIdx.x, nm, nn, mt, nt);
-  Tile<BMODE, FAST, FA, FB> t;
+  Tile<BMODE, FAST, FA, FB, OUT> t;
   t.a = a;
   t.sa = sa;
   t.b = b;
   t.sb = sb;
   t.c = c;
+  t.q_out = q;
+  t.s_out = s;
   t.m0 = mt * BM;
   t.m_end = (mt + 1) * BM < M ? (mt + 1) * BM : M;
   t.n0 = nt * BN;
@@ -628,8 +637,8 @@ static void launch_gemm_fmt(int a_elem, int b_elem, dim3 grid, const uint8_t* A,
                             const uint8_t* B, const uint8_t* SB, uint16_t* C, int64_t M, int64_t N,
                             int64_t K, hipStream_t stream) {
 #define MX_GEMM_LAUNCH(FA_, FB_)                                                                  \
-  hipLaunchKernelGGL((gemm_kernel<BMODE, FAST, FA_, FB_>), grid, dim3(NT), 0, stream, A, SA, B, SB, \
-                     C, M, N, K)
+  hipLaunchKernelGGL((gemm_kernel<BMODE, FAST, FA_, FB_, 0>), grid, dim3(NT), 0, stream, A, SA, B,  \
+                     SB, C, (uint8_t*)nullptr, (uint8_t*)nullptr, M, N, K)
   if (a_elem == 0 && b_elem == 0) MX_GEMM_LAUNCH(0, 0);
   else if (a_elem == 1 && b_elem == 0) MX_GEMM_LAUNCH(1, 0);
   else if (a_elem == 0 && b_elem == 1) MX_GEMM_LAUNCH(0, 1);
@@ -663,6 +672,42 @@ hipError_t launch_gemm(int bmode, int a_elem, int b_elem, int64_t M, int64_t N, 
     default:
       return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_q(int bmode, int out_elem, int64_t M, int64_t N, int64_t K, const void* a,
+                         const void* sa, const void* b, const void* sb, void* q, void* s,
+                         hipStream_t stream) {
+  if ((out_elem != 0 && out_elem != 1) || N % 32 != 0) return hipErrorInvalidValue;
+  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  dim3 grid((unsigned)tiles);
+  const uint8_t *A = (const uint8_t*)a, *SA = (const uint8_t*)sa, *B = (const uint8_t*)b,
+                *SB = (const uint8_t*)sb;
+  uint8_t *Q = (uint8_t*)q, *S = (uint8_t*)s;
+  const bool ka = (K % (4 * BK)) == 0 && (bmode != GEMM_B_TILE_T || N % 128 == 0);
+#define MX_GEMMQ_LAUNCH(BM_, KA_)                                                                 \
+  do {                                                                                            \
+    if (out_elem == 0)                                                                            \
+      hipLaunchKernelGGL((gemm_kernel<BM_, KA_, 0, 0, 1>), grid, dim3(NT), 0, stream, A, SA, B, SB, \
+                         (uint16_t*)nullptr, Q, S, M, N, K);                                      \
+    else                                                                                          \
+      hipLaunchKernelGGL((gemm_kernel<BM_, KA_, 0, 0, 2>), grid, dim3(NT), 0, stream, A, SA, B, SB, \
+                         (uint16_t*)nullptr, Q, S, M, N, K);                                      \
+  } while (0)
+  switch (bmode) {
+    case GEMM_B_ROW:
+      if (ka) MX_GEMMQ_LAUNCH(GEMM_B_ROW, true); else MX_GEMMQ_LAUNCH(GEMM_B_ROW, false);
+      break;
+    case GEMM_B_TILE:
+      if (ka) MX_GEMMQ_LAUNCH(GEMM_B_TILE, true); else MX_GEMMQ_LAUNCH(GEMM_B_TILE, false);
+      break;
+    case GEMM_B_TILE_T:
+      if (ka) MX_GEMMQ_LAUNCH(GEMM_B_TILE_T, true); else MX_GEMMQ_LAUNCH(GEMM_B_TILE_T, false);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef MX_GEMMQ_LAUNCH
   return hipGetLastError();
 }
 

@@ -207,6 +207,57 @@ __device__ __forceinline__ void store_tile_bf16(const v16f (&acc)[4][4], uint16_
   }
 }
 
+// Fused producer epilogue: the tile's BF16 result (the same values
+// store_tile_bf16 writes) quantised in 1x32 blocks along N, written as
+// payload q [M, ldq] (EL: E4M3 or E5M2) and scales s [M, ldq / 32].  After
+// the lane-pair swap of store_tile_bf16, lanes i and i + 32 together hold the
+// 32 columns of one block (16 each): a block's amax is one exchange between
+// them, and the scale and conversion are those of the row quantiser, so the
+// bytes equal quantising the BF16 output.  Requires N % 32 == 0.
+template <int EL>
+__device__ __forceinline__ void store_tile_q(const v16f (&acc)[4][4], uint8_t* __restrict__ q,
+                                             uint8_t* __restrict__ s, int64_t ldq, int64_t m0,
+                                             int64_t m_end, int64_t n0, int64_t N, int wm, int wn,
+                                             int lane) {
+  const int g = lane >> 5, i = lane & 31;
+#pragma unroll
+  for (int fn = 0; fn < 4; fn++) {
+#pragma unroll
+    for (int fm = 0; fm < 4; fm++) {
+      const v16f& v = acc[fn][fm];
+      uint32_t p[4][2];
+#pragma unroll
+      for (int r4 = 0; r4 < 4; r4++) {
+        p[r4][0] = cvt_pk_bf16(v[4 * r4 + 0], v[4 * r4 + 1]);
+        p[r4][1] = cvt_pk_bf16(v[4 * r4 + 2], v[4 * r4 + 3]);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; h++)
+#pragma unroll
+        for (int d = 0; d < 2; d++) {
+          const auto sw = __builtin_amdgcn_permlane32_swap(p[2 * h][d], p[2 * h + 1][d], false, false);
+          p[2 * h][d] = sw[0];
+          p[2 * h + 1][d] = sw[1];
+        }
+      // this lane's 16 values: h = 0 -> p[0], p[1]; h = 1 -> p[2], p[3]
+      uint32_t m = 0;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; r4++) m = umax(m, umax(pair_absmax(p[r4][0]), pair_absmax(p[r4][1])));
+      m = umax(m, (uint32_t)__shfl_xor((int)m, 32, 64));
+      const uint32_t sb = scale_byte_t<EL>(m);
+      const int64_t row = m0 + 128 * wm + 32 * fm + i;
+      const int64_t nb = n0 + 128 * wn + 32 * fn;  // first column of the block
+      if (row >= m_end || nb >= N) continue;
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+        const uint4 w = make_uint4(p[2 * h][0], p[2 * h][1], p[2 * h + 1][0], p[2 * h + 1][1]);
+        *(uint2*)(q + row * ldq + nb + 16 * h + 8 * g) = cvt8_t<EL>(w, sb);
+      }
+      if (g == 0) s[row * (ldq >> 5) + (nb >> 5)] = (uint8_t)sb;
+    }
+  }
+}
+
 // Linear workgroup id -> a contiguous run of tiles per XCD (workgroups are
 // dealt to the 8 XCDs round-robin), then grouped M-major order inside the
 // run so neighbouring tiles share A rows and B rows in that XCD's L2.

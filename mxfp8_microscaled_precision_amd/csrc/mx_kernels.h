@@ -34,6 +34,12 @@ hipError_t launch_gemm(int bmode, int a_elem, int b_elem, int64_t M, int64_t N, 
                        const void* a, const void* sa, const void* b, const void* sb, void* c,
                        hipStream_t stream);
 
+// The same GEMM (E4M3 operands) with its BF16 result quantised in 1x32
+// blocks along N (out_elem 0 = E4M3, 1 = E5M2): q [M, N], s [M, N/32].
+hipError_t launch_gemm_q(int bmode, int out_elem, int64_t M, int64_t N, int64_t K, const void* a,
+                         const void* sa, const void* b, const void* sb, void* q, void* s,
+                         hipStream_t stream);
+
 hipError_t launch_grouped_gemm(int64_t G, const int64_t* offsets, int64_t T, int64_t N, int64_t K,
                                const void* a, const void* sa, const void* b, const void* sb,
                                void* c, int num_cus, hipStream_t stream);

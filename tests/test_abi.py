@@ -180,3 +180,14 @@ def test_binding_rejects_unknown_elem_names():
         mx.quant(None, "row", "e3m4")
     with pytest.raises(ValueError):
         mx.gemm(None, None, None, None, "fprop", "1x32", None, "fp8", "e4m3")
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 0, 2, 4, 32, 32, 1, 1, 1, 1, 1, 1, 0), INVALID),    # unknown output element type
+    ((2, 1, 0, 4, 32, 32, 1, 1, 1, 1, 1, 1, 0), INVALID),    # wgrad has no 32x32 weight
+    ((0, 0, 0, 4, 40, 32, 1, 1, 1, 1, 1, 1, 0), SHAPE),      # N % 32 for the output blocks
+    ((0, 0, 0, 4, 32, 48, 1, 1, 1, 1, 1, 1, 0), SHAPE),      # K % 32
+    ((0, 0, 0, 4, 32, 32, 1, 1, 1, 1, 0, 1, 0), INVALID),    # NULL q
+])
+def test_gemm_quant_validation(args, status):
+    assert mx.mx_gemm_quant(*args) == status
