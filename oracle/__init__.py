@@ -20,7 +20,11 @@ import numpy as np
 
 _DIR = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_DIR, "mx_oracle.c")
-_LIB = os.path.join(_DIR, "liboracle.so")
+# MX_ORACLE_LIB points the wrappers at another build of the oracle (the
+# mutation tests load deliberately broken copies this way); it is never
+# rebuilt from here.
+_ALT = os.environ.get("MX_ORACLE_LIB")
+_LIB = _ALT or os.path.join(_DIR, "liboracle.so")
 
 # gcc flags: no fast-math and no FMA contraction, so every binary64 operation
 # is the plain IEEE operation written in the source.
@@ -38,6 +42,8 @@ ELEMS = {"e4m3": ELEM_E4M3, "e5m2": ELEM_E5M2}
 
 def build(force: bool = True) -> str:
     """Compile mx_oracle.c into liboracle.so (always, when force)."""
+    if _ALT:
+        return _LIB
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp%d" % os.getpid()
         subprocess.check_call(["gcc", *CFLAGS, "-o", tmp, _SRC, "-lm"])
@@ -51,7 +57,7 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        if not _ALT and (not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
             build()
         L = ctypes.CDLL(_LIB)
         u8p = ctypes.POINTER(ctypes.c_uint8)
