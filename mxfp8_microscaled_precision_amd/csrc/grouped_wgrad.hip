@@ -14,10 +14,12 @@
 // the scale row of a group starts on a 4-byte word.
 //
 // Tile 256 x 256 of one expert, four waves of 128 x 128, the MFMA layout and
-// fragment reads of the dense GEMM.  Each LDS stage holds the A and B
-// payload of one K step and their scales (four bytes per row per step,
-// loaded with buffer_load_dword ... lds), so payload and scales move and are
-// waited for together.  A workgroup runs one tile; groups differ in length,
+// fragment reads of the dense GEMM; two LDS stages of payload.  Scales are
+// staged per group of four K steps: a [256 rows][16 B] tile for A and one for
+// B (four bytes per row per step), double-buffered, loaded with
+// buffer_load_dword ... lds where one instruction covers 16 rows x 4 steps
+// (16 cache lines instead of 64 for one step of 64 rows).  A workgroup runs
+// one tile; groups differ in length,
 // so the hardware's in-order dispatch balances the load, and consecutive
 // workgroups (dealt round-robin to the 8 XCDs) take contiguous runs of one
 // expert's tile order per XCD so that tiles sharing rows share an L2.
@@ -25,19 +27,20 @@
 
 namespace mx {
 
-constexpr int W_SA = A_TILE + B_TILE;      // A scales [256 rows][4 B] of the step
-constexpr int W_SB = W_SA + BM * 4;        // B scales
-constexpr int W_STAGE = W_SB + BN * 4;     // 66 KB
+constexpr int W_STAGE = A_TILE + B_TILE;   // 64 KB of payload per K step
+constexpr int W_SCALES = (BM + BN) * 16;   // A then B scales of four K steps: 8 KB
 constexpr int W_MAX_GROUPS = 512;
 
 struct WTile {
   u32x4 ra, rb, rsa, rsb;
   uint32_t voff_a, voff_b, rows32;  // chunk offset of this lane; offset of 32 rows
-  uint32_t svoff;                   // scale row of this lane (64 wave + lane)
+  uint32_t rows16;                  // scale offset of one row
+  uint32_t svoff;                   // scale offset of this lane: row 64 wave + lane/4, step lane%4
   uint32_t pf_row, pf_a, pf_b;      // L2 prefetch: row offset, enable (0) or OOB
   int64_t nk;                       // K steps of the group
   lds_u8* st0;
   lds_u8* st1;
+  lds_u8* ss;                       // two scale tiles of W_SCALES bytes
   lds_u8* pf_scratch;
 
   // Rows past the tile edge and columns past the group's range read zero.
@@ -55,22 +58,35 @@ struct WTile {
     voff_a = (uint32_t)((8 * wave + (lane >> 3)) * ld + 16 * ((lane & 7) ^ sw));
     voff_b = voff_a;
     rows32 = (uint32_t)(32 * ld);
-    svoff = (uint32_t)((64 * wave + lane) * lds);
+    rows16 = (uint32_t)lds;
+    svoff = (uint32_t)((64 * wave + (lane >> 2)) * lds + 4 * (lane & 3));
     pf_row = (uint32_t)((64 * wave + lane) * ld);
   }
 
-  // Payload and scales of K step kt into stage st; steps past the group's end
-  // get out-of-range offsets and touch no memory.
+  // Payload of K step kt into stage st; steps past the group's end get
+  // out-of-range offsets and touch no memory.
   __device__ __forceinline__ void issue(lds_u8* st, int64_t kt, int wave) {
     const uint32_t base = kt < nk ? (uint32_t)(kt * BK) : OOB;
-    const uint32_t sbase = kt < nk ? (uint32_t)(4 * kt) : OOB;
 #pragma unroll
     for (int u = 0; u < CHUNKS; u++) dma16(st + (wave + 4 * u) * 1024, voff_a + base + u * rows32, ra);
 #pragma unroll
     for (int u = 0; u < CHUNKS; u++)
       dma16(st + A_TILE + (wave + 4 * u) * 1024, voff_b + base + u * rows32, rb);
-    dma4(st + W_SA + wave * 256, svoff + sbase, rsa);
-    dma4(st + W_SB + wave * 256, svoff + sbase, rsb);
+  }
+
+  // Scales of step group q (steps 4q .. 4q+3), part u (0..3): rows
+  // 64 wave + 16u .. +15 of A and of B, lane i -> row + i/4, step 4q + i%4,
+  // into scale tile q % 2.  Steps at or past the group's end read zero (an
+  // out-of-range offset): scale byte 0x00 is finite, and those steps' payload
+  // is zero.
+  __device__ __forceinline__ void issue_scales(int64_t q, int u, int wave, int lane) {
+    const int64_t left = nk - 4 * q;  // steps of the group in range
+    const int lim = left < 0 ? 0 : (left > 4 ? 4 : (int)left);
+    const uint32_t base = (uint32_t)(16 * q) + (uint32_t)(16 * u) * rows16;
+    const uint32_t off = (lane & 3) < lim ? svoff + base : OOB;
+    lds_u8* tile = ss + (q & 1) * W_SCALES + (64 * wave + 16 * u) * 16;
+    dma4(tile, off, rsa);
+    dma4(tile + BM * 16, off, rsb);
   }
 
   __device__ __forceinline__ void prefetch(int64_t kt, int wave) {
@@ -80,15 +96,16 @@ struct WTile {
     prefetch_lines(pf_scratch + wave * 512 + 256, (pf_row + kp) | pf_b | live, rb);
   }
 
-  // Scale words of the step held in stage st: bytes 2g, 2g+1 of the row are
-  // the step's blocks 2g and 2g+1, i.e. MFMA half S takes byte S.
-  __device__ __forceinline__ void read_scales(const lds_u8* st, int wm, int wn, int lane,
-                                              uint32_t* sar, uint32_t* sbr) {
+  // Scale words of step kt: bytes 2g, 2g+1 of the row's word for the step
+  // are the step's blocks 2g and 2g+1, i.e. MFMA half S takes byte S.
+  __device__ __forceinline__ void read_scales(int64_t kt, int wm, int wn, int lane, uint32_t* sar,
+                                              uint32_t* sbr) {
     const int g = lane >> 5, i = lane & 31;
+    const lds_u8* tile = ss + ((kt >> 2) & 1) * W_SCALES + 4 * (kt & 3) + 2 * g;
 #pragma unroll
-    for (int f = 0; f < 4; f++) sar[f] = *(const lds_u16*)(st + W_SA + (128 * wm + 32 * f + i) * 4 + 2 * g);
+    for (int f = 0; f < 4; f++) sar[f] = *(const lds_u16*)(tile + (128 * wm + 32 * f + i) * 16);
 #pragma unroll
-    for (int f = 0; f < 4; f++) sbr[f] = *(const lds_u16*)(st + W_SB + (128 * wn + 32 * f + i) * 4 + 2 * g);
+    for (int f = 0; f < 4; f++) sbr[f] = *(const lds_u16*)(tile + BM * 16 + (128 * wn + 32 * f + i) * 16);
   }
 
   template <int S>
@@ -106,8 +123,12 @@ struct WTile {
   //     vmcnt(2) (all but this wave's two latest prefetches) and a barrier:
   //     step kt+1 has landed for every wave and nobody reads `cur` any more;
   //   phase B: scales and half-0 fragments of step kt+1, loads of step kt+2
-  //     into `cur`, the prefetch of step kt+PF_DIST (always the last two
+  //     into `cur`, part (kt+1) % 4 of the scales of step group
+  //     (kt+1) / 4 + 1, the prefetch of step kt+PF_DIST (always the last two
   //     vector-memory ops), MFMAs of half 1.
+  // Group q's scales are loaded by steps 4q-5 .. 4q-2, so the last part has
+  // landed at the barrier of step 4q-1, whose phase B first reads the group;
+  // its tile was last read by step 4q-6, before the barrier of step 4q-5.
   __device__ __forceinline__ void step(lds_u8* cur, lds_u8* nxt, int64_t kt, int wave, int wm,
                                        int wn, int lane, uint32_t* sc_a, uint32_t* sc_b,
                                        v8i* f0a, v8i* f0b, v8i* f1a, v8i* f1b,
@@ -118,9 +139,10 @@ struct WTile {
     wait_vm_but_prefetch();
     __syncthreads();
     uint32_t nx_a[4], nx_b[4];
-    read_scales(nxt, wm, wn, lane, nx_a, nx_b);
+    read_scales(kt + 1, wm, wn, lane, nx_a, nx_b);
     read_frags<0>(nxt, wm, wn, lane, f0a, f0b);
     issue(cur, kt + 2, wave);
+    issue_scales((kt + 1) / 4 + 1, (int)((kt + 1) & 3), wave, lane);
     prefetch(kt + PF_DIST, wave);
     mma_tile<1>(f1a, f1b, sc_a, sc_b, acc);
     interleave_ops<24, 0>();
@@ -141,10 +163,13 @@ struct WTile {
     uint32_t sc_a[4], sc_b[4];
     v8i f0a[4], f0b[4], f1a[4], f1b[4];
     issue(st0, 0, wave);
+#pragma unroll
+    for (int u = 0; u < 4; u++) issue_scales(0, u, wave, lane);
     wait_vm_all();
     __syncthreads();
-    read_scales(st0, wm, wn, lane, sc_a, sc_b);
+    read_scales(0, wm, wn, lane, sc_a, sc_b);
     issue(st1, 1, wave);
+    issue_scales(1, 0, wave, lane);  // the part step -1 would load
     prefetch(2, wave);  // the steps' vmcnt(2) waits assume the latest two ops are prefetches
     read_frags<0>(st0, wm, wn, lane, f0a, f0b);
     // an even number of steps: a step past the end multiplies the zero
@@ -164,6 +189,7 @@ grouped_wgrad_kernel(int64_t G, const int64_t* __restrict__ offsets, int64_t T, 
                      const uint8_t* __restrict__ sb, uint16_t* __restrict__ c) {
   __shared__ __attribute__((aligned(16))) uint8_t smem0[W_STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t smem1[W_STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sscale[2 * W_SCALES];
   __shared__ __attribute__((aligned(16))) uint8_t spf[2048];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -187,6 +213,7 @@ grouped_wgrad_kernel(int64_t G, const int64_t* __restrict__ offsets, int64_t T, 
   w.nk = (hi - lo + BK - 1) / BK;
   w.st0 = (lds_u8*)smem0;
   w.st1 = (lds_u8*)smem1;
+  w.ss = (lds_u8*)sscale;
   w.pf_scratch = (lds_u8*)spf;
   const int64_t m0 = mt * BM, n0 = nt * BN;
   const int64_t m_end = (m0 + BM) < M ? m0 + BM : M, n_end = (n0 + BN) < N ? n0 + BN : N;
