@@ -126,17 +126,19 @@ def _p(t):
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemm_row_hbm_traffic.md")
-GEMM_SOURCE = os.path.join(ROOT, "mxfp8_microscaled_precision_amd", "csrc", "gemm.hip")
+GEMM_SOURCES = [os.path.join(ROOT, "mxfp8_microscaled_precision_amd", "csrc", f)
+                for f in ("gemm.hip", "gemm_common.h")]
 
 
 def gemm_traffic():
     """HBM bytes per launch of the 1x32 GEMM kernel from the committed
     FETCH_SIZE / WRITE_SIZE counter summary, or (None, None) when that summary
-    is missing or was taken from a different gemm.hip."""
+    is missing or was taken from a different kernel source (gemm.hip and
+    gemm_common.h, hashed together)."""
     import hashlib
     try:
         text = open(TRAFFIC_PROFILE).read()
-        src = open(GEMM_SOURCE, "rb").read()
+        src = b"".join(open(f, "rb").read() for f in GEMM_SOURCES)
     except OSError:
         return None, None
     fields = dict(re.findall(r"^(\w+): (\S+)$", text, re.M))

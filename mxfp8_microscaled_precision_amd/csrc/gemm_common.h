@@ -258,15 +258,29 @@ __device__ __forceinline__ void store_tile_q(const v16f (&acc)[4][4], uint8_t* _
   }
 }
 
-// Linear workgroup id -> a contiguous run of tiles per XCD (workgroups are
-// dealt to the 8 XCDs round-robin), then grouped M-major order inside the
-// run so neighbouring tiles share A rows and B rows in that XCD's L2.
+// Linear workgroup id -> position t in the grouped tile order (GM_TILES
+// m-tiles, n-tiles outer), so that the 32 tiles an XCD runs at once (8 along
+// M x 4 along N) share A rows and B rows in that XCD's L2.  Workgroups are
+// dealt to the 8 XCDs round-robin.  With few n-tiles (a group of GM_TILES
+// m-tiles has at most 32 n-tiles, i.e. at most 8 runs of 32 tiles) run r of
+// the order goes to XCD r % 8, so the XCDs work on one group at a time and
+// read its A rows once from HBM between them; otherwise each XCD takes a
+// contiguous eighth of the order (measured: 3-8% faster and 1.5% slower
+// respectively than the other choice on the workload shapes).
 __device__ __forceinline__ void tile_of(int64_t bid, int64_t nm, int64_t nn, int64_t& mt,
                                         int64_t& nt) {
   const int64_t total = nm * nn;
   const int64_t x = bid & 7, local = bid >> 3;
-  const int64_t per = total >> 3, rem = total & 7;
-  const int64_t t = x * per + (x < rem ? x : rem) + local;
+  int64_t t;
+  if (nn <= 32) {
+    // runs of 32 round-robin over the XCDs; the tail past the last whole
+    // 256 tiles keeps its position, so the map stays a bijection
+    const int64_t full = total & ~(int64_t)255;
+    t = bid < full ? (((local >> 5) << 3) + x) * 32 + (local & 31) : bid;
+  } else {
+    const int64_t per = total >> 3, rem = total & 7;
+    t = x * per + (x < rem ? x : rem) + local;
+  }
   constexpr int64_t GM = GM_TILES;
   const int64_t group = t / (GM * nn);
   const int64_t first = group * GM;
