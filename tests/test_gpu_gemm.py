@@ -213,3 +213,24 @@ def test_stack_layer_full_six_products():
     torch.cuda.synchronize()
     _end_to_end("stack up wgrad", dW, dYu, "col", Xu, "col", oracle.BKIND_ROW,
                 _sample(F, 12, rng), _sample(H, 12, rng))
+
+
+# --------------------------------------------------------------------------
+# Tile order: every tile written once, in both workgroup-to-tile maps
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K", [
+    (2088, 7264, 512),   # 9 x 29 = 261 tiles, at most 32 n-tiles: runs of 32 dealt to the XCDs
+                         # in turn over the first 256, the last 5 in place; partial edge tiles
+    (2100, 8400, 512),   # 9 x 33 = 297 tiles: a contiguous eighth per XCD, 297 % 8 = 1
+])
+def test_every_tile_written(M, N, K):
+    say(f"[gemm] tile coverage M={M} N={N} K={K}")
+    qa, sa = oracle.quant_row(bits(W.normal_bf16((M, K), 1.0, 51)))
+    qb, sb = oracle.quant_row(bits(W.normal_bf16((N, K), 1.0, 52)))
+    out = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    mx.gemm(dev(qa), dev(sa), dev(qb), dev(sb), "fprop", out=out)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any().item(), "an output tile was never written"
+    ref, bound = oracle.gemm(qa, sa, qb, sb, oracle.BKIND_ROW)
+    assert_gemm(out, ref, bound, f"tile coverage {M}x{N}x{K}")
