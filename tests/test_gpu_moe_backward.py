@@ -113,6 +113,7 @@ def _wgrad_case(sizes, M, N, seed):
     ([0, 0], 64, 64),                            # all experts empty
     ([1000], 256, 512),
     ([130, 128, 129, 127], 256, 256),            # odd and even step counts
+    ([600, 700, 850, 1100], 96, 96),             # 5, 6, 7, 9 steps: partial groups of four steps
 ])
 def test_wgrad_small_cases(sizes, M, N):
     say(f"[moe-bwd] wgrad sizes={sizes} M={M} N={N}")
@@ -122,6 +123,27 @@ def test_wgrad_small_cases(sizes, M, N):
     for g, m in enumerate(sizes):
         if m == 0:
             assert torch.count_nonzero(c[g]) == 0, g
+
+
+def test_wgrad_neighbour_nan_scales_stay_out():
+    """Scale words past a group's last step are not read: with every scale
+    byte of the next group set to NaN (0xFF), an expert whose step count is
+    not a multiple of four still matches the oracle (finite), and the NaN
+    group is NaN where the oracle says so."""
+    sizes = [600, 700]                      # 5 and 6 steps
+    M, N = 64, 96
+    off = _offsets(sizes)
+    T = int(off[-1])
+    qa, sa = oracle.quant_col_grouped(bits(W.normal_bf16((T, M), 0.01, 61)), off)
+    qb, sb = oracle.quant_col_grouped(bits(W.normal_bf16((T, N), 1.0, 62)), off)
+    P1 = oracle.group_col(1, off[1])
+    sa[:, P1 // 32:] = 0xFF
+    sb[:, P1 // 32:] = 0xFF
+    c = mx.grouped_gemm_wgrad(dev(off), T, dev(qa), dev(sa), dev(qb), dev(sb))
+    torch.cuda.synchronize()
+    ref, bound = oracle.grouped_gemm_wgrad(off, qa, sa, qb, sb)
+    assert np.isfinite(ref[0]).all() and np.isnan(ref[1]).all()
+    assert_gemm(c, ref, bound, "wgrad with NaN scales in the next group")
 
 
 def test_wgrad_equals_dense_gemm_per_expert():
