@@ -48,6 +48,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=20.0,
                    help="rough budget for the oracle sample")
+    p.add_argument("--no-other-configs", action="store_true",
+                   help="skip the dense and 32x32-weight configuration timings")
     p.add_argument("--calibration-copy", action="store_true",
                    help="run one plain 1 GiB device-to-device copy before warm-up (untimed), the "
                         "reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -367,6 +369,89 @@ def fused_producer(torch, mx, t, reps=5):
     return out
 
 
+def other_configs(torch, mx, W, warm=5, reps=20):
+    """The dense (8192 x 4096 x 4096, dual-axis) and 32x32-weight (16384
+    tokens, 7168 <-> 2048) configurations, outside the timed step.  Every
+    kernel is launched warm + reps times with a 1 GiB buffer fill before each
+    launch, so no operand stays in L2 or the Infinity Cache; the median
+    launch (HIP events on the launch stream) is reported."""
+    import statistics
+    u8, bf = torch.uint8, torch.bfloat16
+    dev = "cuda"
+    flush = torch.empty(1 << 30, dtype=u8, device=dev)
+    L = Launcher(torch, mx)
+    L.record = True
+
+    def med(call):
+        L.events.clear()
+        for i in range(warm + reps):
+            flush.fill_(i & 255)
+            call()
+        torch.cuda.synchronize()
+        ev = L.events[warm:]
+        ms = statistics.median(s.elapsed_time(e) for _, _, _, s, e in ev)
+        work, unit = ev[0][1], ev[0][2]
+        rate = work / (ms * 1e-3)
+        if unit == "FLOP":
+            return {"tflops": round(rate / 1e12, 1), "frac_peak": round(rate / 1e12 / PEAK_FP8_TFLOPS, 4),
+                    "ms": round(ms, 4)}
+        return {"gbps": round(rate / 1e9, 1), "frac_peak": round(rate / 1e9 / PEAK_HBM_GBPS, 4),
+                "ms": round(ms, 4)}
+
+    def dual(R, C):
+        return (torch.empty((R, C), dtype=u8, device=dev), torch.empty((R, C // 32), dtype=u8, device=dev),
+                torch.empty((C, R), dtype=u8, device=dev), torch.empty((C, R // 32), dtype=u8, device=dev))
+
+    def row(R, C):
+        return (torch.empty((R, C), dtype=u8, device=dev), torch.empty((R, C // 32), dtype=u8, device=dev),
+                None, None)
+
+    def tile(R, C):
+        return (torch.empty((R, C), dtype=u8, device=dev),
+                torch.empty((R // 32, C // 32), dtype=u8, device=dev), None, None)
+
+    out = {}
+    d = W.dense(dev)
+    X, Wt, dY = d["X"], d["W"], d["dY"]
+    M, K = X.shape
+    N = Wt.shape[0]
+    bx, bw, bd = dual(M, K), dual(N, K), dual(M, N)
+    Y = torch.empty((M, N), dtype=bf, device=dev)
+    dX = torch.empty((M, K), dtype=bf, device=dev)
+    dW = torch.empty((N, K), dtype=bf, device=dev)
+    r = {
+        "quant_dual_X": med(lambda: L.quant("q", 2, X, bx)),
+        "quant_dual_W": med(lambda: L.quant("q", 2, Wt, bw)),
+        "quant_dual_dY": med(lambda: L.quant("q", 2, dY, bd)),
+        "fprop": med(lambda: L.gemm("g", 0, 0, M, N, K, bx[0], bx[1], bw[0], bw[1], Y)),
+        "dgrad": med(lambda: L.gemm("g", 1, 0, M, K, N, bd[0], bd[1], bw[2], bw[3], dX)),
+        "wgrad": med(lambda: L.gemm("g", 2, 0, N, K, M, bd[2], bd[3], bx[2], bx[3], dW)),
+    }
+    out[f"dense {M}x{K} -> {N}"] = r
+    del d, X, Wt, dY, bx, bw, bd, Y, dX, dW
+    d = W.block32(dev)
+    W1, W2, X1, X2 = d["W1"], d["W2"], d["X1"], d["X2"]
+    T, H = X1.shape
+    F = W1.shape[0]
+    b1, b2, bx1, bx2 = tile(F, H), tile(H, F), row(T, H), row(T, F)
+    Y1 = torch.empty((T, F), dtype=bf, device=dev)
+    Y2 = torch.empty((T, H), dtype=bf, device=dev)
+    r = {
+        "quant_32x32_W1": med(lambda: L.quant("q", 3, W1, b1)),
+        "quant_32x32_W2": med(lambda: L.quant("q", 3, W2, b2)),
+        "quant_row_X1": med(lambda: L.quant("q", 0, X1, bx1)),
+        "quant_row_X2": med(lambda: L.quant("q", 0, X2, bx2)),
+        "fprop1": med(lambda: L.gemm("g", 0, 1, T, F, H, bx1[0], bx1[1], b1[0], b1[1], Y1)),
+        "fprop2": med(lambda: L.gemm("g", 0, 1, T, H, F, bx2[0], bx2[1], b2[0], b2[1], Y2)),
+        "dgrad1": med(lambda: L.gemm("g", 1, 1, T, H, F, bx2[0], bx2[1], b1[0], b1[1], Y2)),
+        "dgrad2": med(lambda: L.gemm("g", 1, 1, T, F, H, bx1[0], bx1[1], b2[0], b2[1], Y1)),
+    }
+    out[f"32x32 weights, {T} tokens, {H} <-> {F}"] = r
+    del flush
+    torch.cuda.synchronize()
+    return out
+
+
 def cpu_baseline(W, x_dev, w_dev, budget_s):
     """The oracle (untuned) on a bounded sample of the step: dual-axis
     quantisation of leading token rows of the up-projection input and of
@@ -519,6 +604,9 @@ def main():
     out["quantisation_error"] = {k: float(f"{v:.6g}") for k, v in
                                  quantisation_error(torch, mx, stack[0]).items()}
     out["fused_producer"] = fused_producer(torch, mx, stack[0])
+    if not args.no_other_configs:
+        print("[bench] other configurations", file=sys.stderr, flush=True)
+        out["other_configs"] = other_configs(torch, mx, W)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(W, stack[0]["X_up"], stack[0]["W_up"], args.cpu_seconds)
