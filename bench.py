@@ -411,6 +411,18 @@ def other_configs(torch, mx, W, warm=5, reps=20):
                 torch.empty((R // 32, C // 32), dtype=u8, device=dev), None, None)
 
     out = {}
+    # the tiny linear: launch-latency-bound, so microseconds are the figure
+    d = W.tiny(dev)
+    A, Wq = d["A"], d["W"]
+    ba, bw1 = row(*A.shape), row(*Wq.shape)
+    C1 = torch.empty((A.shape[0], Wq.shape[0]), dtype=bf, device=dev)
+    r = {
+        "quant_row_A": med(lambda: L.quant("q", 0, A, ba)),
+        "quant_row_W": med(lambda: L.quant("q", 0, Wq, bw1)),
+        "fprop": med(lambda: L.gemm("g", 0, 0, A.shape[0], Wq.shape[0], A.shape[1], ba[0], ba[1],
+                                    bw1[0], bw1[1], C1)),
+    }
+    out[f"tiny {A.shape[0]}x{A.shape[1]} -> {Wq.shape[0]} (launch-bound; see ms)"] = r
     d = W.dense(dev)
     X, Wt, dY = d["X"], d["W"], d["dY"]
     M, K = X.shape
