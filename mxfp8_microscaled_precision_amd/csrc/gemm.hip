@@ -29,16 +29,23 @@ namespace mx {
 //     stage kt+1 into F0 interleaved.
 // The loop body has no branches so the scheduler can interleave freely.
 //
-// Scales.  With LDS_SCALES (K a multiple of 512, so the K loop is a whole
-// number of 4-step groups) the per-row scale bytes of four K steps are
-// staged through LDS like the operands: one 16-byte load per row every four
-// steps (rows cost one cache line per four steps instead of one per step),
-// read back per step with ds_read_u16 at the lane half's two blocks.  The
-// 32x32 weight scales are the same for all lanes of a fragment and are read
-// from global memory.  Otherwise every step loads scale words from global.
-template <int BMODE, bool FAST, int FA = 0, int FB = 0, int OUT = 0>
+// Scales.  With LDS_SCALES (K a multiple of the K step and at least four
+// steps) the per-row scale bytes of four K steps are staged through LDS like
+// the operands: one 16-byte load per row every four steps (rows cost one
+// cache line per four steps instead of one per step), read back per step
+// with ds_read_u16 at the lane half's two blocks.  When the step count is not
+// a multiple of four, the last group's 16 bytes are loaded ending at the
+// row's last scale byte (never past it) and read at a matching offset, and
+// the group's steps past the end (zero payload from out-of-range loads) get
+// scale words 0 (finite).  Otherwise every step loads scale words from
+// global memory.
+// FAST: 0 = the general variant (any K a multiple of 32); 1 = the pipeline
+// with LDS-staged scales, K a multiple of 512; 2 = the same with a partial last
+// group of four K steps (K a multiple of 128, at least 512).
+template <int BMODE, int FAST, int FA = 0, int FB = 0, int OUT = 0>
 struct Tile {
-  static constexpr bool LDS_SCALES = FAST;
+  static constexpr bool LDS_SCALES = FAST != 0;
+  static constexpr bool PARTIAL = FAST == 2;
   const uint8_t* __restrict__ a;
   const uint8_t* __restrict__ sa;
   const uint8_t* __restrict__ b;
@@ -47,6 +54,9 @@ struct Tile {
   uint8_t* __restrict__ q_out;  // OUT != 0: row-quantised result (payload, scales)
   uint8_t* __restrict__ s_out;
   int64_t m0, m_end, n0, N, K, nkb;
+  int64_t nks;      // K steps
+  int64_t last_g;   // LDS_SCALES: index of the last 4-step group
+  uint32_t sdelta;  // LDS_SCALES: bytes the last group's load is shifted back by
   lds_u8* st0;  // the two LDS stages (distinct arrays, so the compiler can
   lds_u8* st1;  // tell the loads into one from the reads of the other)
   lds_u8* ss0;  // two scale tiles (LDS_SCALES): [256 rows][16 B] of A, then
@@ -67,6 +77,9 @@ struct Tile {
 
   __device__ __forceinline__ void setup(int wave, int lane) {
     const int64_t mrows = m_end - m0;
+    nks = (K + BK - 1) / BK;
+    last_g = (nks - 1) >> 2;
+    sdelta = (uint32_t)(16 * (last_g + 1) - 4 * nks);  // 16 - 4 * (steps in the last group)
     ra = make_rsrc(a + m0 * K, mrows * K);
     // A: instruction t = wave + 4u covers LDS rows 8t .. 8t+7 (1 KB); lane i
     // lands in row r = 8t + i/8 at physical chunk i%8, holding logical chunk
@@ -271,8 +284,16 @@ struct Tile {
   // after wave 0's own vmcnt wait publishes them.
   __device__ __forceinline__ void dma_scales(lds_u8* buf, int64_t kb0, int wave) {
     const bool live = kb0 < nkb;  // none past the end
-    dma16(buf + wave * 1024, live ? svoff + (uint32_t)kb0 : OOB, rsa);
-    const uint32_t offb = live ? svoff_b + (uint32_t)kb0 * sb_row : OOB;
+    // per-row 16-byte loads of the last group end at the row's last byte
+    const int64_t kbl = (!PARTIAL || kb0 + 16 <= nkb) ? kb0 : nkb - 16;
+    dma16(buf + wave * 1024, live ? svoff + (uint32_t)kbl : OOB, rsa);
+    uint32_t offb = live ? svoff_b + (uint32_t)(BMODE == GEMM_B_TILE_T ? kb0 : kbl) * sb_row : OOB;
+    if (BMODE == GEMM_B_TILE_T && PARTIAL) {
+      // lane 2r + h loads row kb0 + r of the tile scales; rows past the end
+      // read zero
+      const int lane = threadIdx.x & 63;
+      offb = kb0 + (lane >> 1) < nkb ? offb : OOB;
+    }
     if (BMODE == GEMM_B_ROW)
       dma16(buf + 4096 + wave * 1024, offb, rsb);
     else if (BMODE == GEMM_B_TILE) {
@@ -282,16 +303,20 @@ struct Tile {
     }
   }
 
-  __device__ __forceinline__ void read_scales(const lds_u8* buf, int q, int wm, int wn, int lane,
-                                              uint32_t* sar, uint32_t* sbr) {
+  // Scale words of step kst, step q = kst % 4 of its group (q is passed as a
+  // compile-time value where the caller has it).
+  __device__ __forceinline__ void read_scales(const lds_u8* buf, int q, int64_t kst, int wm, int wn,
+                                              int lane, uint32_t* sar, uint32_t* sbr) {
     const int g = lane >> 5, i = lane & 31;
+    const uint32_t dl = (PARTIAL && (kst >> 2) == last_g) ? sdelta : 0u;  // the last group's shift
+    const uint32_t keep = (!PARTIAL || kst < nks) ? 0xFFFFFFFFu : 0u;   // steps past the end: 0
 #pragma unroll
     for (int f = 0; f < 4; f++)
-      sar[f] = *(const lds_u16*)(buf + (128 * wm + 32 * f + i) * 16 + 4 * q + 2 * g);
+      sar[f] = keep & *(const lds_u16*)(buf + (128 * wm + 32 * f + i) * 16 + 4 * q + dl + 2 * g);
     if (BMODE == GEMM_B_ROW) {
 #pragma unroll
       for (int f = 0; f < 4; f++)
-        sbr[f] = *(const lds_u16*)(buf + 4096 + (128 * wn + 32 * f + i) * 16 + 4 * q + 2 * g);
+        sbr[f] = keep & *(const lds_u16*)(buf + 4096 + (128 * wn + 32 * f + i) * 16 + 4 * q + dl + 2 * g);
     } else {
       // one word per fragment (B_TILE: the tile row's four blocks of step q)
       // or per block (B_TILE_T: the wave's four tile columns of block 4q+i),
@@ -299,9 +324,9 @@ struct Tile {
       uint32_t w[4];
 #pragma unroll
       for (int f = 0; f < 4; f++)
-        w[f] = BMODE == GEMM_B_TILE
-                   ? *(const __attribute__((address_space(3))) uint32_t*)(buf + 4096 + (4 * wn + f) * 16 + 4 * q)
-                   : *(const __attribute__((address_space(3))) uint32_t*)(buf + 4096 + (4 * q + f) * 8 + 4 * wn);
+        w[f] = keep & (BMODE == GEMM_B_TILE
+                   ? *(const __attribute__((address_space(3))) uint32_t*)(buf + 4096 + (4 * wn + f) * 16 + 4 * q + dl)
+                   : *(const __attribute__((address_space(3))) uint32_t*)(buf + 4096 + (4 * q + f) * 8 + 4 * wn));
       finish_scales_b(lane, w, sbr);
     }
   }
@@ -396,7 +421,7 @@ struct Tile {
     __syncthreads();
     // phase B
     if (U == 0) dma_scales(sdma, (kt + 4) * (BK / 32), wave);
-    read_scales(sread, (U + 1) & 3, wm, wn, lane, nx_a, nx_b);
+    read_scales(sread, (U + 1) & 3, kt + 1, wm, wn, lane, nx_a, nx_b);
     const int64_t k2 = (kt + 2) * BK;
     const uint32_t ba = step_base_a(k2), bb = step_base_b(k2);
     const int g = lane >> 5, i = lane & 31;
@@ -449,12 +474,12 @@ struct Tile {
     v8i f0a[4], f0b[4], f1a[4], f1b[4];
 
     if (LDS_SCALES) {
-      // nk is a multiple of 4
+      // nk >= 4; the last group may be partial
       issue_stage(st0, 0, wave, lane);
       dma_scales(ss0, 0, wave);
       wait_vm_all();
       __syncthreads();
-      read_scales(ss0, 0, wm, wn, lane, sc_a, sc_b);
+      read_scales(ss0, 0, 0, wm, wn, lane, sc_a, sc_b);
       issue_stage(st1, BK, wave, lane);
       // The steps wait with vmcnt(2), which leaves the two most recent loads
       // in flight: those must be prefetches, never stage loads.  So the
@@ -502,7 +527,7 @@ struct Tile {
 
 // OUT: 0 = BF16 result in c; 1 / 2 = the result quantised in 1x32 blocks
 // along N with E4M3 / E5M2 payload into q, s (fused producer).
-template <int BMODE, bool FAST, int FA, int FB, int OUT>
+template <int BMODE, int FAST, int FA, int FB, int OUT>
 __global__ void __launch_bounds__(NT)
 gemm_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa,
             const uint8_t* __restrict__ b, const uint8_t* __restrict__ sb, uint16_t* __restrict__ c,
@@ -546,7 +571,7 @@ gemm_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa,
 // device-side offsets (clamped into [0, T] and made non-decreasing, so bad
 // offsets can never address outside the operands) and walks it with a static
 // stride.  Tile t -> (group g, m tile within g, n tile).
-template <bool FAST>
+template <int FAST>
 __global__ void __launch_bounds__(NT)
 grouped_gemm_kernel(int64_t G, const int64_t* __restrict__ offsets, int64_t T, int64_t N,
                     int64_t K, const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa,
@@ -632,7 +657,7 @@ __global__ void fill_zero_kernel(uint4* __restrict__ p, int64_t n16, uint16_t* _
     for (int64_t i = threadIdx.x; i < ntail; i += blockDim.x) tail[i] = 0;
 }
 
-template <int BMODE, bool FAST>
+template <int BMODE, int FAST>
 static void launch_gemm_fmt(int a_elem, int b_elem, dim3 grid, const uint8_t* A, const uint8_t* SA,
                             const uint8_t* B, const uint8_t* SB, uint16_t* C, int64_t M, int64_t N,
                             int64_t K, hipStream_t stream) {
@@ -646,6 +671,14 @@ static void launch_gemm_fmt(int a_elem, int b_elem, dim3 grid, const uint8_t* A,
 #undef MX_GEMM_LAUNCH
 }
 
+// Pipeline variant for a shape (the FAST parameter of Tile): 1 when K is a
+// multiple of 512, 2 when it is a multiple of 128 and at least 512, else 0;
+// the transposed 32x32 weight also needs N % 128 == 0 for the pipeline.
+static int pipe_of(int bmode, int64_t N, int64_t K) {
+  if (K % BK != 0 || K < 4 * BK || (bmode == GEMM_B_TILE_T && N % 128 != 0)) return 0;
+  return K % (4 * BK) == 0 ? 1 : 2;
+}
+
 hipError_t launch_gemm(int bmode, int a_elem, int b_elem, int64_t M, int64_t N, int64_t K,
                        const void* a, const void* sa, const void* b, const void* sb, void* c,
                        hipStream_t stream) {
@@ -655,23 +688,28 @@ hipError_t launch_gemm(int bmode, int a_elem, int b_elem, int64_t M, int64_t N, 
   const uint8_t *A = (const uint8_t*)a, *SA = (const uint8_t*)sa, *B = (const uint8_t*)b,
                 *SB = (const uint8_t*)sb;
   uint16_t* C = (uint16_t*)c;
-  const bool ka = (K % (4 * BK)) == 0 && (bmode != GEMM_B_TILE_T || N % 128 == 0);
+  const int pipe = pipe_of(bmode, N, K);
+#define MX_GEMM_MODE(BM_)                                                                         \
+  do {                                                                                            \
+    if (pipe == 1) launch_gemm_fmt<BM_, 1>(a_elem, b_elem, grid, A, SA, B, SB, C, M, N, K, stream); \
+    else if (pipe == 2)                                                                           \
+      launch_gemm_fmt<BM_, 2>(a_elem, b_elem, grid, A, SA, B, SB, C, M, N, K, stream);            \
+    else launch_gemm_fmt<BM_, 0>(a_elem, b_elem, grid, A, SA, B, SB, C, M, N, K, stream);         \
+  } while (0)
   switch (bmode) {
     case GEMM_B_ROW:
-      if (ka) launch_gemm_fmt<GEMM_B_ROW, true>(a_elem, b_elem, grid, A, SA, B, SB, C, M, N, K, stream);
-      else launch_gemm_fmt<GEMM_B_ROW, false>(a_elem, b_elem, grid, A, SA, B, SB, C, M, N, K, stream);
+      MX_GEMM_MODE(GEMM_B_ROW);
       break;
     case GEMM_B_TILE:
-      if (ka) launch_gemm_fmt<GEMM_B_TILE, true>(a_elem, b_elem, grid, A, SA, B, SB, C, M, N, K, stream);
-      else launch_gemm_fmt<GEMM_B_TILE, false>(a_elem, b_elem, grid, A, SA, B, SB, C, M, N, K, stream);
+      MX_GEMM_MODE(GEMM_B_TILE);
       break;
     case GEMM_B_TILE_T:
-      if (ka) launch_gemm_fmt<GEMM_B_TILE_T, true>(a_elem, b_elem, grid, A, SA, B, SB, C, M, N, K, stream);
-      else launch_gemm_fmt<GEMM_B_TILE_T, false>(a_elem, b_elem, grid, A, SA, B, SB, C, M, N, K, stream);
+      MX_GEMM_MODE(GEMM_B_TILE_T);
       break;
     default:
       return hipErrorInvalidValue;
   }
+#undef MX_GEMM_MODE
   return hipGetLastError();
 }
 
@@ -684,7 +722,7 @@ hipError_t launch_gemm_q(int bmode, int out_elem, int64_t M, int64_t N, int64_t 
   const uint8_t *A = (const uint8_t*)a, *SA = (const uint8_t*)sa, *B = (const uint8_t*)b,
                 *SB = (const uint8_t*)sb;
   uint8_t *Q = (uint8_t*)q, *S = (uint8_t*)s;
-  const bool ka = (K % (4 * BK)) == 0 && (bmode != GEMM_B_TILE_T || N % 128 == 0);
+  const int pipe = pipe_of(bmode, N, K);
 #define MX_GEMMQ_LAUNCH(BM_, KA_)                                                                 \
   do {                                                                                            \
     if (out_elem == 0)                                                                            \
@@ -694,19 +732,26 @@ hipError_t launch_gemm_q(int bmode, int out_elem, int64_t M, int64_t N, int64_t 
       hipLaunchKernelGGL((gemm_kernel<BM_, KA_, 0, 0, 2>), grid, dim3(NT), 0, stream, A, SA, B, SB, \
                          (uint16_t*)nullptr, Q, S, M, N, K);                                      \
   } while (0)
+#define MX_GEMMQ_MODE(BM_)                                                                        \
+  do {                                                                                            \
+    if (pipe == 1) MX_GEMMQ_LAUNCH(BM_, 1);                                                       \
+    else if (pipe == 2) MX_GEMMQ_LAUNCH(BM_, 2);                                                  \
+    else MX_GEMMQ_LAUNCH(BM_, 0);                                                                 \
+  } while (0)
   switch (bmode) {
     case GEMM_B_ROW:
-      if (ka) MX_GEMMQ_LAUNCH(GEMM_B_ROW, true); else MX_GEMMQ_LAUNCH(GEMM_B_ROW, false);
+      MX_GEMMQ_MODE(GEMM_B_ROW);
       break;
     case GEMM_B_TILE:
-      if (ka) MX_GEMMQ_LAUNCH(GEMM_B_TILE, true); else MX_GEMMQ_LAUNCH(GEMM_B_TILE, false);
+      MX_GEMMQ_MODE(GEMM_B_TILE);
       break;
     case GEMM_B_TILE_T:
-      if (ka) MX_GEMMQ_LAUNCH(GEMM_B_TILE_T, true); else MX_GEMMQ_LAUNCH(GEMM_B_TILE_T, false);
+      MX_GEMMQ_MODE(GEMM_B_TILE_T);
       break;
     default:
       return hipErrorInvalidValue;
   }
+#undef MX_GEMMQ_MODE
 #undef MX_GEMMQ_LAUNCH
   return hipGetLastError();
 }
@@ -721,14 +766,15 @@ hipError_t launch_grouped_gemm(int64_t G, const int64_t* offsets, int64_t T, int
   wgs = (wgs + 7) / 8 * 8;
   if (upper < wgs) wgs = (upper + 7) / 8 * 8;
   if (wgs < 8) wgs = 8;
-  if (K % (4 * BK) == 0)
-    hipLaunchKernelGGL(grouped_gemm_kernel<true>, dim3((unsigned)wgs), dim3(NT), 0, stream, G,
-                       offsets, T, N, K, (const uint8_t*)a, (const uint8_t*)sa, (const uint8_t*)b,
-                       (const uint8_t*)sb, (uint16_t*)c);
-  else
-    hipLaunchKernelGGL(grouped_gemm_kernel<false>, dim3((unsigned)wgs), dim3(NT), 0, stream, G,
-                       offsets, T, N, K, (const uint8_t*)a, (const uint8_t*)sa, (const uint8_t*)b,
-                       (const uint8_t*)sb, (uint16_t*)c);
+  const int pipe = pipe_of(GEMM_B_ROW, N, K);
+#define MX_GROUPED_LAUNCH(P_)                                                                     \
+  hipLaunchKernelGGL(grouped_gemm_kernel<P_>, dim3((unsigned)wgs), dim3(NT), 0, stream, G, offsets, \
+                     T, N, K, (const uint8_t*)a, (const uint8_t*)sa, (const uint8_t*)b,            \
+                     (const uint8_t*)sb, (uint16_t*)c)
+  if (pipe == 1) MX_GROUPED_LAUNCH(1);
+  else if (pipe == 2) MX_GROUPED_LAUNCH(2);
+  else MX_GROUPED_LAUNCH(0);
+#undef MX_GROUPED_LAUNCH
   return hipGetLastError();
 }
 

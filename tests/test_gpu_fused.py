@@ -27,6 +27,8 @@ CASES = [  # (M, N, K, layout, bscale)
     (512, 384, 2048, "fprop", "1x32"),
     (384, 256, 2048, "fprop", "32x32"),
     (320, 384, 1536, "dgrad", "32x32"),
+    (300, 256, 1152, "fprop", "1x32"),   # partial last group of four K steps
+    (256, 384, 1408, "dgrad", "32x32"),
 ]
 
 

@@ -32,7 +32,10 @@ def test_tiny_config_fprop():
 
 
 SHAPES = [(1, 1, 32), (64, 64, 32), (300, 200, 160), (257, 513, 96), (512, 256, 4096),
-          (33, 290, 1056), (256, 256, 128)]
+          (33, 290, 1056), (256, 256, 128),
+          # K a multiple of 128 but not of 512: the pipelined kernel with a partial last
+          # group of four K steps (1, 2 and 3 steps of it real)
+          (300, 520, 1152), (257, 384, 1280), (512, 256, 1408)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
@@ -54,7 +57,8 @@ def test_row_scales_all_layouts(M, N, K, layout):
 
 
 @pytest.mark.parametrize("M,N,K", [(64, 64, 64), (300, 224, 160), (257, 544, 1056), (512, 256, 4096),
-                                   (384, 384, 2048), (640, 896, 1536)])
+                                   (384, 384, 2048), (640, 896, 1536),
+                                   (300, 512, 1152), (257, 384, 1408)])
 def test_block32_weight_fprop_and_dgrad(M, N, K):
     # fprop: Y[M, out=N] = X[M, in=K] W[out=N, in=K]^T with W in 32x32 tiles
     qx, sx = oracle.quant_row(bits(W.normal_bf16((M, K), 1.0, M + K)))

@@ -40,6 +40,7 @@ def _case(sizes, N, K, seed, what):
     ([0, 0, 700, 0], 256, 256),          # everything in one expert, empties around it
     ([1] * 40, 96, 96),                  # single-row groups
     ([513], 512, 1056),                  # one group, ragged against the 256-row tile
+    ([300, 0, 257, 700], 256, 1152),     # K steps not a multiple of four
 ])
 def test_small_cases(sizes, N, K):
     _case(sizes, N, K, sum(sizes) + N + K, f"sizes={sizes[:6]}")
