@@ -238,3 +238,57 @@ def test_every_tile_written(M, N, K):
     assert not torch.isnan(out).any().item(), "an output tile was never written"
     ref, bound = oracle.gemm(qa, sa, qb, sb, oracle.BKIND_ROW)
     assert_gemm(out, ref, bound, f"tile coverage {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("product", ["fprop", "dgrad", "wgrad"])
+def test_dense_config_every_element(product):
+    """The dense configuration (8192 x 4096 x 4096): every output element of
+    one product against the oracle's own dual-axis quantisation and binary64
+    product of the same BF16 inputs."""
+    d = W.dense("cuda")
+    X, Wt, dY = d["X"], d["W"], d["dY"]
+    M, K = X.shape
+    N = Wt.shape[0]
+    say(f"[gemm] dense config {product}, every element: M={M} N={N} K={K}")
+    qx, sx, qxt, sxt = mx.quant(X, "dual")
+    qw, sw, qwt, swt = mx.quant(Wt, "dual")
+    qd, sd, qdt, sdt = mx.quant(dY, "dual")
+    if product == "fprop":
+        got = mx.gemm(qx, sx, qw, sw, "fprop")
+    elif product == "dgrad":
+        got = mx.gemm(qd, sd, qwt, swt, "dgrad")
+    else:
+        got = mx.gemm(qdt, sdt, qxt, sxt, "wgrad")
+    torch.cuda.synchronize()
+    ox, osx, oxt, osxt = oracle.quant_dual(bits(X))
+    ow, osw, owt, oswt = oracle.quant_dual(bits(Wt))
+    od, osd, odt, osdt = oracle.quant_dual(bits(dY))
+    a, sa, b, sb = {"fprop": (ox, osx, ow, osw), "dgrad": (od, osd, owt, oswt),
+                    "wgrad": (odt, osdt, oxt, osxt)}[product]
+    ref, bound = oracle.gemm(a, sa, b, sb, oracle.BKIND_ROW)
+    assert_gemm(got, ref, bound, f"dense {product}, every element")
+
+
+@pytest.mark.parametrize("product", ["fprop1", "fprop2", "dgrad1", "dgrad2"])
+def test_block32_config_every_element(product):
+    """The 32x32-weight configuration (16384 tokens, 7168 <-> 2048): every
+    output element of one product against the oracle's own quantisation
+    (32x32 tiles for the weights, 1x32 rows for the activations) and binary64
+    product of the same BF16 inputs."""
+    d = W.block32("cuda")
+    W1, W2, X1, X2 = d["W1"], d["W2"], d["X1"], d["X2"]
+    say(f"[gemm] block32 config {product}, every element")
+    x, w, layout, bk, wsel = {
+        "fprop1": (X1, W1, "fprop", oracle.BKIND_TILE, 0),
+        "fprop2": (X2, W2, "fprop", oracle.BKIND_TILE, 0),
+        "dgrad1": (X2, W1, "dgrad", oracle.BKIND_TILE_T, 1),
+        "dgrad2": (X1, W2, "dgrad", oracle.BKIND_TILE_T, 1),
+    }[product]
+    qx, sx = mx.quant(x, "row")
+    qw, sw = mx.quant(w, "32x32")[:2]
+    got = mx.gemm(qx, sx, qw, sw, layout, "32x32")
+    torch.cuda.synchronize()
+    ox, osx = oracle.quant_row(bits(x))
+    ow, osw = oracle.quant_block32(bits(w))
+    ref, bound = oracle.gemm(ox, osx, ow, osw, bk)
+    assert_gemm(got, ref, bound, f"block32 {product}, every element")
