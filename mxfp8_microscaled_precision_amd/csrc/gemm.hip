@@ -42,7 +42,10 @@ namespace mx {
 // FAST: 0 = the general variant (any K a multiple of 32); 1 = the pipeline
 // with LDS-staged scales, K a multiple of 512; 2 = the same with a partial last
 // group of four K steps (K a multiple of 128, at least 512).
-template <int BMODE, int FAST, int FA = 0, int FB = 0, int OUT = 0>
+// TAIL: with FAST == 2, run only the real steps of the last group (the
+// persistent grouped kernel keeps the whole group, which needs fewer
+// registers there).
+template <int BMODE, int FAST, int FA = 0, int FB = 0, int OUT = 0, bool TAIL = true>
 struct Tile {
   static constexpr bool LDS_SCALES = FAST != 0;
   static constexpr bool PARTIAL = FAST == 2;
@@ -486,7 +489,10 @@ struct Tile {
       // prologue ends with the two prefetches of stage 2.
       prefetch(2, wave);
       read_frags<0>(st0, wm, wn, lane, f0a, f0b);
-      for (int64_t j = 0; 4 * j < nk; j++) {
+      // with PARTIAL && TAIL the last group runs only its real steps (the
+      // loads the skipped ones would issue lie past the end)
+      const int64_t kend = (PARTIAL && TAIL) ? 4 * last_g : nk;
+      for (int64_t j = 0; 4 * j < kend; j++) {
         const int64_t kt = 4 * j;
         lds_u8* scur = (j & 1) ? ss1 : ss0;
         lds_u8* snxt = (j & 1) ? ss0 : ss1;
@@ -498,6 +504,19 @@ struct Tile {
                    f0b, f1a, f1b, acc);
         step_ls<3>(st1, st0, snxt, snxt, kt + 3, wave, wm, wn, lane, sc_a, sc_b, nx_a, nx_b, f0a,
                    f0b, f1a, f1b, acc);
+      }
+      if (PARTIAL && TAIL) {
+        const int64_t j = last_g, kt = 4 * j, r = nk - kt;  // 1 .. 3 real steps
+        lds_u8* scur = (j & 1) ? ss1 : ss0;
+        lds_u8* snxt = (j & 1) ? ss0 : ss1;
+        step_ls<0>(st0, st1, scur, snxt, kt, wave, wm, wn, lane, sc_a, sc_b, nx_a, nx_b, f0a, f0b,
+                   f1a, f1b, acc);
+        if (r > 1)
+          step_ls<1>(st1, st0, scur, snxt, kt + 1, wave, wm, wn, lane, sc_a, sc_b, nx_a, nx_b, f0a,
+                     f0b, f1a, f1b, acc);
+        if (r > 2)
+          step_ls<2>(st0, st1, scur, snxt, kt + 2, wave, wm, wn, lane, sc_a, sc_b, nx_a, nx_b, f0a,
+                     f0b, f1a, f1b, acc);
       }
     } else {
       issue_stage(st0, 0, wave, lane);
@@ -623,7 +642,7 @@ grouped_gemm_kernel(int64_t G, const int64_t* __restrict__ offsets, int64_t T, i
     const int64_t gsz = (nmg - first) < GM_TILES ? (nmg - first) : GM_TILES;
     const int64_t in = local % (GM_TILES * nn);
     const int64_t mt = first + in % gsz, nt = in / gsz;
-    Tile<GEMM_B_ROW, FAST> tl;
+    Tile<GEMM_B_ROW, FAST, 0, 0, 0, false> tl;
     tl.a = a;
     tl.sa = sa;
     tl.b = b + g * N * K;
