@@ -19,8 +19,10 @@
 // B (four bytes per row per step), double-buffered, loaded with
 // buffer_load_dword ... lds where one instruction covers 16 rows x 4 steps
 // (16 cache lines instead of 64 for one step of 64 rows).  A workgroup runs
-// one tile; groups differ in length,
-// so the hardware's in-order dispatch balances the load, and consecutive
+// one tile; groups differ in length, so
+// the experts are taken longest first (up to 128 groups; the rank of each is
+// counted in LDS) and the hardware's in-order dispatch balances the rest by
+// giving the short tiles to the CUs that free up last; consecutive
 // workgroups (dealt round-robin to the 8 XCDs) take contiguous runs of one
 // expert's tile order per XCD so that tiles sharing rows share an L2.
 #include "gemm_common.h"
@@ -30,6 +32,7 @@ namespace mx {
 constexpr int W_STAGE = A_TILE + B_TILE;   // 64 KB of payload per K step
 constexpr int W_SCALES = (BM + BN) * 16;   // A then B scales of four K steps: 8 KB
 constexpr int W_MAX_GROUPS = 512;
+constexpr int W_LPT_GROUPS = 128;           // longest-first expert order up to this many groups
 
 struct WTile {
   u32x4 ra, rb, rsa, rsb;
@@ -191,10 +194,37 @@ grouped_wgrad_kernel(int64_t G, const int64_t* __restrict__ offsets, int64_t T, 
   __shared__ __attribute__((aligned(16))) uint8_t smem1[W_STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t sscale[2 * W_SCALES];
   __shared__ __attribute__((aligned(16))) uint8_t spf[2048];
+  __shared__ int64_t s_nk[W_LPT_GROUPS];
+  __shared__ int s_g;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nm = (M + BM - 1) / BM, nn = (N + BN - 1) / BN, per = nm * nn;
-  const int64_t t = blockIdx.x, g = t / per, u = t % per;
+  const int64_t t = blockIdx.x, pos_g = t / per, u = t % per;
+  // Which expert: with at most W_LPT_GROUPS groups, position pos_g of the
+  // experts ordered by K steps, longest first (ties by index), so the
+  // longest tiles start first and the short ones fill in at the end;
+  // otherwise expert pos_g.  Offsets are clamped as below.
+  int64_t g = pos_g;
+  if (G <= W_LPT_GROUPS) {
+    for (int64_t gg = threadIdx.x; gg < G; gg += NT) {
+      int64_t l = offsets[gg], r = offsets[gg + 1];
+      l = l < 0 ? 0 : (l > T ? T : l);
+      r = r < l ? l : (r > T ? T : r);
+      s_nk[gg] = (r - l + BK - 1) / BK;
+    }
+    __syncthreads();
+    for (int64_t gg = threadIdx.x; gg < G; gg += NT) {
+      const int64_t k = s_nk[gg];
+      int64_t rank = 0;
+      for (int64_t j = 0; j < G; j++) {
+        const int64_t kj = s_nk[j];
+        rank += (kj > k || (kj == k && j < gg)) ? 1 : 0;
+      }
+      if (rank == pos_g) s_g = (int)gg;
+    }
+    __syncthreads();
+    g = s_g;
+  }
   // XCD x = u % 8 takes the contiguous run x * per/8 .. of the group's order
   const int64_t run = per >> 3;
   const int64_t L = (per & 7) == 0 ? (u & 7) * run + (u >> 3) : u;

@@ -114,6 +114,8 @@ def _wgrad_case(sizes, M, N, seed):
     ([1000], 256, 512),
     ([130, 128, 129, 127], 256, 256),            # odd and even step counts
     ([600, 700, 850, 1100], 96, 96),             # 5, 6, 7, 9 steps: partial groups of four steps
+    ([128, 1000, 128, 1000, 0, 5, 1000], 64, 64),  # equal step counts: longest-first order ties
+    ([(7 * g) % 45 for g in range(130)], 64, 32),  # more groups than the longest-first order takes
 ])
 def test_wgrad_small_cases(sizes, M, N):
     say(f"[moe-bwd] wgrad sizes={sizes} M={M} N={N}")
