@@ -94,9 +94,17 @@ __device__ __forceinline__ int col_chunk(int c, int k) { return k ^ ((c >> 3) & 
 // Grouped column mode: the wave's 32 output rows r0 .. r0+31 (a block of
 // the padded token axis) -> first source row and number of real rows.  The
 // group is the last g with P_g <= r0, found by counting (one ballot per 64
-// groups, all offsets loaded at once); offsets are clamped into [0, T], so
+// groups, all offsets loaded at once, lane l of word k holding offsets[64k+l]);
+// offsets are clamped into [0, T], so
 // bad offsets give wrong blocks but only rows inside [0, T) are read.
 constexpr int GCOL_MAX_GROUPS = 512;
+
+// A wave-uniform lane's copy of a 64-bit register.
+__device__ __forceinline__ int64_t readlane64(int64_t v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)v >> 32), l);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 
 __device__ __forceinline__ void gcol_block(const int64_t* __restrict__ offsets, int64_t G,
                                            int64_t T, int64_t r0, int lane, int64_t& src,
@@ -105,7 +113,7 @@ __device__ __forceinline__ void gcol_block(const int64_t* __restrict__ offsets, 
 #pragma unroll
   for (int k = 0; k < GCOL_MAX_GROUPS / 64; k++) {
     const int64_t gg = 64 * k + lane;
-    o[k] = gg < G ? offsets[gg] : T;
+    o[k] = gg <= G ? offsets[gg] : T;
   }
   int cnt = 0;
 #pragma unroll
@@ -118,7 +126,15 @@ __device__ __forceinline__ void gcol_block(const int64_t* __restrict__ offsets, 
   nreal = 0;
   if (cnt == 0) return;
   const int64_t g = cnt - 1;
-  int64_t lo = offsets[g], hi = offsets[g + 1];
+  // offsets[g] and offsets[g + 1] from the lanes that loaded them (g is
+  // uniform); only offsets[512] lies past the loaded words
+  int64_t lo = 0, hi = 0;
+#pragma unroll
+  for (int k = 0; k < GCOL_MAX_GROUPS / 64; k++) {
+    if ((g >> 6) == k) lo = readlane64(o[k], (int)(g & 63));
+    if (((g + 1) >> 6) == k) hi = readlane64(o[k], (int)((g + 1) & 63));
+  }
+  if (g + 1 == GCOL_MAX_GROUPS) hi = offsets[g + 1];
   lo = lo < 0 ? 0 : (lo > T ? T : lo);
   hi = hi < lo ? lo : (hi > T ? T : hi);
   const int64_t first = 128 * (lo / 128 + g);

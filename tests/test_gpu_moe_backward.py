@@ -43,6 +43,8 @@ def test_quant_batched_equals_per_matrix(mode):
     ([300, 0, 0, 257, 1, 511, 96], 160),     # C not a multiple of the 128-column tile
     ([128, 256, 129], 96),
     ([0], 32),                               # no tokens at all: all zero blocks
+    ([(5 * g) % 37 for g in range(512)], 32),  # the most groups: the last group's end is offsets[512]
+    ([(3 * g) % 29 for g in range(65)], 64),   # a group boundary across two words of 64 offsets
 ])
 def test_quant_grouped_col_exact(sizes, C):
     off = _offsets(sizes)
