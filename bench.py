@@ -149,6 +149,25 @@ def gemm_traffic():
     return int(fields["traffic_bytes_per_launch"]), int(fields["algorithmic_bytes_per_launch"])
 
 
+CLOCK_PROFILE = os.path.join(ROOT, "profiles", "bench_step_clock_mfma_busy.md")
+
+
+def gemm_clock():
+    """Engine clock (GHz) and MFMA busy fraction of the 1x32 GEMM kernel under
+    the step from the committed counter summary, or (None, None) when it is
+    missing or was taken from a different kernel source."""
+    import hashlib
+    try:
+        text = open(CLOCK_PROFILE).read()
+        src = b"".join(open(f, "rb").read() for f in GEMM_SOURCES)
+    except OSError:
+        return None, None
+    fields = dict(re.findall(r"^(\w+): (\S+)$", text, re.M))
+    if fields.get("source_sha256") != hashlib.sha256(src).hexdigest():
+        return None, None
+    return float(fields["gemm_row_clock_ghz"]), float(fields["gemm_row_mfma_busy"])
+
+
 def build_workload(torch, W, layers):
     dev = "cuda"
     u8, bf = torch.uint8, torch.bfloat16
@@ -508,7 +527,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path).", file=sys.stderr)
+              "(the library has no multi-GPU path).", file=sys.stderr)
         sys.exit(2)
     import torch
     import mxfp8_microscaled_precision_amd as mx
@@ -571,6 +590,7 @@ def main():
     g = per["gemm"]
     g_rate = g["work"] / (g["ms"] * 1e-3) / 1e12
     traffic, alg_bytes = gemm_traffic()
+    clock_ghz, mfma_busy = gemm_clock()
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -609,6 +629,15 @@ def main():
                     for k, v in kernels.items()},
         "wall_s_timed": round(wall, 3),
     }
+    if clock_ghz is not None:
+        # the dense FP8 MFMA rate at the clock the chip holds under this
+        # kernel (from the committed counter run): 256 CUs x 4 SIMDs x 2048
+        # FLOP per cycle
+        at_clock = 256 * 4 * 2048 * clock_ghz * 1e9 / 1e12
+        out["roofline"]["clock_ghz_measured"] = clock_ghz
+        out["roofline"]["peak_at_measured_clock"] = round(at_clock, 1)
+        out["roofline"]["frac_at_measured_clock"] = round(g_rate / at_clock, 4)
+        out["roofline"]["mfma_busy_measured"] = mfma_busy
     print("[bench] copy rate, quantisation error", file=sys.stderr, flush=True)
     cg = copy_rate(torch)
     out["quant"]["d2d_copy_gbps"] = round(cg, 1)

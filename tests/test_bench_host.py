@@ -1,0 +1,38 @@
+"""Host-side pieces of bench.py (CPU only): the committed profile figures it
+reports are parsed and tied to the GEMM sources they were taken from, and a
+request for more than one GPU is refused before anything touches a device."""
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_profile_figures_parse_or_are_withheld():
+    traffic, alg = bench.gemm_traffic()
+    clock, busy = bench.gemm_clock()
+    # either both figures match the current GEMM sources, or they are withheld
+    assert (traffic is None) == (alg is None)
+    assert (clock is None) == (busy is None)
+    if traffic is not None:
+        assert traffic > alg > 0
+    if clock is not None:
+        assert 0.5 < clock < 2.5 and 0.0 < busy <= 1.0
+
+
+def test_figures_withheld_for_other_sources(tmp_path, monkeypatch):
+    src = tmp_path / "gemm.hip"
+    src.write_text("// a different kernel source\n")
+    monkeypatch.setattr(bench, "GEMM_SOURCES", [str(src)])
+    assert bench.gemm_traffic() == (None, None)
+    assert bench.gemm_clock() == (None, None)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
