@@ -179,6 +179,17 @@ mx_status mx_grouped_gemm(int64_t G, const int64_t* offsets, int64_t T, int64_t 
                           const void* a, const void* sa, const void* b, const void* sb, void* c,
                           hipStream_t stream);
 
+/* mx_grouped_gemm with the payload element type of each operand chosen
+ * (E4M3 or E5M2, the RFC's two FP8 dst_types, section 3.5.2.3): a_elem for
+ * the token rows a (e.g. E5M2 gradients in the MoE backward-data product),
+ * b_elem for the expert weights b.  Scales, layouts, rules and errors as
+ * mx_grouped_gemm, which is this call with E4M3 for both; an unknown
+ * element type returns MX_ERR_INVALID_ARG. */
+mx_status mx_grouped_gemm_elem(mx_elem_type a_elem, mx_elem_type b_elem, int64_t G,
+                               const int64_t* offsets, int64_t T, int64_t N, int64_t K,
+                               const void* a, const void* sa, const void* b, const void* sb,
+                               void* c, hipStream_t stream);
+
 /* mx_quant over a batch of equally shaped matrices, e.g. the per-expert
  * weights [G, rows, cols] of an MoE layer (the RFC quantises gate_up_proj /
  * down_proj of every expert, section 2.2).  x holds `batch` contiguous BF16

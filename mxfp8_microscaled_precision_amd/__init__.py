@@ -18,6 +18,7 @@ import os
 __all__ = [
     "MXError", "lib", "mx_device_check", "mx_arch_supported", "mx_status_string",
     "mx_last_error", "mx_quant", "mx_gemm", "mx_grouped_gemm", "mx_quant_elem", "mx_gemm_elem",
+    "mx_grouped_gemm_elem",
     "mx_gemm_quant", "gemm_quant",
     "mx_quant_batched",
     "mx_grouped_col_capacity", "mx_quant_grouped_col", "mx_grouped_gemm_wgrad", "quant", "gemm",
@@ -72,6 +73,8 @@ def lib() -> ctypes.CDLL:
         L.mx_quant_elem.argtypes = [c_int, c_int, vp, i64, i64, vp, vp, vp, vp, vp]
         L.mx_gemm_elem.restype = c_int
         L.mx_gemm_elem.argtypes = [c_int, c_int, c_int, c_int, i64, i64, i64, vp, vp, vp, vp, vp, vp]
+        L.mx_grouped_gemm_elem.restype = c_int
+        L.mx_grouped_gemm_elem.argtypes = [c_int, c_int, i64, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp]
         L.mx_gemm_quant.restype = c_int
         L.mx_gemm_quant.argtypes = [c_int, c_int, c_int, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
         L.mx_quant_batched.restype = c_int
@@ -116,6 +119,10 @@ def mx_gemm(layout, bkind, M, N, K, a, sa, b, sb, c, stream) -> int:
 
 def mx_grouped_gemm(G, offsets, T, N, K, a, sa, b, sb, c, stream) -> int:
     return lib().mx_grouped_gemm(G, offsets, T, N, K, a, sa, b, sb, c, stream)
+
+
+def mx_grouped_gemm_elem(a_elem, b_elem, G, offsets, T, N, K, a, sa, b, sb, c, stream) -> int:
+    return lib().mx_grouped_gemm_elem(a_elem, b_elem, G, offsets, T, N, K, a, sa, b, sb, c, stream)
 
 
 def mx_quant_elem(mode, elem, x, rows, cols, q, s, q_t, s_t, stream) -> int:
@@ -262,13 +269,16 @@ def gemm_quant(a, sa, b, sb, layout: str = "fprop", bscale: str = "1x32", out_el
     return q, s
 
 
-def grouped_gemm(offsets, a, sa, b, sb, out=None):
+def grouped_gemm(offsets, a, sa, b, sb, out=None, a_elem: str = "e4m3", b_elem: str = "e4m3"):
     """MoE grouped MXFP8 GEMM: rows offsets[g]:offsets[g+1] of a times b[g]^T.
 
     offsets int64 [G+1] on the device; a [T,K] u8 + sa [T,K/32];
-    b [G,N,K] u8 + sb [G,N,K/32]; returns BF16 [T,N].
+    b [G,N,K] u8 + sb [G,N,K/32]; returns BF16 [T,N].  a_elem / b_elem:
+    payload element types ("e4m3" or "e5m2").
     """
     torch = _torch()
+    if a_elem not in ELEM_TYPES or b_elem not in ELEM_TYPES:
+        raise ValueError(f"unknown element types {a_elem!r}, {b_elem!r}")
     _need(offsets, torch.int64, "offsets", 1)
     for t, n in ((a, "a"), (sa, "sa")):
         _need(t, torch.uint8, n, 2)
@@ -280,8 +290,8 @@ def grouped_gemm(offsets, a, sa, b, sb, out=None):
     if out is None:
         out = torch.empty((T, N), dtype=torch.bfloat16, device=a.device)
     _need(out, torch.bfloat16, "out", 2)
-    _check(mx_grouped_gemm(G, _ptr(offsets), T, N, K, _ptr(a), _ptr(sa), _ptr(b), _ptr(sb),
-                           _ptr(out), _stream(a.device)))
+    _check(mx_grouped_gemm_elem(ELEM_TYPES[a_elem], ELEM_TYPES[b_elem], G, _ptr(offsets), T, N, K,
+                                _ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(out), _stream(a.device)))
     return out
 
 

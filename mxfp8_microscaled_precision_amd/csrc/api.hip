@@ -230,10 +230,14 @@ mx_status mx_gemm_quant(mx_gemm_layout layout, mx_bscale_kind bkind, mx_elem_typ
   return MX_OK;
 }
 
-mx_status mx_grouped_gemm(int64_t G, const int64_t* offsets, int64_t T, int64_t N, int64_t K,
-                          const void* a, const void* sa, const void* b, const void* sb, void* c,
-                          hipStream_t stream) {
+mx_status mx_grouped_gemm_elem(mx_elem_type a_elem, mx_elem_type b_elem, int64_t G,
+                               const int64_t* offsets, int64_t T, int64_t N, int64_t K,
+                               const void* a, const void* sa, const void* b, const void* sb,
+                               void* c, hipStream_t stream) {
   g_err[0] = '\0';
+  if ((a_elem != MX_ELEM_E4M3 && a_elem != MX_ELEM_E5M2) ||
+      (b_elem != MX_ELEM_E4M3 && b_elem != MX_ELEM_E5M2))
+    return fail(MX_ERR_INVALID_ARG, "unknown element type (a %d, b %d)", (int)a_elem, (int)b_elem);
   if (G < 1 || G > 512) return fail(MX_ERR_INVALID_ARG, "group count %lld not in [1, 512]", (long long)G);
   if (T < 0 || N < 0 || K < 0) return fail(MX_ERR_INVALID_ARG, "negative grouped GEMM shape");
   if (mul_overflows(T, K) || mul_overflows(T, N) || mul_overflows(G, N) || mul_overflows(G * N, K))
@@ -256,10 +260,18 @@ mx_status mx_grouped_gemm(int64_t G, const int64_t* offsets, int64_t T, int64_t 
       std::lock_guard<std::mutex> lk(g_mu);
       cus = g_num_cus[dev];
     }
-    e = mx::launch_grouped_gemm(G, offsets, T, N, K, a, sa, b, sb, c, cus, stream);
+    e = mx::launch_grouped_gemm((int)a_elem, (int)b_elem, G, offsets, T, N, K, a, sa, b, sb, c, cus,
+                                stream);
   }
   if (e != hipSuccess) return hip_fail(e, "grouped GEMM kernel launch");
   return MX_OK;
+}
+
+mx_status mx_grouped_gemm(int64_t G, const int64_t* offsets, int64_t T, int64_t N, int64_t K,
+                          const void* a, const void* sa, const void* b, const void* sb, void* c,
+                          hipStream_t stream) {
+  return mx_grouped_gemm_elem(MX_ELEM_E4M3, MX_ELEM_E4M3, G, offsets, T, N, K, a, sa, b, sb, c,
+                              stream);
 }
 
 mx_status mx_quant_batched(mx_quant_mode mode, const void* x, int64_t batch, int64_t rows,

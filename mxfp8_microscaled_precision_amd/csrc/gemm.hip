@@ -590,7 +590,8 @@ gemm_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa,
 // device-side offsets (clamped into [0, T] and made non-decreasing, so bad
 // offsets can never address outside the operands) and walks it with a static
 // stride.  Tile t -> (group g, m tile within g, n tile).
-template <int FAST>
+// FA / FB: element formats of the token rows and of the expert weights.
+template <int FAST, int FA = 0, int FB = 0>
 __global__ void __launch_bounds__(NT)
 grouped_gemm_kernel(int64_t G, const int64_t* __restrict__ offsets, int64_t T, int64_t N,
                     int64_t K, const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa,
@@ -642,7 +643,7 @@ grouped_gemm_kernel(int64_t G, const int64_t* __restrict__ offsets, int64_t T, i
     const int64_t gsz = (nmg - first) < GM_TILES ? (nmg - first) : GM_TILES;
     const int64_t in = local % (GM_TILES * nn);
     const int64_t mt = first + in % gsz, nt = in / gsz;
-    Tile<GEMM_B_ROW, FAST, 0, 0, 0, false> tl;
+    Tile<GEMM_B_ROW, FAST, FA, FB, 0, false> tl;
     tl.a = a;
     tl.sa = sa;
     tl.b = b + g * N * K;
@@ -775,10 +776,11 @@ hipError_t launch_gemm_q(int bmode, int out_elem, int64_t M, int64_t N, int64_t 
   return hipGetLastError();
 }
 
-hipError_t launch_grouped_gemm(int64_t G, const int64_t* offsets, int64_t T, int64_t N, int64_t K,
-                               const void* a, const void* sa, const void* b, const void* sb,
-                               void* c, int num_cus, hipStream_t stream) {
+hipError_t launch_grouped_gemm(int a_elem, int b_elem, int64_t G, const int64_t* offsets, int64_t T,
+                               int64_t N, int64_t K, const void* a, const void* sa, const void* b,
+                               const void* sb, void* c, int num_cus, hipStream_t stream) {
   if (G > MAX_GROUPS) return hipErrorInvalidValue;
+  if ((a_elem != 0 && a_elem != 1) || (b_elem != 0 && b_elem != 1)) return hipErrorInvalidValue;
   const int64_t nn = (N + BN - 1) / BN;
   const int64_t upper = ((T + BM - 1) / BM + G) * nn;
   int64_t wgs = num_cus > 0 ? num_cus : 256;
@@ -786,13 +788,21 @@ hipError_t launch_grouped_gemm(int64_t G, const int64_t* offsets, int64_t T, int
   if (upper < wgs) wgs = (upper + 7) / 8 * 8;
   if (wgs < 8) wgs = 8;
   const int pipe = pipe_of(GEMM_B_ROW, N, K);
-#define MX_GROUPED_LAUNCH(P_)                                                                     \
-  hipLaunchKernelGGL(grouped_gemm_kernel<P_>, dim3((unsigned)wgs), dim3(NT), 0, stream, G, offsets, \
-                     T, N, K, (const uint8_t*)a, (const uint8_t*)sa, (const uint8_t*)b,            \
-                     (const uint8_t*)sb, (uint16_t*)c)
-  if (pipe == 1) MX_GROUPED_LAUNCH(1);
-  else if (pipe == 2) MX_GROUPED_LAUNCH(2);
-  else MX_GROUPED_LAUNCH(0);
+#define MX_GROUPED_LAUNCH(P_, FA_, FB_)                                                           \
+  hipLaunchKernelGGL((grouped_gemm_kernel<P_, FA_, FB_>), dim3((unsigned)wgs), dim3(NT), 0, stream, \
+                     G, offsets, T, N, K, (const uint8_t*)a, (const uint8_t*)sa,                    \
+                     (const uint8_t*)b, (const uint8_t*)sb, (uint16_t*)c)
+#define MX_GROUPED_FMT(P_)                                                                        \
+  do {                                                                                            \
+    if (a_elem == 0 && b_elem == 0) MX_GROUPED_LAUNCH(P_, 0, 0);                                  \
+    else if (a_elem == 1 && b_elem == 0) MX_GROUPED_LAUNCH(P_, 1, 0);                             \
+    else if (a_elem == 0 && b_elem == 1) MX_GROUPED_LAUNCH(P_, 0, 1);                             \
+    else MX_GROUPED_LAUNCH(P_, 1, 1);                                                             \
+  } while (0)
+  if (pipe == 1) MX_GROUPED_FMT(1);
+  else if (pipe == 2) MX_GROUPED_FMT(2);
+  else MX_GROUPED_FMT(0);
+#undef MX_GROUPED_FMT
 #undef MX_GROUPED_LAUNCH
   return hipGetLastError();
 }

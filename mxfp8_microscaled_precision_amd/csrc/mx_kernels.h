@@ -40,9 +40,11 @@ hipError_t launch_gemm_q(int bmode, int out_elem, int64_t M, int64_t N, int64_t 
                          const void* sa, const void* b, const void* sb, void* q, void* s,
                          hipStream_t stream);
 
-hipError_t launch_grouped_gemm(int64_t G, const int64_t* offsets, int64_t T, int64_t N, int64_t K,
-                               const void* a, const void* sa, const void* b, const void* sb,
-                               void* c, int num_cus, hipStream_t stream);
+// a_elem / b_elem: payload element types of the token rows and the expert
+// weights.
+hipError_t launch_grouped_gemm(int a_elem, int b_elem, int64_t G, const int64_t* offsets, int64_t T,
+                               int64_t N, int64_t K, const void* a, const void* sa, const void* b,
+                               const void* sb, void* c, int num_cus, hipStream_t stream);
 
 // Per-expert weight gradient c[g] [M, N] over group g's token columns of
 // a [M, cap] and b [N, cap] (grouped column layout above).

@@ -169,6 +169,10 @@ def test_elem_validation():
     assert mx.mx_quant_elem(0, 2, 1, 4, 32, 1, 1, 0, 0, 0) == INVALID
     assert mx.mx_gemm_elem(0, 0, 0, 5, 4, 4, 32, 1, 1, 1, 1, 1, 0) == INVALID
     assert mx.mx_gemm_elem(0, 0, 3, 0, 4, 4, 32, 1, 1, 1, 1, 1, 0) == INVALID
+    assert mx.mx_grouped_gemm_elem(2, 0, 1, 1, 4, 4, 32, 1, 1, 1, 1, 1, 0) == INVALID
+    assert mx.mx_grouped_gemm_elem(0, -1, 1, 1, 4, 4, 32, 1, 1, 1, 1, 1, 0) == INVALID
+    assert mx.mx_grouped_gemm_elem(1, 1, 1, 1, 4, 4, 48, 1, 1, 1, 1, 1, 0) == SHAPE
+    assert mx.mx_grouped_gemm_elem(1, 0, 0, 1, 4, 4, 32, 1, 1, 1, 1, 1, 0) == INVALID   # G = 0
     # the shape rules of the E4M3 entry points hold for E5M2
     assert mx.mx_quant_elem(0, 1, 1, 4, 33, 1, 1, 0, 0, 0) == SHAPE
     assert mx.mx_gemm_elem(0, 0, 1, 1, 4, 4, 48, 1, 1, 1, 1, 1, 0) == SHAPE

@@ -1,7 +1,8 @@
 """GPU parity of the E5M2 payload option against the oracle: quantisation
 bytes exact for every mode (including every BF16 magnitude under every scale
-exponent, special values, ragged tiles) and GEMMs with E5M2 and mixed
-E5M2/E4M3 operands within the GEMM tolerance."""
+exponent, special values, ragged tiles) and GEMMs (dense and the MoE
+grouped GEMM) with E5M2 and mixed E5M2/E4M3 operands within the GEMM
+tolerance."""
 import numpy as np
 import pytest
 import torch
@@ -103,3 +104,52 @@ def test_gemm_32x32_weight_with_e5m2_gradients(M, N, K):
     torch.cuda.synchronize()
     ref2, bound2 = oracle.gemm(qx, sx, qw2, sw2, oracle.BKIND_TILE, a_elem=E5M2, b_elem=E5M2)
     assert_gemm(c2, ref2, bound2, "32x32 fprop e5m2 x e5m2")
+
+
+def _offsets(sizes):
+    o = np.zeros(len(sizes) + 1, np.int64)
+    np.cumsum(sizes, out=o[1:])
+    return o
+
+
+@pytest.mark.parametrize("a_elem,b_elem", [("e5m2", "e4m3"), ("e5m2", "e5m2"), ("e4m3", "e5m2")])
+@pytest.mark.parametrize("sizes,N,K", [
+    ([70, 0, 300, 1, 129], 96, 160),      # general pipeline (K not a multiple of 128)
+    ([257, 31, 0, 400], 224, 640),        # five K steps: partial last group of four
+    ([513, 0, 2, 256], 288, 1024),        # K a multiple of 512
+])
+def test_grouped_gemm_mixed_elems(a_elem, b_elem, sizes, N, K):
+    """The MoE grouped GEMM with E5M2 token rows (e.g. gradients in the
+    backward-data product) and/or E5M2 expert weights: every row against the
+    oracle's element-typed GEMM of its group."""
+    ea, eb = oracle.ELEMS[a_elem], oracle.ELEMS[b_elem]
+    off = _offsets(sizes)
+    T, G = int(off[-1]), len(sizes)
+    qa, sa = oracle.quant_row(bits(W.normal_bf16((T, K), 0.01, T + K)), ea)
+    qb, sb = oracle.quant_row(bits(W.normal_bf16((G * N, K), 0.02, G + N + K)), eb)
+    qb, sb = qb.reshape(G, N, K), sb.reshape(G, N, K // 32)
+    say(f"[e5m2] grouped {a_elem} x {b_elem} sizes={sizes} N={N} K={K}")
+    c = mx.grouped_gemm(dev(off), dev(qa), dev(sa), dev(qb), dev(sb), a_elem=a_elem, b_elem=b_elem)
+    torch.cuda.synchronize()
+    ref = np.full((T, N), np.nan)
+    bound = np.full((T, N), np.nan)
+    for g in range(G):
+        lo, hi = int(off[g]), int(off[g + 1])
+        if hi > lo:
+            ref[lo:hi], bound[lo:hi] = oracle.gemm(qa[lo:hi], sa[lo:hi], qb[g], sb[g], a_elem=ea,
+                                                   b_elem=eb)
+    assert_gemm(c, ref, bound, f"grouped {a_elem}x{b_elem} sizes={sizes}")
+
+
+def test_grouped_gemm_e4m3_names_the_default():
+    """grouped_gemm with E4M3 named for both operands is mx_grouped_gemm."""
+    sizes, N, K = [100, 0, 37], 64, 512
+    off = _offsets(sizes)
+    T, G = int(off[-1]), len(sizes)
+    qa, sa = oracle.quant_row(bits(W.normal_bf16((T, K), 1.0, 5)))
+    qb, sb = oracle.quant_row(bits(W.normal_bf16((G * N, K), 0.02, 6)))
+    args = (dev(off), dev(qa), dev(sa), dev(qb.reshape(G, N, K)), dev(sb.reshape(G, N, K // 32)))
+    c0 = mx.grouped_gemm(*args)
+    c1 = mx.grouped_gemm(*args, a_elem="e4m3", b_elem="e4m3")
+    torch.cuda.synchronize()
+    assert torch.equal(c0, c1)
