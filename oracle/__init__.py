@@ -107,6 +107,16 @@ def lib():
         L.orc_quant_col_grouped.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                             ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
                                             ctypes.c_void_p]
+        L.orc_quant_col_grouped_elem.restype = ctypes.c_int
+        L.orc_quant_col_grouped_elem.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                                 ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        L.orc_grouped_gemm_wgrad_elem.restype = ctypes.c_int
+        L.orc_grouped_gemm_wgrad_elem.argtypes = [ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                                  ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                                  ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                  ctypes.c_void_p]
         L.orc_grouped_gemm_wgrad.restype = ctypes.c_int
         L.orc_grouped_gemm_wgrad.argtypes = [ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
                                              ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
@@ -258,11 +268,11 @@ def group_col(g: int, o_g: int) -> int:
     return 128 * (int(o_g) // 128 + int(g))
 
 
-def quant_col_grouped(x, offsets):
+def quant_col_grouped(x, offsets, elem=ELEM_E4M3):
     """MoE backward column blocks restarting at each group offset (R20).
 
     x [T,C] BF16 bits, offsets int64 [G+1] -> (q_t [C,cap] u8, s_t [C,cap/32] u8)
-    with cap = grouped_col_capacity(T, G)."""
+    with cap = grouped_col_capacity(T, G); elem is the payload element type."""
     x = _bits(x)
     offsets = _c(np.asarray(offsets, dtype=np.int64), np.int64)
     T, C = x.shape
@@ -270,7 +280,8 @@ def quant_col_grouped(x, offsets):
     cap = grouped_col_capacity(T, G)
     q = np.empty((C, cap), np.uint8)
     s = np.empty((C, cap // 32), np.uint8)
-    rc = lib().orc_quant_col_grouped(_ptr(x), T, C, G, _ptr(offsets), _ptr(q), _ptr(s))
+    rc = lib().orc_quant_col_grouped_elem(_ptr(x), T, C, G, _ptr(offsets), _elem(elem), _ptr(q),
+                                          _ptr(s))
     if rc:
         raise ValueError(f"oracle grouped column quantisation rejected the arguments (rc={rc})")
     return q, s
@@ -336,11 +347,13 @@ def grouped_gemm(offsets, a, sa, b, sb, want_bound: bool = True):
     return ref, bound
 
 
-def grouped_gemm_wgrad(offsets, a, sa, b, sb, want_bound: bool = True):
+def grouped_gemm_wgrad(offsets, a, sa, b, sb, want_bound: bool = True, a_elem=ELEM_E4M3,
+                       b_elem=ELEM_E4M3):
     """Per-expert weight gradient over each group's tokens (R20 layout).
 
     offsets int64 [G+1] with offsets[G] = T; a [M,cap] u8 + sa [M,cap/32];
-    b [N,cap] u8 + sb [N,cap/32]; returns ref/bound [G,M,N]."""
+    b [N,cap] u8 + sb [N,cap/32]; returns ref/bound [G,M,N].  a_elem / b_elem:
+    the payload element types."""
     offsets = _c(np.asarray(offsets, dtype=np.int64), np.int64)
     a = _c(a, np.uint8)
     sa = _c(sa, np.uint8)
@@ -351,8 +364,9 @@ def grouped_gemm_wgrad(offsets, a, sa, b, sb, want_bound: bool = True):
     M, N = a.shape[0], b.shape[0]
     ref = np.empty((G, M, N), np.float64)
     bound = np.empty((G, M, N), np.float64) if want_bound else None
-    rc = lib().orc_grouped_gemm_wgrad(G, _ptr(offsets), T, M, N, _ptr(a), _ptr(sa), _ptr(b),
-                                      _ptr(sb), _ptr(ref), _ptr(bound) if bound is not None else None)
+    rc = lib().orc_grouped_gemm_wgrad_elem(G, _ptr(offsets), T, M, N, _elem(a_elem), _elem(b_elem),
+                                           _ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(ref),
+                                           _ptr(bound) if bound is not None else None)
     if rc:
         raise ValueError(f"oracle grouped wgrad rejected the arguments (rc={rc})")
     return ref, bound

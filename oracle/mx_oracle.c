@@ -264,11 +264,6 @@ static uint8_t quant_block_elem(int elem, int n, const double *v, uint8_t *codes
     return (uint8_t)(e + 127);
 }
 
-/* E4M3 (the default element type). */
-static uint8_t quant_block(int n, const double *v, uint8_t *codes)
-{
-    return quant_block_elem(ELEM_E4M3, n, v, codes);
-}
 
 /* ------------------------------------------------------------------------ */
 /* Quantisation modes.  x is BF16 [R, C] row-major.                          */
@@ -472,12 +467,14 @@ static int offsets_ok(int64_t G, const int64_t *offsets, int64_t T)
 
 /* Column blocks per group (R20): x is BF16 [T][C]; q_t[C][cap] and
  * s_t[C][cap / 32] with cap = orc_grouped_col_capacity(T, G).  The last block
- * of a group is quantised from its remaining rows only.  Returns 0, or -1 on
- * bad offsets or C % 32 != 0. */
-int orc_quant_col_grouped(const uint16_t *x, int64_t T, int64_t C, int64_t G,
-                          const int64_t *offsets, uint8_t *q_t, uint8_t *s_t)
+ * of a group is quantised from its remaining rows only.  elem is the payload
+ * element type (E4M3 or E5M2, the block rule being the same with that
+ * type's largest finite value).  Returns 0, or -1 on bad offsets, an unknown
+ * element type or C % 32 != 0. */
+int orc_quant_col_grouped_elem(const uint16_t *x, int64_t T, int64_t C, int64_t G,
+                               const int64_t *offsets, int elem, uint8_t *q_t, uint8_t *s_t)
 {
-    if (!offsets_ok(G, offsets, T) || C % 32 != 0)
+    if (!offsets_ok(G, offsets, T) || C % 32 != 0 || (elem != ELEM_E4M3 && elem != ELEM_E5M2))
         return -1;
     const int64_t cap = orc_grouped_col_capacity(T, G), nbc = cap / 32;
     memset(q_t, 0, (size_t)(C * cap));
@@ -494,7 +491,7 @@ int orc_quant_col_grouped(const uint16_t *x, int64_t T, int64_t C, int64_t G,
                 const int n = (int)((rows - 32 * j) < 32 ? (rows - 32 * j) : 32);
                 for (int k = 0; k < n; k++)
                     v[k] = orc_bf16_value(x[(o + 32 * j + k) * C + c]);
-                s_t[c * nbc + P / 32 + j] = quant_block(n, v, codes);
+                s_t[c * nbc + P / 32 + j] = quant_block_elem(elem, n, v, codes);
                 memcpy(q_t + c * cap + P + 32 * j, codes, (size_t)n);
             }
         }
@@ -502,17 +499,27 @@ int orc_quant_col_grouped(const uint16_t *x, int64_t T, int64_t C, int64_t G,
     return 0;
 }
 
+int orc_quant_col_grouped(const uint16_t *x, int64_t T, int64_t C, int64_t G,
+                          const int64_t *offsets, uint8_t *q_t, uint8_t *s_t)
+{
+    return orc_quant_col_grouped_elem(x, T, C, G, offsets, ELEM_E4M3, q_t, s_t);
+}
+
 /* Per-expert weight gradient: for every group g,
  *   ref[g][m][n] = sum over the group's tokens t of A[m][t] * B[n][t]
  * where A = a [M][cap] (scales [M][cap/32]) and B = b [N][cap] are the
  * per-group column-quantised copies of (for MoE) the output gradient and the
  * expert input, token t of group g sitting at column P_g + (t - o_g) (R20).
- * An empty group gives ref = bound = 0.  ref/bound are [G][M][N]. */
-int orc_grouped_gemm_wgrad(int64_t G, const int64_t *offsets, int64_t T, int64_t M, int64_t N,
-                           const uint8_t *a, const uint8_t *sa, const uint8_t *b,
-                           const uint8_t *sb, double *ref, double *bound)
+ * An empty group gives ref = bound = 0.  ref/bound are [G][M][N].  a_elem /
+ * b_elem are the payload element types of A and B (E4M3 or E5M2); -1 on an
+ * unknown one. */
+int orc_grouped_gemm_wgrad_elem(int64_t G, const int64_t *offsets, int64_t T, int64_t M,
+                                int64_t N, int a_elem, int b_elem, const uint8_t *a,
+                                const uint8_t *sa, const uint8_t *b, const uint8_t *sb,
+                                double *ref, double *bound)
 {
-    if (!offsets_ok(G, offsets, T) || M < 0 || N < 0)
+    if (!offsets_ok(G, offsets, T) || M < 0 || N < 0 ||
+        (a_elem != ELEM_E4M3 && a_elem != ELEM_E5M2) || (b_elem != ELEM_E4M3 && b_elem != ELEM_E5M2))
         return -1;
     const int64_t cap = orc_grouped_col_capacity(T, G), nbc = cap / 32;
     for (int64_t g = 0; g < G; g++) {
@@ -524,8 +531,8 @@ int orc_grouped_gemm_wgrad(int64_t G, const int64_t *offsets, int64_t T, int64_t
                 double acc = 0.0, mag = 0.0;
                 for (int64_t t = 0; t < rows; t++) {
                     const int64_t k = P + t;
-                    double p = orc_e4m3_value(a[m * cap + k]) * orc_e8m0_value(sa[m * nbc + k / 32]) *
-                               orc_e4m3_value(b[n * cap + k]) * orc_e8m0_value(sb[n * nbc + k / 32]);
+                    double p = elem_value(a_elem, a[m * cap + k]) * orc_e8m0_value(sa[m * nbc + k / 32]) *
+                               elem_value(b_elem, b[n * cap + k]) * orc_e8m0_value(sb[n * nbc + k / 32]);
                     acc += p;
                     mag += fabs(p);
                 }
@@ -537,6 +544,15 @@ int orc_grouped_gemm_wgrad(int64_t G, const int64_t *offsets, int64_t T, int64_t
         }
     }
     return 0;
+}
+
+/* The same with E4M3 operands. */
+int orc_grouped_gemm_wgrad(int64_t G, const int64_t *offsets, int64_t T, int64_t M, int64_t N,
+                           const uint8_t *a, const uint8_t *sa, const uint8_t *b,
+                           const uint8_t *sb, double *ref, double *bound)
+{
+    return orc_grouped_gemm_wgrad_elem(G, offsets, T, M, N, ELEM_E4M3, ELEM_E4M3, a, sa, b, sb, ref,
+                                       bound);
 }
 
 int orc_num_threads(void)

@@ -176,3 +176,71 @@ def test_bad_offsets_rejected(orc):
     with pytest.raises(ValueError):
         orc.quant_col_grouped(W.bf16_bits(W.normal_bf16((10, 40), 1.0, 1)),
                               np.array([0, 10], np.int64))
+
+
+# --- E5M2 payload option ------------------------------------------------------
+
+def _deq_elem(q, s, dtype):
+    v = torch.from_numpy(np.ascontiguousarray(q)).view(dtype).to(torch.float64).numpy()
+    sc = torch.from_numpy(np.ascontiguousarray(np.repeat(s, 32, axis=1))).view(
+        torch.float8_e8m0fnu).to(torch.float64).numpy()
+    return v * sc
+
+
+@pytest.mark.parametrize("sizes,C", [
+    ([5, 0, 33, 1, 31, 32, 64, 0, 70], 64),
+    ([100], 32),
+    ([0, 7, 129], 96),
+])
+def test_grouped_col_e5m2_equals_col_of_padded_matrix(orc, sizes, C):
+    """E5M2 grouped column blocks = the (pinned) E5M2 column quantisation of
+    the zero-padded token matrix, as for E4M3."""
+    off = _offsets(sizes)
+    T = int(off[-1])
+    x = W.bf16_bits(W.normal_with_outliers_bf16((T, C), 1.0, 0.01, 100.0, 3 * sum(sizes) + C))
+    q, s = orc.quant_col_grouped(x, off, orc.ELEM_E5M2)
+    qp, sp = orc.quant_col(_padded(x, off), orc.ELEM_E5M2)
+    assert np.array_equal(q, qp)
+    assert np.array_equal(s, sp)
+    # and the E5M2 scales are those of the 57344 rceil rule: E4M3's minus 7
+    # wherever neither is clamped
+    _, s4 = orc.quant_col_grouped(x, off)
+    live = (s4 > 7) & (s4 != 0xFF)
+    assert np.array_equal(s[live].astype(int), s4[live].astype(int) - 7)
+
+
+@pytest.mark.parametrize("a_elem,b_elem", [("e5m2", "e4m3"), ("e4m3", "e5m2"), ("e5m2", "e5m2")])
+def test_wgrad_elem_matches_numpy_per_group(orc, a_elem, b_elem):
+    sizes, M, N = [5, 0, 33, 64, 1], 20, 12
+    off = _offsets(sizes)
+    T, G = int(off[-1]), len(sizes)
+    cap = orc.grouped_col_capacity(T, G)
+    rng = np.random.default_rng(7 + M + N)
+
+    def codes(rows, elem):
+        c = rng.integers(0, 256, size=(rows, cap), dtype=np.uint8)
+        if elem == "e5m2":
+            c[(c & 0x7C) == 0x7C] = 0x3C      # no Inf / NaN codes
+        else:
+            c[(c & 0x7F) == 0x7F] = 0x3C
+        return c
+
+    a, b = codes(M, a_elem), codes(N, b_elem)
+    sa = rng.integers(115, 135, size=(M, cap // 32), dtype=np.uint8)
+    sb = rng.integers(115, 135, size=(N, cap // 32), dtype=np.uint8)
+    ref, bound = orc.grouped_gemm_wgrad(off, a, sa, b, sb, a_elem=orc.ELEMS[a_elem],
+                                        b_elem=orc.ELEMS[b_elem])
+    dt = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
+    A, B = _deq_elem(a, sa, dt[a_elem]), _deq_elem(b, sb, dt[b_elem])
+    for g in range(G):
+        P, m = orc.group_col(g, off[g]), sizes[g]
+        want = A[:, P:P + m] @ B[:, P:P + m].T
+        mag = np.abs(A[:, P:P + m]) @ np.abs(B[:, P:P + m]).T
+        assert np.all(np.abs(ref[g] - want) <= 2.0 * max(m, 1) * 2.0 ** -53 * mag + 1e-300)
+        assert np.allclose(bound[g], mag, rtol=1e-12, atol=0)
+
+
+def test_unknown_elem_rejected(orc):
+    x = W.bf16_bits(W.normal_bf16((10, 32), 1.0, 1))
+    with pytest.raises(ValueError):
+        orc.quant_col_grouped(x, np.array([0, 10], np.int64), 2)
