@@ -225,6 +225,16 @@ int64_t mx_grouped_col_capacity(int64_t T, int64_t G);
 mx_status mx_quant_grouped_col(const void* x, int64_t T, int64_t C, int64_t G,
                                const int64_t* offsets, void* q_t, void* s_t, hipStream_t stream);
 
+/* mx_quant_grouped_col with the payload element type chosen (E4M3 or E5M2,
+ * the RFC's two FP8 dst_types, section 3.5.2.3; e.g. E5M2 gradients for the
+ * weight-gradient product).  The scale rule is rceil against the type's
+ * largest finite value, as in mx_quant_elem; layout, rules and errors as
+ * mx_quant_grouped_col (which is this call with E4M3); an unknown element
+ * type returns MX_ERR_INVALID_ARG. */
+mx_status mx_quant_grouped_col_elem(mx_elem_type elem, const void* x, int64_t T, int64_t C,
+                                    int64_t G, const int64_t* offsets, void* q_t, void* s_t,
+                                    hipStream_t stream);
+
 /* Per-expert weight gradient of the MoE backward (RFC section 2.2):
  *   c[g][m][n] = sum over the tokens t of group g of dY[t][m] * X[t][n]
  * from the grouped column quantisations a = (q_t, s_t) of dY [T, M] and
@@ -237,6 +247,16 @@ mx_status mx_quant_grouped_col(const void* x, int64_t T, int64_t C, int64_t G,
 mx_status mx_grouped_gemm_wgrad(int64_t G, const int64_t* offsets, int64_t T, int64_t M, int64_t N,
                                 const void* a, const void* sa, const void* b, const void* sb,
                                 void* c, hipStream_t stream);
+
+/* mx_grouped_gemm_wgrad with the payload element type of each operand
+ * chosen: a_elem for a (the gradient), b_elem for b (the input), each E4M3
+ * or E5M2 as its mx_quant_grouped_col_elem call wrote it.  Rules and errors
+ * as mx_grouped_gemm_wgrad (which is this call with E4M3 for both); an
+ * unknown element type returns MX_ERR_INVALID_ARG. */
+mx_status mx_grouped_gemm_wgrad_elem(mx_elem_type a_elem, mx_elem_type b_elem, int64_t G,
+                                     const int64_t* offsets, int64_t T, int64_t M, int64_t N,
+                                     const void* a, const void* sa, const void* b, const void* sb,
+                                     void* c, hipStream_t stream);
 
 #ifdef __cplusplus
 }

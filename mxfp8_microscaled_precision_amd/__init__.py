@@ -18,7 +18,7 @@ import os
 __all__ = [
     "MXError", "lib", "mx_device_check", "mx_arch_supported", "mx_status_string",
     "mx_last_error", "mx_quant", "mx_gemm", "mx_grouped_gemm", "mx_quant_elem", "mx_gemm_elem",
-    "mx_grouped_gemm_elem",
+    "mx_grouped_gemm_elem", "mx_quant_grouped_col_elem", "mx_grouped_gemm_wgrad_elem",
     "mx_gemm_quant", "gemm_quant",
     "mx_quant_batched",
     "mx_grouped_col_capacity", "mx_quant_grouped_col", "mx_grouped_gemm_wgrad", "quant", "gemm",
@@ -85,6 +85,11 @@ def lib() -> ctypes.CDLL:
         L.mx_quant_grouped_col.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp]
         L.mx_grouped_gemm_wgrad.restype = c_int
         L.mx_grouped_gemm_wgrad.argtypes = [i64, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp]
+        L.mx_quant_grouped_col_elem.restype = c_int
+        L.mx_quant_grouped_col_elem.argtypes = [c_int, vp, i64, i64, i64, vp, vp, vp, vp]
+        L.mx_grouped_gemm_wgrad_elem.restype = c_int
+        L.mx_grouped_gemm_wgrad_elem.argtypes = [c_int, c_int, i64, vp, i64, i64, i64, vp, vp, vp, vp,
+                                                 vp, vp]
         _lib = L
     return _lib
 
@@ -151,6 +156,15 @@ def mx_quant_grouped_col(x, T, C, G, offsets, q_t, s_t, stream) -> int:
 
 def mx_grouped_gemm_wgrad(G, offsets, T, M, N, a, sa, b, sb, c, stream) -> int:
     return lib().mx_grouped_gemm_wgrad(G, offsets, T, M, N, a, sa, b, sb, c, stream)
+
+
+def mx_quant_grouped_col_elem(elem, x, T, C, G, offsets, q_t, s_t, stream) -> int:
+    return lib().mx_quant_grouped_col_elem(elem, x, T, C, G, offsets, q_t, s_t, stream)
+
+
+def mx_grouped_gemm_wgrad_elem(a_elem, b_elem, G, offsets, T, M, N, a, sa, b, sb, c, stream) -> int:
+    return lib().mx_grouped_gemm_wgrad_elem(a_elem, b_elem, G, offsets, T, M, N, a, sa, b, sb, c,
+                                            stream)
 
 
 def _check(status: int):
@@ -330,12 +344,15 @@ def grouped_col_capacity(T: int, G: int) -> int:
     return cap
 
 
-def quant_grouped_col(x, offsets):
+def quant_grouped_col(x, offsets, elem: str = "e4m3"):
     """Per-expert column quantisation along the token axis (MoE backward):
     x BF16 [T, C], offsets int64 [G+1] on the device ->
     (q_t [C, cap] u8, s_t [C, cap/32] u8), cap = grouped_col_capacity(T, G);
-    group g's tokens at columns 128 (offsets[g] // 128 + g) on."""
+    group g's tokens at columns 128 (offsets[g] // 128 + g) on.  elem: the
+    payload element type ("e4m3" or "e5m2")."""
     torch = _torch()
+    if elem not in ELEM_TYPES:
+        raise ValueError(f"unknown element type {elem!r}")
     _need(x, torch.bfloat16, "x", 2)
     _need(offsets, torch.int64, "offsets", 1)
     T, C = x.shape
@@ -343,16 +360,20 @@ def quant_grouped_col(x, offsets):
     cap = grouped_col_capacity(T, G)
     qt = torch.empty((C, cap), dtype=torch.uint8, device=x.device)
     st = torch.empty((C, cap // 32), dtype=torch.uint8, device=x.device)
-    _check(mx_quant_grouped_col(_ptr(x), T, C, G, _ptr(offsets), _ptr(qt), _ptr(st),
-                                _stream(x.device)))
+    _check(mx_quant_grouped_col_elem(ELEM_TYPES[elem], _ptr(x), T, C, G, _ptr(offsets), _ptr(qt),
+                                     _ptr(st), _stream(x.device)))
     return qt, st
 
 
-def grouped_gemm_wgrad(offsets, T: int, a, sa, b, sb, out=None):
+def grouped_gemm_wgrad(offsets, T: int, a, sa, b, sb, out=None, a_elem: str = "e4m3",
+                       b_elem: str = "e4m3"):
     """Per-expert weight gradient: out[g] = A_g * B_g^T over group g's token
     columns of a [M, cap] and b [N, cap] (both from ``quant_grouped_col`` with
-    the same offsets); returns BF16 [G, M, N]."""
+    the same offsets); returns BF16 [G, M, N].  a_elem / b_elem: the payload
+    element types of a and b."""
     torch = _torch()
+    if a_elem not in ELEM_TYPES or b_elem not in ELEM_TYPES:
+        raise ValueError(f"unknown element types {a_elem!r}, {b_elem!r}")
     _need(offsets, torch.int64, "offsets", 1)
     for t, n in ((a, "a"), (sa, "sa"), (b, "b"), (sb, "sb")):
         _need(t, torch.uint8, n, 2)
@@ -366,8 +387,9 @@ def grouped_gemm_wgrad(offsets, T: int, a, sa, b, sb, out=None):
     _need(out, torch.bfloat16, "out", 3)
     if tuple(out.shape) != (G, M, N):
         raise ValueError(f"out must be [{G}, {M}, {N}]")
-    _check(mx_grouped_gemm_wgrad(G, _ptr(offsets), T, M, N, _ptr(a), _ptr(sa), _ptr(b), _ptr(sb),
-                                 _ptr(out), _stream(a.device)))
+    _check(mx_grouped_gemm_wgrad_elem(ELEM_TYPES[a_elem], ELEM_TYPES[b_elem], G, _ptr(offsets), T, M,
+                                      N, _ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(out),
+                                      _stream(a.device)))
     return out
 
 

@@ -323,9 +323,12 @@ int64_t mx_grouped_col_capacity(int64_t T, int64_t G) {
   return 128 * (T / 128 + G);
 }
 
-mx_status mx_quant_grouped_col(const void* x, int64_t T, int64_t C, int64_t G,
-                               const int64_t* offsets, void* q_t, void* s_t, hipStream_t stream) {
+mx_status mx_quant_grouped_col_elem(mx_elem_type elem, const void* x, int64_t T, int64_t C,
+                                    int64_t G, const int64_t* offsets, void* q_t, void* s_t,
+                                    hipStream_t stream) {
   g_err[0] = '\0';
+  if (elem != MX_ELEM_E4M3 && elem != MX_ELEM_E5M2)
+    return fail(MX_ERR_INVALID_ARG, "unknown element type %d", (int)elem);
   if (G < 1 || G > 512) return fail(MX_ERR_INVALID_ARG, "group count %lld not in [1, 512]", (long long)G);
   if (T < 0 || C < 0) return fail(MX_ERR_INVALID_ARG, "negative shape [%lld, %lld]", (long long)T,
                                   (long long)C);
@@ -342,15 +345,24 @@ mx_status mx_quant_grouped_col(const void* x, int64_t T, int64_t C, int64_t G,
   int dev;
   mx_status st = current_device(&dev);
   if (st != MX_OK) return st;
-  hipError_t e = mx::launch_quant_grouped_col(x, T, C, G, offsets, cap, q_t, s_t, stream);
+  hipError_t e = mx::launch_quant_grouped_col(x, T, C, G, offsets, cap, q_t, s_t, (int)elem, stream);
   if (e != hipSuccess) return hip_fail(e, "grouped column quantisation kernel launch");
   return MX_OK;
 }
 
-mx_status mx_grouped_gemm_wgrad(int64_t G, const int64_t* offsets, int64_t T, int64_t M, int64_t N,
-                                const void* a, const void* sa, const void* b, const void* sb,
-                                void* c, hipStream_t stream) {
+mx_status mx_quant_grouped_col(const void* x, int64_t T, int64_t C, int64_t G,
+                               const int64_t* offsets, void* q_t, void* s_t, hipStream_t stream) {
+  return mx_quant_grouped_col_elem(MX_ELEM_E4M3, x, T, C, G, offsets, q_t, s_t, stream);
+}
+
+mx_status mx_grouped_gemm_wgrad_elem(mx_elem_type a_elem, mx_elem_type b_elem, int64_t G,
+                                     const int64_t* offsets, int64_t T, int64_t M, int64_t N,
+                                     const void* a, const void* sa, const void* b, const void* sb,
+                                     void* c, hipStream_t stream) {
   g_err[0] = '\0';
+  if ((a_elem != MX_ELEM_E4M3 && a_elem != MX_ELEM_E5M2) ||
+      (b_elem != MX_ELEM_E4M3 && b_elem != MX_ELEM_E5M2))
+    return fail(MX_ERR_INVALID_ARG, "unknown element type (a %d, b %d)", (int)a_elem, (int)b_elem);
   if (G < 1 || G > 512) return fail(MX_ERR_INVALID_ARG, "group count %lld not in [1, 512]", (long long)G);
   if (T < 0 || M < 0 || N < 0) return fail(MX_ERR_INVALID_ARG, "negative grouped wgrad shape");
   const int64_t cap = mx_grouped_col_capacity(T, G);
@@ -363,9 +375,17 @@ mx_status mx_grouped_gemm_wgrad(int64_t G, const int64_t* offsets, int64_t T, in
   int dev;
   mx_status st = current_device(&dev);
   if (st != MX_OK) return st;
-  hipError_t e = mx::launch_grouped_wgrad(G, offsets, T, M, N, cap, a, sa, b, sb, c, stream);
+  hipError_t e = mx::launch_grouped_wgrad((int)a_elem, (int)b_elem, G, offsets, T, M, N, cap, a, sa,
+                                          b, sb, c, stream);
   if (e != hipSuccess) return hip_fail(e, "grouped wgrad kernel launch");
   return MX_OK;
+}
+
+mx_status mx_grouped_gemm_wgrad(int64_t G, const int64_t* offsets, int64_t T, int64_t M, int64_t N,
+                                const void* a, const void* sa, const void* b, const void* sb,
+                                void* c, hipStream_t stream) {
+  return mx_grouped_gemm_wgrad_elem(MX_ELEM_E4M3, MX_ELEM_E4M3, G, offsets, T, M, N, a, sa, b, sb,
+                                    c, stream);
 }
 
 }  // extern "C"

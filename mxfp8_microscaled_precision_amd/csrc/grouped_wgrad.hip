@@ -34,6 +34,8 @@ constexpr int W_SCALES = (BM + BN) * 16;   // A then B scales of four K steps: 8
 constexpr int W_MAX_GROUPS = 512;
 constexpr int W_LPT_GROUPS = 128;           // longest-first expert order up to this many groups
 
+// FA / FB: element formats of A (the gradient) and B (the input).
+template <int FA, int FB>
 struct WTile {
   u32x4 ra, rb, rsa, rsb;
   uint32_t voff_a, voff_b, rows32;  // chunk offset of this lane; offset of 32 rows
@@ -137,7 +139,7 @@ struct WTile {
                                        v8i* f0a, v8i* f0b, v8i* f1a, v8i* f1b,
                                        v16f (&acc)[4][4]) {
     read_frags<1>(cur, wm, wn, lane, f1a, f1b);
-    mma_tile<0>(f0a, f0b, sc_a, sc_b, acc);
+    mma_tile<0, FA, FB>(f0a, f0b, sc_a, sc_b, acc);
     interleave_ops<16, 0>();
     wait_vm_but_prefetch();
     __syncthreads();
@@ -147,7 +149,7 @@ struct WTile {
     issue(cur, kt + 2, wave);
     issue_scales((kt + 1) / 4 + 1, (int)((kt + 1) & 3), wave, lane);
     prefetch(kt + PF_DIST, wave);
-    mma_tile<1>(f1a, f1b, sc_a, sc_b, acc);
+    mma_tile<1, FA, FB>(f1a, f1b, sc_a, sc_b, acc);
     interleave_ops<24, 0>();
 #pragma unroll
     for (int f = 0; f < 4; f++) {
@@ -185,6 +187,7 @@ struct WTile {
   }
 };
 
+template <int FA, int FB>
 __global__ void __launch_bounds__(NT)
 grouped_wgrad_kernel(int64_t G, const int64_t* __restrict__ offsets, int64_t T, int64_t M,
                      int64_t N, int64_t ld, const uint8_t* __restrict__ a,
@@ -239,7 +242,7 @@ grouped_wgrad_kernel(int64_t G, const int64_t* __restrict__ offsets, int64_t T, 
   lo = lo < 0 ? 0 : (lo > T ? T : lo);
   hi = hi < lo ? lo : (hi > T ? T : hi);
   const int64_t P = 128 * (lo / 128 + g);
-  WTile w;
+  WTile<FA, FB> w;
   w.nk = (hi - lo + BK - 1) / BK;
   w.st0 = (lds_u8*)smem0;
   w.st1 = (lds_u8*)smem1;
@@ -259,15 +262,22 @@ grouped_wgrad_kernel(int64_t G, const int64_t* __restrict__ offsets, int64_t T, 
   store_tile_bf16(acc, c + g * M * N, N, m0, m_end, n0, N, wave & 1, wave >> 1, lane);
 }
 
-hipError_t launch_grouped_wgrad(int64_t G, const int64_t* offsets, int64_t T, int64_t M, int64_t N,
-                                int64_t cap, const void* a, const void* sa, const void* b,
-                                const void* sb, void* c, hipStream_t stream) {
+hipError_t launch_grouped_wgrad(int a_elem, int b_elem, int64_t G, const int64_t* offsets, int64_t T,
+                                int64_t M, int64_t N, int64_t cap, const void* a, const void* sa,
+                                const void* b, const void* sb, void* c, hipStream_t stream) {
   if (G < 1 || G > W_MAX_GROUPS || cap % BK != 0) return hipErrorInvalidValue;
+  if ((a_elem != 0 && a_elem != 1) || (b_elem != 0 && b_elem != 1)) return hipErrorInvalidValue;
   const int64_t tiles = G * ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL(grouped_wgrad_kernel, dim3((unsigned)tiles), dim3(NT), 0, stream, G, offsets, T,
-                     M, N, cap, (const uint8_t*)a, (const uint8_t*)sa, (const uint8_t*)b,
-                     (const uint8_t*)sb, (uint16_t*)c);
+#define MX_WGRAD_LAUNCH(FA_, FB_)                                                                 \
+  hipLaunchKernelGGL((grouped_wgrad_kernel<FA_, FB_>), dim3((unsigned)tiles), dim3(NT), 0, stream, \
+                     G, offsets, T, M, N, cap, (const uint8_t*)a, (const uint8_t*)sa,            \
+                     (const uint8_t*)b, (const uint8_t*)sb, (uint16_t*)c)
+  if (a_elem == 0 && b_elem == 0) MX_WGRAD_LAUNCH(0, 0);
+  else if (a_elem == 1 && b_elem == 0) MX_WGRAD_LAUNCH(1, 0);
+  else if (a_elem == 0 && b_elem == 1) MX_WGRAD_LAUNCH(0, 1);
+  else MX_WGRAD_LAUNCH(1, 1);
+#undef MX_WGRAD_LAUNCH
   return hipGetLastError();
 }
 

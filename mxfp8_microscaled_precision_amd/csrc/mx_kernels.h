@@ -20,7 +20,7 @@ hipError_t launch_quant_tile(int mode, const void* x, int64_t R, int64_t C, void
 // x [T, C]; q_t [C, cap], s_t [C, cap/32] with cap = 128 (T / 128 + G).
 hipError_t launch_quant_grouped_col(const void* x, int64_t T, int64_t C, int64_t G,
                                     const int64_t* offsets, int64_t cap, void* qt, void* st,
-                                    hipStream_t stream);
+                                    int elem, hipStream_t stream);
 
 // B operand layouts of the GEMM.
 enum GemmB {
@@ -48,9 +48,9 @@ hipError_t launch_grouped_gemm(int a_elem, int b_elem, int64_t G, const int64_t*
 
 // Per-expert weight gradient c[g] [M, N] over group g's token columns of
 // a [M, cap] and b [N, cap] (grouped column layout above).
-hipError_t launch_grouped_wgrad(int64_t G, const int64_t* offsets, int64_t T, int64_t M, int64_t N,
-                                int64_t cap, const void* a, const void* sa, const void* b,
-                                const void* sb, void* c, hipStream_t stream);
+hipError_t launch_grouped_wgrad(int a_elem, int b_elem, int64_t G, const int64_t* offsets, int64_t T,
+                                int64_t M, int64_t N, int64_t cap, const void* a, const void* sa,
+                                const void* b, const void* sb, void* c, hipStream_t stream);
 
 hipError_t launch_fill_zero_bf16(void* c, int64_t n, hipStream_t stream);
 

@@ -369,10 +369,10 @@ hipError_t launch_quant_tile(int mode, const void* x, int64_t R, int64_t C, void
 
 hipError_t launch_quant_grouped_col(const void* x, int64_t T, int64_t C, int64_t G,
                                     const int64_t* offsets, int64_t cap, void* qt, void* st,
-                                    hipStream_t stream) {
+                                    int elem, hipStream_t stream) {
   if (G < 1 || G > GCOL_MAX_GROUPS) return hipErrorInvalidValue;
   dim3 grid((unsigned)((cap + TILE_ROWS - 1) / TILE_ROWS), (unsigned)((C + TILE_COLS - 1) / TILE_COLS));
-  launch_tile<TILE_GCOL, ELEM_E4M3>(grid, x, cap, C, nullptr, nullptr, qt, st, G, offsets, T, stream);
+  launch_tile_elem<TILE_GCOL>(elem, grid, x, cap, C, nullptr, nullptr, qt, st, G, offsets, T, stream);
   return hipGetLastError();
 }
 

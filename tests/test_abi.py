@@ -173,6 +173,10 @@ def test_elem_validation():
     assert mx.mx_grouped_gemm_elem(0, -1, 1, 1, 4, 4, 32, 1, 1, 1, 1, 1, 0) == INVALID
     assert mx.mx_grouped_gemm_elem(1, 1, 1, 1, 4, 4, 48, 1, 1, 1, 1, 1, 0) == SHAPE
     assert mx.mx_grouped_gemm_elem(1, 0, 0, 1, 4, 4, 32, 1, 1, 1, 1, 1, 0) == INVALID   # G = 0
+    assert mx.mx_quant_grouped_col_elem(3, 1, 64, 32, 2, 1, 1, 1, 0) == INVALID
+    assert mx.mx_quant_grouped_col_elem(1, 1, 64, 33, 2, 1, 1, 1, 0) == SHAPE
+    assert mx.mx_grouped_gemm_wgrad_elem(0, 7, 2, 1, 64, 32, 32, 1, 1, 1, 1, 1, 0) == INVALID
+    assert mx.mx_grouped_gemm_wgrad_elem(1, 1, 0, 1, 64, 32, 32, 1, 1, 1, 1, 1, 0) == INVALID  # G = 0
     # the shape rules of the E4M3 entry points hold for E5M2
     assert mx.mx_quant_elem(0, 1, 1, 4, 33, 1, 1, 0, 0, 0) == SHAPE
     assert mx.mx_gemm_elem(0, 0, 1, 1, 4, 4, 48, 1, 1, 1, 1, 1, 0) == SHAPE

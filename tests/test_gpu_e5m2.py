@@ -153,3 +153,51 @@ def test_grouped_gemm_e4m3_names_the_default():
     c1 = mx.grouped_gemm(*args, a_elem="e4m3", b_elem="e4m3")
     torch.cuda.synchronize()
     assert torch.equal(c0, c1)
+
+
+@pytest.mark.parametrize("sizes,C", [
+    ([5, 0, 33, 1, 31, 32, 64, 0, 70], 64),
+    ([300, 0, 0, 257, 1, 511, 96], 160),
+    ([0], 32),
+])
+def test_grouped_col_e5m2_exact(sizes, C):
+    """MoE backward column blocks along the tokens with E5M2 payload: bytes
+    equal to the oracle's (blocks restart at each group offset, partial last
+    blocks, zero blocks between groups)."""
+    off = _offsets(sizes)
+    T = int(off[-1])
+    say(f"[e5m2] grouped col sizes={sizes} C={C}")
+    x = W.normal_with_outliers_bf16((max(T, 1), C), 1.0, 0.01, 100.0, 2 * T + C)[:T]
+    q, s = mx.quant_grouped_col(x.cuda(), dev(off), "e5m2")
+    torch.cuda.synchronize()
+    wq, ws = oracle.quant_col_grouped(bits(x) if T else np.zeros((0, C), np.uint16), off, E5M2)
+    assert_bytes(q, wq, "grouped e5m2 q_t")
+    assert_bytes(s, ws, "grouped e5m2 s_t")
+
+
+@pytest.mark.parametrize("a_elem,b_elem", [("e5m2", "e4m3"), ("e4m3", "e5m2"), ("e5m2", "e5m2")])
+@pytest.mark.parametrize("sizes,M,N", [
+    ([300, 0, 0, 257, 1, 511, 96], 288, 160),
+    ([600, 700, 850, 1100], 96, 96),
+])
+def test_grouped_wgrad_mixed_elems(a_elem, b_elem, sizes, M, N):
+    """The per-expert weight gradient from E5M2 (and mixed) grouped column
+    quantisations, the whole chain on the GPU, against the oracle quantising
+    and multiplying the same BF16 sources."""
+    off = _offsets(sizes)
+    T = int(off[-1])
+    dy = W.normal_bf16((T, M), 0.01, T + M)
+    xx = W.normal_bf16((T, N), 1.0, T + N + 1)
+    say(f"[e5m2] grouped wgrad {a_elem} x {b_elem} sizes={sizes} M={M} N={N}")
+    offd = dev(off)
+    qa, sa = mx.quant_grouped_col(dy.cuda(), offd, a_elem)
+    qb, sb = mx.quant_grouped_col(xx.cuda(), offd, b_elem)
+    c = mx.grouped_gemm_wgrad(offd, T, qa, sa, qb, sb, a_elem=a_elem, b_elem=b_elem)
+    torch.cuda.synchronize()
+    ea, eb = oracle.ELEMS[a_elem], oracle.ELEMS[b_elem]
+    oa, osa = oracle.quant_col_grouped(bits(dy), off, ea)
+    ob, osb = oracle.quant_col_grouped(bits(xx), off, eb)
+    assert_bytes(qa, oa, "wgrad operand a")
+    assert_bytes(qb, ob, "wgrad operand b")
+    ref, bound = oracle.grouped_gemm_wgrad(off, oa, osa, ob, osb, a_elem=ea, b_elem=eb)
+    assert_gemm(c, ref, bound, f"grouped wgrad {a_elem}x{b_elem} sizes={sizes}")
