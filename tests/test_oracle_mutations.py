@@ -7,7 +7,9 @@ pass the same tests.  The mistakes: a wrong rounding rule, a wrong
 saturation bound, a dropped sign, a wrong subnormal grid, wrong exponent
 biases, a strict instead of a non-strict scale bound, a signed amax, a
 reversed block, a dropped scale in the GEMM, a block that reaches past its
-group, groups sharing columns, and the E4M3 limit used for E5M2 scales.
+group, groups sharing columns, the E4M3 limit used for E5M2 scales, and the
+MoE backward's E5M2 paths falling back to E4M3 or mixing up the operands'
+element types.
 """
 import os
 import subprocess
@@ -76,6 +78,13 @@ MUTATIONS = [
     ("E5M2 scaled against 448",
      "return rceil_for(amax, 57344.0);", "return rceil_for(amax, 448.0);",
      [E5 + "::test_e5m2_layouts"]),
+    ("grouped column blocks ignore the element type",
+     "s_t[c * nbc + P / 32 + j] = quant_block_elem(elem, n, v, codes);",
+     "s_t[c * nbc + P / 32 + j] = quant_block_elem(ELEM_E4M3, n, v, codes);",
+     [MB + "::test_grouped_col_e5m2_equals_col_of_padded_matrix"]),
+    ("weight gradient decodes B with A's element type",
+     "elem_value(b_elem, b[n * cap + k])", "elem_value(a_elem, b[n * cap + k])",
+     [MB + "::test_wgrad_elem_matches_numpy_per_group"]),
 ]
 
 
