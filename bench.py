@@ -513,14 +513,20 @@ def cpu_baseline(W, x_dev, w_dev, budget_s):
     t0 = time.perf_counter()
     qa, sa, _, _ = oracle.quant_dual(xb)
     qb, sb, _, _ = oracle.quant_dual(wb)
+    t1 = time.perf_counter()
     oracle.gemm(qa, sa, qb, sb)
-    dt = time.perf_counter() - t0
+    t2 = time.perf_counter()
+    dt = t2 - t0
     flops = 2.0 * m * n * H
+    quant_bytes = 4.0625 * (m + n) * H          # dual-axis: 2 B read, 2 + 2/32 B written
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": nthreads,
             "kind": "oracle",
             "sample": f"dual-axis quantisation of {m} token rows and {n} weight rows (K={H}) of "
                       f"the up projection, then the binary64 GEMM of the {m}x{n} fprop outputs; "
-                      f"{dt:.1f} s"}
+                      f"{dt:.1f} s",
+            # the two parts of the same sample, each in its own unit
+            "quant_gbps": round(quant_bytes / max(t1 - t0, 1e-9) / 1e9, 3),
+            "gemm_tflops": round(flops / max(t2 - t1, 1e-9) / 1e12, 6)}
 
 
 def main():
