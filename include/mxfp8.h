@@ -19,6 +19,9 @@
  *     Validation errors mirror the ValueError the pages raise for an
  *     unsupported block size or recipe (MindSpeed RFC "add MXFP8-32x32
  *     quantisation support to FSDP", sections 3.4 and 3.5.2.1).
+ *   - A shape whose launch grid would reach 2^32 work-items in one
+ *     dimension (far beyond any tensor that fits in device memory) returns
+ *     MX_ERR_UNSUPPORTED_SHAPE rather than launching a truncated grid.
  *   - The current device must be gfx950; otherwise calls return
  *     MX_ERR_UNSUPPORTED_DEVICE (the pages' init-time hardware gate:
  *     torchtitan-npu MXFP8/HiF8 tutorial, "hardware requirement").

@@ -62,6 +62,15 @@ mx_status current_device(int* dev) {
 
 bool mul_overflows(int64_t a, int64_t b) { return a != 0 && b > INT64_MAX / a; }
 
+// A launch grid holds fewer than 2^32 work-items per dimension: `tiles`
+// workgroups of 256 threads (one per 256 x 256 output tile).
+bool grid_too_large(int64_t tiles) { return tiles >= (int64_t(1) << 32) / 256; }
+
+int64_t gemm_tiles(int64_t M, int64_t N) { return ((M + 255) / 256) * ((N + 255) / 256); }
+
+// The 2-D quantisation grid: one 512-thread workgroup per 128-row tile in x.
+bool row_tiles_too_large(int64_t R) { return ((R + 127) / 128) * 512 >= (int64_t(1) << 32); }
+
 // The GEMM kernels address a 256-row tile with 32-bit offsets (rows * K or
 // rows * cap bytes, out-of-range loads flagged by bit 31).
 constexpr int64_t K_LIMIT = (int64_t(1) << 31) / 256;
@@ -119,6 +128,8 @@ mx_status mx_quant_elem(mx_quant_mode mode, mx_elem_type elem, const void* x, in
     return fail(MX_ERR_UNSUPPORTED_SHAPE, "rows %lld is not a multiple of 32", (long long)rows);
   if (mode != MX_QUANT_ROW_1x32 && (cols + 127) / 128 > 65535)
     return fail(MX_ERR_UNSUPPORTED_SHAPE, "cols %lld exceeds the column-tile grid", (long long)cols);
+  if (mode != MX_QUANT_ROW_1x32 && row_tiles_too_large(rows))
+    return fail(MX_ERR_UNSUPPORTED_SHAPE, "rows %lld exceed the row-tile grid", (long long)rows);
   if (rows == 0 || cols == 0) return MX_OK;
   if (!x) return fail(MX_ERR_INVALID_ARG, "x is NULL");
   if (need_row && (!q || !s)) return fail(MX_ERR_INVALID_ARG, "q and s are required for this mode");
@@ -163,6 +174,9 @@ mx_status mx_gemm_elem(mx_gemm_layout layout, mx_bscale_kind bkind, mx_elem_type
   if (K % 32 != 0) return fail(MX_ERR_UNSUPPORTED_SHAPE, "K %lld is not a multiple of 32", (long long)K);
   if (K >= K_LIMIT)
     return fail(MX_ERR_UNSUPPORTED_SHAPE, "K %lld too large for 32-bit tile offsets", (long long)K);
+  if (grid_too_large(gemm_tiles(M, N)))
+    return fail(MX_ERR_UNSUPPORTED_SHAPE, "%lld x %lld output tiles exceed one launch grid",
+                (long long)M, (long long)N);
   if (bkind == MX_BSCALE_32x32 && layout == MX_GEMM_DGRAD && (K + 256) * N >= (int64_t(1) << 31))
     return fail(MX_ERR_UNSUPPORTED_SHAPE, "transposed 32x32 weight of %lld x %lld bytes too large",
                 (long long)K, (long long)N);
@@ -214,6 +228,9 @@ mx_status mx_gemm_quant(mx_gemm_layout layout, mx_bscale_kind bkind, mx_elem_typ
                 (long long)N);
   if (K >= K_LIMIT)
     return fail(MX_ERR_UNSUPPORTED_SHAPE, "K %lld too large for 32-bit tile offsets", (long long)K);
+  if (grid_too_large(gemm_tiles(M, N)))
+    return fail(MX_ERR_UNSUPPORTED_SHAPE, "%lld x %lld output tiles exceed one launch grid",
+                (long long)M, (long long)N);
   if (bkind == MX_BSCALE_32x32 && layout == MX_GEMM_DGRAD && (K + 256) * N >= (int64_t(1) << 31))
     return fail(MX_ERR_UNSUPPORTED_SHAPE, "transposed 32x32 weight of %lld x %lld bytes too large",
                 (long long)K, (long long)N);
@@ -296,6 +313,11 @@ mx_status mx_quant_batched(mx_quant_mode mode, const void* x, int64_t batch, int
   if (mode != MX_QUANT_ROW_1x32 && (cols + 127) / 128 > 65535)
     return fail(MX_ERR_UNSUPPORTED_SHAPE, "cols %lld exceeds the column-tile grid", (long long)cols);
   if (batch == 0 || rows == 0 || cols == 0) return MX_OK;
+  // 32x32 tiles run the stack as one [batch * rows, cols] matrix (no
+  // overflow: batch * rows * cols was checked above and cols > 0)
+  if (mode != MX_QUANT_ROW_1x32 &&
+      row_tiles_too_large(mode == MX_QUANT_BLOCK_32x32 ? batch * rows : rows))
+    return fail(MX_ERR_UNSUPPORTED_SHAPE, "rows %lld exceed the row-tile grid", (long long)rows);
   if (!x) return fail(MX_ERR_INVALID_ARG, "x is NULL");
   if (need_row && (!q || !s)) return fail(MX_ERR_INVALID_ARG, "q and s are required for this mode");
   if (need_col && (!q_t || !s_t))
@@ -370,6 +392,9 @@ mx_status mx_grouped_gemm_wgrad_elem(mx_elem_type a_elem, mx_elem_type b_elem, i
     return fail(MX_ERR_UNSUPPORTED_SHAPE, "token capacity %lld too large", (long long)cap);
   if (mul_overflows(M, cap) || mul_overflows(N, cap) || mul_overflows(M, N) || mul_overflows(G, M * N))
     return fail(MX_ERR_INVALID_ARG, "grouped wgrad shape too large");
+  if (grid_too_large(G * gemm_tiles(M, N)))
+    return fail(MX_ERR_UNSUPPORTED_SHAPE, "%lld experts x %lld x %lld output tiles exceed one launch grid",
+                (long long)G, (long long)M, (long long)N);
   if (M == 0 || N == 0) return MX_OK;
   if (!offsets || !c || !a || !sa || !b || !sb) return fail(MX_ERR_INVALID_ARG, "a pointer is NULL");
   int dev;

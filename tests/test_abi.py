@@ -63,6 +63,7 @@ INVALID, SHAPE = 1, 2
     ((0, 0, 4, 32, 1, 1, 0, 0, 0), INVALID),           # NULL x
     ((0, 1, 4, 32, 0, 1, 0, 0, 0), INVALID),           # NULL q
     ((2, 1, 32, 32, 1, 1, 0, 1, 0), INVALID),          # NULL q_t for dual
+    ((1, 1, 1 << 30, 32, 0, 0, 1, 1, 0), SHAPE),       # more row tiles than one launch grid
 ])
 def test_quant_validation(args, status):
     assert mx.mx_quant(*args) == status
@@ -83,6 +84,7 @@ def test_quant_empty_is_noop():
     ((0, 0, -4, 4, 32, 1, 1, 1, 1, 1, 0), INVALID),    # negative
     ((0, 0, 4, 4, 32, 1, 1, 1, 1, 0, 0), INVALID),     # NULL c
     ((0, 0, 4, 4, 32, 0, 1, 1, 1, 1, 0), INVALID),     # NULL a
+    ((0, 0, 1 << 26, 1 << 26, 32, 1, 1, 1, 1, 1, 0), SHAPE),  # more tiles than one launch grid
 ])
 def test_gemm_validation(args, status):
     assert mx.mx_gemm(*args) == status
@@ -119,6 +121,7 @@ def test_quant_rejects_unknown_mode_name():
     ((1, 1, 2, 33, 32, 0, 0, 1, 1, 0), SHAPE),         # column blocks need rows % 32
     ((0, 1, 2, 4, 40, 1, 1, 0, 0, 0), SHAPE),          # row blocks need cols % 32
     ((2, 1, 2, 32, 32, 1, 1, 0, 1, 0), INVALID),       # NULL q_t for dual
+    ((3, 1, 2, 1 << 29, 32, 1, 1, 0, 0, 0), SHAPE),    # stacked 32x32 rows beyond one launch grid
 ])
 def test_quant_batched_validation(args, status):
     assert mx.mx_quant_batched(*args) == status
@@ -155,6 +158,7 @@ def test_quant_grouped_col_validation(args, status):
     ((2, 0, 64, 32, 32, 1, 1, 1, 1, 1, 0), INVALID),   # NULL offsets
     ((2, 1, 64, 32, 32, 1, 1, 1, 1, 0, 0), INVALID),   # NULL c
     ((2, 1, 1 << 31, 32, 32, 1, 1, 1, 1, 1, 0), SHAPE),
+    ((512, 1, 64, 1 << 20, 1 << 20, 1, 1, 1, 1, 1, 0), SHAPE),  # more tiles than one launch grid
 ])
 def test_grouped_wgrad_validation(args, status):
     assert mx.mx_grouped_gemm_wgrad(*args) == status
