@@ -192,31 +192,48 @@ def test_block32_full_four_products():
                 _sample(T, 40, rng), _groups32(W2.shape[1], 2, rng))
 
 
-def test_stack_layer_full_six_products():
-    d = W.stack_layer(0, "cuda")
-    Xu, Xd, dYu, dYd, Wu, Wd = (d[k] for k in ("X_up", "X_dn", "dY_up", "dY_dn", "W_up", "W_dn"))
-    T, H = Xu.shape
-    F = Wu.shape[0]
-    say(f"[gemm] stack layer T={T} H={H} F={F}")
-    rng = np.random.default_rng(41)
-    # up projection H -> F
-    qx, sx, qxt, sxt = mx.quant(Xu, "dual")
-    qw, sw, qwt, swt = mx.quant(Wu, "dual")
-    qd, sd, qdt, sdt = mx.quant(dYu, "dual")
+def _corners(n):
+    """The first and last 32 indices: with the matching columns, the four
+    corner 32x32 tiles of a product."""
+    return np.concatenate([np.arange(min(32, n)), np.arange(max(n - 32, 0), n)])
+
+
+def _linear_layer_products(name, X, Wt, dY, rng, k):
+    """fprop, dgrad and wgrad of one linear layer at full size, each checked
+    on a sampled grid of rows x columns (random ones, the first and last, and
+    the four corner 32x32 tiles) against the oracle quantising and
+    multiplying the same BF16 sources."""
+    T, H = X.shape
+    F = Wt.shape[0]
+    qx, sx, qxt, sxt = mx.quant(X, "dual")
+    qw, sw, qwt, swt = mx.quant(Wt, "dual")
+    qd, sd, qdt, sdt = mx.quant(dY, "dual")
     Y = mx.gemm(qx, sx, qw, sw, "fprop")
     torch.cuda.synchronize()
-    _end_to_end("stack up fprop", Y, Xu, "row", Wu, "row", oracle.BKIND_ROW,
-                _sample(T, 24, rng), _sample(F, 24, rng))
+    _end_to_end(f"stack {name} fprop", Y, X, "row", Wt, "row", oracle.BKIND_ROW,
+                _sample(T, k, rng, _corners(T)), _sample(F, k, rng, _corners(F)))
     del Y
     dX = mx.gemm(qd, sd, qwt, swt, "dgrad")
     torch.cuda.synchronize()
-    _end_to_end("stack up dgrad", dX, dYu, "row", Wu, "col", oracle.BKIND_ROW,
-                _sample(T, 24, rng), _sample(H, 24, rng))
+    _end_to_end(f"stack {name} dgrad", dX, dY, "row", Wt, "col", oracle.BKIND_ROW,
+                _sample(T, k, rng, _corners(T)), _sample(H, k, rng, _corners(H)))
     del dX
     dW = mx.gemm(qdt, sdt, qxt, sxt, "wgrad")
     torch.cuda.synchronize()
-    _end_to_end("stack up wgrad", dW, dYu, "col", Xu, "col", oracle.BKIND_ROW,
-                _sample(F, 12, rng), _sample(H, 12, rng))
+    _end_to_end(f"stack {name} wgrad", dW, dY, "col", X, "col", oracle.BKIND_ROW,
+                _sample(F, k // 2, rng, _corners(F)), _sample(H, k // 2, rng, _corners(H)))
+    del dW
+
+
+def test_stack_layer_full_six_products():
+    """Both linear layers of one stack layer (7168 -> 18432 -> 7168 at 32768
+    tokens): the up projection's and the down projection's three products."""
+    d = W.stack_layer(0, "cuda")
+    Xu, Xd, dYu, dYd, Wu, Wd = (d[k] for k in ("X_up", "X_dn", "dY_up", "dY_dn", "W_up", "W_dn"))
+    say(f"[gemm] stack layer T={Xu.shape[0]} H={Xu.shape[1]} F={Wu.shape[0]}")
+    rng = np.random.default_rng(41)
+    _linear_layer_products("up", Xu, Wu, dYu, rng, 24)
+    _linear_layer_products("down", Xd, Wd, dYd, rng, 24)
 
 
 # --------------------------------------------------------------------------
