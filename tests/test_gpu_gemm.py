@@ -236,6 +236,34 @@ def test_stack_layer_full_six_products():
     _linear_layer_products("down", Xd, Wd, dYd, rng, 24)
 
 
+def test_stack_layer_full_32x32_variant():
+    """The 32x32-weight variant of the same stack layer: each weight
+    quantised once in 32x32 tiles, fprop with the tile scales and dgrad
+    reading the same FP8 weight transposed, for both projections (N up to
+    18432, i.e. more than 32 n-tiles: the other workgroup-to-tile map than
+    the 16384-token weight configuration uses)."""
+    d = W.stack_layer(0, "cuda")
+    T = d["X_up"].shape[0]
+    rng = np.random.default_rng(43)
+    for name, X, Wt, dY in (("up", d["X_up"], d["W_up"], d["dY_up"]),
+                            ("down", d["X_dn"], d["W_dn"], d["dY_dn"])):
+        F, H = Wt.shape
+        say(f"[gemm] stack 32x32 {name}: W {F}x{H}")
+        q32, s32 = mx.quant(Wt, "32x32")
+        qx, sx = mx.quant(X, "row")
+        Y = mx.gemm(qx, sx, q32, s32, "fprop", "32x32")
+        torch.cuda.synchronize()
+        _end_to_end(f"stack 32x32 {name} fprop", Y, X, "row", Wt, "tile", oracle.BKIND_TILE,
+                    _sample(T, 24, rng, _corners(T)), _groups32(F, 2, rng))
+        del Y, qx, sx
+        qd, sd = mx.quant(dY, "row")
+        dX = mx.gemm(qd, sd, q32, s32, "dgrad", "32x32")
+        torch.cuda.synchronize()
+        _end_to_end(f"stack 32x32 {name} dgrad", dX, dY, "row", Wt, "tile_t", oracle.BKIND_TILE_T,
+                    _sample(T, 24, rng, _corners(T)), _groups32(H, 2, rng))
+        del dX, qd, sd
+
+
 # --------------------------------------------------------------------------
 # Tile order: every tile written once, in both workgroup-to-tile maps
 # --------------------------------------------------------------------------
