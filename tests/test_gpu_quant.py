@@ -176,9 +176,20 @@ def _sampled_dual(x: torch.Tensor, what: str, nrows=64, ncols=64, seed=0):
 
 
 def test_stack_layer_full_sampled():
+    """Every tensor of one stack layer, dual-axis at full size, checked on
+    seeded rows and columns (a fixed seed per tensor)."""
     d = W.stack_layer(0, "cuda")
-    for name in ("X_up", "X_dn", "dY_up", "W_up"):
-        _sampled_dual(d[name], f"stack {name}", seed=hash(name) % 1000)
+    for seed, name in enumerate(("X_up", "X_dn", "dY_up", "dY_dn", "W_up", "W_dn")):
+        _sampled_dual(d[name], f"stack {name}", seed=100 + seed)
+    del d
+
+
+def test_stack_weights_full_32x32():
+    """The stack layer's two weights in 32x32 tiles (the weight-sharing
+    variant), every byte against the oracle."""
+    d = W.stack_layer(0, "cuda")
+    for name in ("W_up", "W_dn"):
+        _check_full(d[name], "32x32", f"stack {name}")
     del d
 
 
