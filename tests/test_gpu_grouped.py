@@ -87,6 +87,9 @@ def test_equals_dense_per_group():
 
 
 def test_moe_full_sampled():
+    """gate_up and down at full size: the first and last row of every
+    non-empty expert group plus 32 seeded rows, every column, against the
+    oracle quantising and multiplying the same BF16 sources."""
     d = W.moe("cuda")
     off = d["offsets"]
     offd = torch.from_numpy(off).cuda()
@@ -104,7 +107,7 @@ def test_moe_full_sampled():
         c = mx.grouped_gemm(offd, qa, sa, qb.reshape(G, N, K), sb.reshape(G, N, K // 32))
         torch.cuda.synchronize()
         ri = torch.from_numpy(rows).cuda()
-        cols = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, 64)])).astype(np.int64)
+        cols = np.arange(N, dtype=np.int64)   # every column of the sampled rows
         ci = torch.from_numpy(cols).cuda()
         # oracle: each sampled row times its expert's sampled weight rows,
         # quantised by the oracle from the BF16 sources
