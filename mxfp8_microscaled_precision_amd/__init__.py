@@ -200,6 +200,39 @@ def _need(t, dtype, name, ndim=None):
         raise ValueError(f"{name} must be contiguous")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+    # the library launches on the current device
+    if t.get_device() != torch.cuda.current_device():
+        raise ValueError(f"{name} is on cuda:{t.get_device()}, not on the current device "
+                         f"cuda:{torch.cuda.current_device()}")
+
+
+def _shape(t, shape, name):
+    """The library reads exactly the bytes the sizes describe, so every
+    operand must have them (a short tensor would be read past its end)."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {list(shape)}, got {list(t.shape)}")
+
+
+def _gemm_operands(a, sa, b, sb, layout, bscale):
+    """(M, N, K) of a dense GEMM call, after checking every operand's shape
+    against them (K % 32 and N % 32 for 32x32 tiles are left to the library,
+    which reports them as unsupported shapes)."""
+    M, K = a.shape
+    tiles = bscale == "32x32"
+    N = b.shape[1] if (tiles and layout == "dgrad") else b.shape[0]
+    if K % 32 == 0:
+        _shape(sa, (M, K // 32), "sa")
+        if not tiles:
+            _shape(b, (N, K), "b")
+            _shape(sb, (N, K // 32), "sb")
+        elif N % 32 == 0:
+            if layout == "dgrad":      # the shared weight [K, N], tiles along both
+                _shape(b, (K, N), "b")
+                _shape(sb, (K // 32, N // 32), "sb")
+            else:
+                _shape(b, (N, K), "b")
+                _shape(sb, (N // 32, K // 32), "sb")
+    return M, N, K
 
 
 def quant(x, mode: str = "row", elem: str = "e4m3"):
@@ -252,8 +285,7 @@ def gemm(a, sa, b, sb, layout: str = "fprop", bscale: str = "1x32", out=None,
         raise ValueError(f"unknown element types {a_elem!r}, {b_elem!r}")
     for t, n in ((a, "a"), (sa, "sa"), (b, "b"), (sb, "sb")):
         _need(t, torch.uint8, n, 2)
-    M, K = a.shape
-    N = b.shape[1] if (bscale == "32x32" and layout == "dgrad") else b.shape[0]
+    M, N, K = _gemm_operands(a, sa, b, sb, layout, bscale)
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
     _need(out, torch.bfloat16, "out", 2)
@@ -274,8 +306,7 @@ def gemm_quant(a, sa, b, sb, layout: str = "fprop", bscale: str = "1x32", out_el
         raise ValueError(f"unknown layout {layout!r}, B scale kind {bscale!r} or element {out_elem!r}")
     for t, n in ((a, "a"), (sa, "sa"), (b, "b"), (sb, "sb")):
         _need(t, torch.uint8, n, 2)
-    M, K = a.shape
-    N = b.shape[1] if (bscale == "32x32" and layout == "dgrad") else b.shape[0]
+    M, N, K = _gemm_operands(a, sa, b, sb, layout, bscale)
     q = torch.empty((M, N), dtype=torch.uint8, device=a.device)
     s = torch.empty((M, N // 32), dtype=torch.uint8, device=a.device)
     _check(mx_gemm_quant(GEMM_LAYOUTS[layout], BSCALE_KINDS[bscale], ELEM_TYPES[out_elem], M, N, K,
@@ -301,9 +332,16 @@ def grouped_gemm(offsets, a, sa, b, sb, out=None, a_elem: str = "e4m3", b_elem: 
     G = offsets.numel() - 1
     T, K = a.shape
     N = b.shape[1]
+    if G < 1:
+        raise ValueError("offsets must hold at least two entries (one group)")
+    if K % 32 == 0:
+        _shape(sa, (T, K // 32), "sa")
+        _shape(b, (G, N, K), "b")
+        _shape(sb, (G, N, K // 32), "sb")
     if out is None:
         out = torch.empty((T, N), dtype=torch.bfloat16, device=a.device)
     _need(out, torch.bfloat16, "out", 2)
+    _shape(out, (T, N), "out")
     _check(mx_grouped_gemm_elem(ELEM_TYPES[a_elem], ELEM_TYPES[b_elem], G, _ptr(offsets), T, N, K,
                                 _ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(out), _stream(a.device)))
     return out

@@ -337,3 +337,38 @@ def test_block32_config_every_element(product):
     ow, osw = oracle.quant_block32(bits(w))
     ref, bound = oracle.gemm(ox, osx, ow, osw, bk)
     assert_gemm(got, ref, bound, f"block32 {product}, every element")
+
+
+def test_binding_rejects_mismatched_operands():
+    """The binding derives the sizes from the tensors, and the library reads
+    exactly the bytes those sizes describe: operands whose shapes disagree
+    (a short B, wrong scale shapes, a wrong output) raise before any launch."""
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    a, sa = torch.zeros((64, 256), **u8), torch.zeros((64, 8), **u8)
+    b, sb = torch.zeros((96, 256), **u8), torch.zeros((96, 8), **u8)
+    mx.gemm(a, sa, b, sb)                                               # consistent: fine
+    bad = [
+        (a, sa, torch.zeros((96, 128), **u8), torch.zeros((96, 4), **u8), "fprop", "1x32"),  # short K
+        (a, torch.zeros((64, 4), **u8), b, sb, "fprop", "1x32"),            # sa for another K
+        (a, sa, b, torch.zeros((96, 4), **u8), "wgrad", "1x32"),            # sb for another K
+        (a, sa, b, sb, "fprop", "32x32"),                                   # row scales, not tiles [N/32, K/32]
+        (a, sa, torch.zeros((128, 96), **u8), torch.zeros((4, 2), **u8), "dgrad", "32x32"),  # weight [K, N]
+    ]
+    for args in bad:
+        with pytest.raises(ValueError):
+            mx.gemm(*args[:4], layout=args[4], bscale=args[5])
+        with pytest.raises(ValueError):
+            mx.gemm_quant(*args[:4], layout=args[4], bscale=args[5])
+    with pytest.raises(ValueError):
+        mx.gemm(a, sa, b, sb, out=torch.zeros((64, 64), dtype=torch.bfloat16, device="cuda"))
+    off = torch.tensor([0, 30, 64], dtype=torch.int64, device="cuda")
+    be, sbe = torch.zeros((2, 96, 256), **u8), torch.zeros((2, 96, 8), **u8)
+    mx.grouped_gemm(off, a, sa, be, sbe)                                # consistent: fine
+    for bb, ss in ((torch.zeros((3, 96, 256), **u8), torch.zeros((3, 96, 8), **u8)),  # 3 experts, 2 groups
+                   (torch.zeros((2, 96, 128), **u8), torch.zeros((2, 96, 4), **u8)),  # short K
+                   (be, torch.zeros((2, 96, 4), **u8))):                              # scales
+        with pytest.raises(ValueError):
+            mx.grouped_gemm(off, a, sa, bb, ss)
+    with pytest.raises(ValueError):
+        mx.grouped_gemm(off, a, sa, be, sbe, out=torch.zeros((64, 32), dtype=torch.bfloat16, device="cuda"))
+    torch.cuda.synchronize()
