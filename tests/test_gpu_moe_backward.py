@@ -78,23 +78,21 @@ def test_quant_grouped_col_special_values():
     assert_bytes(s, ws, "special s_t")
 
 
-def test_quant_grouped_col_full_moe_sampled_features():
-    """The MoE tokens [131072, 4096] over 64 Zipf-sized experts: every token
-    of 48 sampled features against the oracle (features are independent)."""
+def test_quant_grouped_col_full_moe():
+    """The MoE backward's per-group column quantisation at full size: the
+    tokens [131072, 4096] and the down-projection input [131072, 2048] over
+    64 Zipf-sized experts, every byte against the oracle."""
     d = W.moe("cuda")
     off = d["offsets"]
-    x = d["X"]
-    say(f"[moe-bwd] grouped col full X {tuple(x.shape)}")
-    q, s = mx.quant_grouped_col(x, dev(off))
-    torch.cuda.synchronize()
-    C = x.shape[1]
-    cols = np.unique(np.concatenate([[0, C - 1], np.random.default_rng(8).choice(
-        np.arange(1, C - 1), 62, replace=False)]))          # 64 features (a multiple of 32)
-    ci = torch.from_numpy(cols).cuda()
-    wq, ws = oracle.quant_col_grouped(bits(x.index_select(1, ci)), off)
-    assert_bytes(q.index_select(0, ci), wq, "full grouped q_t rows")
-    assert_bytes(s.index_select(0, ci), ws, "full grouped s_t rows")
-    del q, s
+    for name in ("X", "H"):
+        x = d[name]
+        say(f"[moe-bwd] grouped col full {name} {tuple(x.shape)}")
+        q, s = mx.quant_grouped_col(x, dev(off))
+        torch.cuda.synchronize()
+        wq, ws = oracle.quant_col_grouped(bits(x), off)
+        assert_bytes(q, wq, f"full grouped {name} q_t")
+        assert_bytes(s, ws, f"full grouped {name} s_t")
+        del q, s, wq, ws
 
 
 def _wgrad_case(sizes, M, N, seed):

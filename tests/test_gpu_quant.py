@@ -156,31 +156,12 @@ def test_block32_full():
     _check_full(d["X2"], "row", "block32 X2")
 
 
-def _sampled_dual(x: torch.Tensor, what: str, nrows=64, ncols=64, seed=0):
-    """Full-size dual quantisation checked on seeded rows and columns."""
-    R, C = x.shape
-    say(f"[quant] sampled dual {what} shape={tuple(x.shape)}")
-    q, s, qt, st = mx.quant(x, "dual")
-    torch.cuda.synchronize()
-    rng = np.random.default_rng(seed)
-    rows = np.unique(np.concatenate([[0, R - 1], rng.integers(0, R, nrows)]))
-    cols = np.unique(np.concatenate([[0, C - 1], rng.integers(0, C, ncols)]))
-    ri = torch.from_numpy(rows).cuda()
-    ci = torch.from_numpy(cols).cuda()
-    rq, rs = oracle.quant_row(bits(x.index_select(0, ri)))
-    assert_bytes(q.index_select(0, ri), rq, f"{what} q rows")
-    assert_bytes(s.index_select(0, ri), rs, f"{what} s rows")
-    cq, cs = oracle.quant_col(bits(x.index_select(1, ci)))
-    assert_bytes(qt.index_select(0, ci), cq, f"{what} q_t rows")
-    assert_bytes(st.index_select(0, ci), cs, f"{what} s_t rows")
-
-
-def test_stack_layer_full_sampled():
-    """Every tensor of one stack layer, dual-axis at full size, checked on
-    seeded rows and columns (a fixed seed per tensor)."""
+def test_stack_layer_full_dual():
+    """Every tensor of one stack layer (32768 tokens, 7168 <-> 18432),
+    dual-axis quantised at full size, every byte against the oracle."""
     d = W.stack_layer(0, "cuda")
-    for seed, name in enumerate(("X_up", "X_dn", "dY_up", "dY_dn", "W_up", "W_dn")):
-        _sampled_dual(d[name], f"stack {name}", seed=100 + seed)
+    for name in ("X_up", "X_dn", "dY_up", "dY_dn", "W_up", "W_dn"):
+        _check_full(d[name], "dual", f"stack {name}")
     del d
 
 
@@ -193,14 +174,12 @@ def test_stack_weights_full_32x32():
     del d
 
 
-def test_moe_weights_full_sampled():
+def test_moe_full_row():
+    """The MoE tensors at full size in 1x32 row blocks (tokens, the
+    down-projection input and both expert weight stacks), every byte against
+    the oracle."""
     d = W.moe("cuda")
-    Wg = d["W_gu"].reshape(-1, d["W_gu"].shape[-1])
-    say(f"[quant] moe W_gu row shape={tuple(Wg.shape)}")
-    q, s = mx.quant(Wg, "row")
-    torch.cuda.synchronize()
-    rng = np.random.default_rng(3)
-    rows = torch.from_numpy(np.unique(rng.integers(0, Wg.shape[0], 256))).cuda()
-    rq, rs = oracle.quant_row(bits(Wg.index_select(0, rows)))
-    assert_bytes(q.index_select(0, rows), rq, "W_gu q rows")
-    assert_bytes(s.index_select(0, rows), rs, "W_gu s rows")
+    for name in ("X", "H", "W_gu", "W_dn"):
+        x = d[name]
+        _check_full(x.reshape(-1, x.shape[-1]), "row", f"moe {name}")
+    del d
