@@ -95,6 +95,22 @@ def test_quant_grouped_col_full_moe():
         del q, s, wq, ws
 
 
+def test_quant_batched_col_full_moe_weights():
+    """The expert weights in column blocks, batched over the 64 experts (the
+    backward-data operand of the MoE), at full size: every byte against the
+    oracle's per-matrix column quantisation."""
+    d = W.moe("cuda")
+    for name in ("W_gu", "W_dn"):
+        w = d[name]
+        say(f"[moe-bwd] batched col full {name} {tuple(w.shape)}")
+        qt, st = mx.quant_batched(w, "col")
+        torch.cuda.synchronize()
+        wq, ws = oracle.quant_col_batched(bits(w))
+        assert_bytes(qt, wq, f"batched col {name} q_t")
+        assert_bytes(st, ws, f"batched col {name} s_t")
+        del qt, st, wq, ws
+
+
 def _wgrad_case(sizes, M, N, seed):
     off = _offsets(sizes)
     T = int(off[-1])
