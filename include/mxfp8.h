@@ -205,6 +205,15 @@ mx_status mx_quant_batched(mx_quant_mode mode, const void* x, int64_t batch, int
                            int64_t cols, void* q, void* s, void* q_t, void* s_t,
                            hipStream_t stream);
 
+/* mx_quant_batched with the payload element type chosen (E4M3 or E5M2, the
+ * RFC's two FP8 dst_types, section 3.5.2.3), with the scale rule for that
+ * type as in mx_quant_elem.  Shapes, layouts and errors as mx_quant_batched,
+ * which is this call with E4M3; an unknown element type returns
+ * MX_ERR_INVALID_ARG. */
+mx_status mx_quant_batched_elem(mx_quant_mode mode, mx_elem_type elem, const void* x,
+                                int64_t batch, int64_t rows, int64_t cols, void* q, void* s,
+                                void* q_t, void* s_t, hipStream_t stream);
+
 /* Columns of the per-group column-quantised token matrix: 128 * (T / 128 + G)
  * (integer division).  Returns -1 for T < 0 or G < 1. */
 int64_t mx_grouped_col_capacity(int64_t T, int64_t G);

@@ -20,7 +20,7 @@ __all__ = [
     "mx_last_error", "mx_quant", "mx_gemm", "mx_grouped_gemm", "mx_quant_elem", "mx_gemm_elem",
     "mx_grouped_gemm_elem", "mx_quant_grouped_col_elem", "mx_grouped_gemm_wgrad_elem",
     "mx_gemm_quant", "gemm_quant",
-    "mx_quant_batched",
+    "mx_quant_batched", "mx_quant_batched_elem",
     "mx_grouped_col_capacity", "mx_quant_grouped_col", "mx_grouped_gemm_wgrad", "quant", "gemm",
     "grouped_gemm", "quant_batched", "quant_grouped_col", "grouped_gemm_wgrad",
     "grouped_col_capacity", "process_quant_result", "QUANT_MODES", "GEMM_LAYOUTS",
@@ -79,6 +79,8 @@ def lib() -> ctypes.CDLL:
         L.mx_gemm_quant.argtypes = [c_int, c_int, c_int, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
         L.mx_quant_batched.restype = c_int
         L.mx_quant_batched.argtypes = [c_int, vp, i64, i64, i64, vp, vp, vp, vp, vp]
+        L.mx_quant_batched_elem.restype = c_int
+        L.mx_quant_batched_elem.argtypes = [c_int, c_int, vp, i64, i64, i64, vp, vp, vp, vp, vp]
         L.mx_grouped_col_capacity.restype = i64
         L.mx_grouped_col_capacity.argtypes = [i64, i64]
         L.mx_quant_grouped_col.restype = c_int
@@ -144,6 +146,10 @@ def mx_gemm_quant(layout, bkind, out_elem, M, N, K, a, sa, b, sb, q, s, stream) 
 
 def mx_quant_batched(mode, x, batch, rows, cols, q, s, q_t, s_t, stream) -> int:
     return lib().mx_quant_batched(mode, x, batch, rows, cols, q, s, q_t, s_t, stream)
+
+
+def mx_quant_batched_elem(mode, elem, x, batch, rows, cols, q, s, q_t, s_t, stream) -> int:
+    return lib().mx_quant_batched_elem(mode, elem, x, batch, rows, cols, q, s, q_t, s_t, stream)
 
 
 def mx_grouped_col_capacity(T, G) -> int:
@@ -347,13 +353,15 @@ def grouped_gemm(offsets, a, sa, b, sb, out=None, a_elem: str = "e4m3", b_elem: 
     return out
 
 
-def quant_batched(x, mode: str = "row"):
+def quant_batched(x, mode: str = "row", elem: str = "e4m3"):
     """mx_quant on every matrix of a BF16 stack x [B, rows, cols] (e.g. the
     per-expert weights of an MoE layer); outputs are the stacked per-matrix
-    outputs of ``quant`` in the same mode."""
+    outputs of ``quant`` in the same mode and element type."""
     torch = _torch()
     if mode not in QUANT_MODES:
         raise ValueError(f"unknown quantisation mode {mode!r}; expected one of {list(QUANT_MODES)}")
+    if elem not in ELEM_TYPES:
+        raise ValueError(f"unknown element type {elem!r}; expected one of {list(ELEM_TYPES)}")
     _need(x, torch.bfloat16, "x", 3)
     B, R, C = x.shape
     dev, u8 = x.device, torch.uint8
@@ -365,8 +373,8 @@ def quant_batched(x, mode: str = "row"):
     if mode in ("col", "dual"):
         qt = torch.empty((B, C, R), dtype=u8, device=dev)
         st = torch.empty((B, C, R // 32), dtype=u8, device=dev)
-    _check(mx_quant_batched(QUANT_MODES[mode], _ptr(x), B, R, C, _ptr(q), _ptr(s), _ptr(qt),
-                            _ptr(st), _stream(dev)))
+    _check(mx_quant_batched_elem(QUANT_MODES[mode], ELEM_TYPES[elem], _ptr(x), B, R, C, _ptr(q),
+                                 _ptr(s), _ptr(qt), _ptr(st), _stream(dev)))
     if mode == "row" or mode == "32x32":
         return q, s
     if mode == "col":

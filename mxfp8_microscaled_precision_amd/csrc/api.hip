@@ -291,12 +291,14 @@ mx_status mx_grouped_gemm(int64_t G, const int64_t* offsets, int64_t T, int64_t 
                               stream);
 }
 
-mx_status mx_quant_batched(mx_quant_mode mode, const void* x, int64_t batch, int64_t rows,
-                           int64_t cols, void* q, void* s, void* q_t, void* s_t,
-                           hipStream_t stream) {
+mx_status mx_quant_batched_elem(mx_quant_mode mode, mx_elem_type elem, const void* x,
+                                int64_t batch, int64_t rows, int64_t cols, void* q, void* s,
+                                void* q_t, void* s_t, hipStream_t stream) {
   g_err[0] = '\0';
   if (mode < MX_QUANT_ROW_1x32 || mode > MX_QUANT_BLOCK_32x32)
     return fail(MX_ERR_INVALID_ARG, "unknown quantisation mode %d", (int)mode);
+  if (elem != MX_ELEM_E4M3 && elem != MX_ELEM_E5M2)
+    return fail(MX_ERR_INVALID_ARG, "unknown element type %d", (int)elem);
   if (batch < 0 || batch > 65535) return fail(MX_ERR_INVALID_ARG, "batch %lld not in [0, 65535]", (long long)batch);
   if (rows < 0 || cols < 0) return fail(MX_ERR_INVALID_ARG, "negative shape [%lld, %lld]",
                                         (long long)rows, (long long)cols);
@@ -326,18 +328,25 @@ mx_status mx_quant_batched(mx_quant_mode mode, const void* x, int64_t batch, int
   mx_status st = current_device(&dev);
   if (st != MX_OK) return st;
   hipError_t e;
+  const int el = (int)elem;
   // row blocks and 32x32 tiles never cross a matrix boundary: the stack is
   // one [batch * rows, cols] matrix for them
   switch (mode) {
-    case MX_QUANT_ROW_1x32: e = mx::launch_quant_row(x, batch * rows * cols, q, s, 0, stream); break;
+    case MX_QUANT_ROW_1x32: e = mx::launch_quant_row(x, batch * rows * cols, q, s, el, stream); break;
     case MX_QUANT_BLOCK_32x32:
-      e = mx::launch_quant_tile(3, x, batch * rows, cols, q, s, q_t, s_t, 1, 0, stream);
+      e = mx::launch_quant_tile(3, x, batch * rows, cols, q, s, q_t, s_t, 1, el, stream);
       break;
-    case MX_QUANT_COL_1x32: e = mx::launch_quant_tile(1, x, rows, cols, q, s, q_t, s_t, batch, 0, stream); break;
-    default: e = mx::launch_quant_tile(2, x, rows, cols, q, s, q_t, s_t, batch, 0, stream); break;
+    case MX_QUANT_COL_1x32: e = mx::launch_quant_tile(1, x, rows, cols, q, s, q_t, s_t, batch, el, stream); break;
+    default: e = mx::launch_quant_tile(2, x, rows, cols, q, s, q_t, s_t, batch, el, stream); break;
   }
   if (e != hipSuccess) return hip_fail(e, "quantisation kernel launch");
   return MX_OK;
+}
+
+mx_status mx_quant_batched(mx_quant_mode mode, const void* x, int64_t batch, int64_t rows,
+                           int64_t cols, void* q, void* s, void* q_t, void* s_t,
+                           hipStream_t stream) {
+  return mx_quant_batched_elem(mode, MX_ELEM_E4M3, x, batch, rows, cols, q, s, q_t, s_t, stream);
 }
 
 int64_t mx_grouped_col_capacity(int64_t T, int64_t G) {

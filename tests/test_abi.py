@@ -185,6 +185,9 @@ def test_elem_validation():
     assert mx.mx_quant_elem(0, 1, 1, 4, 33, 1, 1, 0, 0, 0) == SHAPE
     assert mx.mx_gemm_elem(0, 0, 1, 1, 4, 4, 48, 1, 1, 1, 1, 1, 0) == SHAPE
     assert mx.mx_quant_elem(2, 1, 0, 64, 0, 0, 0, 0, 0, 0) == 0     # empty
+    assert mx.mx_quant_batched_elem(1, 2, 1, 2, 32, 32, 0, 0, 1, 1, 0) == INVALID
+    assert mx.mx_quant_batched_elem(1, 1, 1, 2, 33, 32, 0, 0, 1, 1, 0) == SHAPE
+    assert mx.mx_quant_batched_elem(2, 1, 0, 0, 32, 32, 0, 0, 0, 0, 0) == 0   # empty
 
 
 def test_binding_rejects_unknown_elem_names():

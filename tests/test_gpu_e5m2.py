@@ -71,6 +71,20 @@ def test_ragged_and_heavy_tailed_e5m2(shape, mode):
     _check(x, mode, f"student-t {shape}")
 
 
+@pytest.mark.parametrize("mode", MODES)
+def test_quant_batched_e5m2(mode):
+    """A stack of three matrices (ragged 128-tiles, heavy tails) in E5M2:
+    every matrix's outputs byte-exact against the oracle's."""
+    B, R, C = 3, 160, 96
+    x = W.bf16_bits(W.student_t_bf16((B * R, C), 3, 41)).reshape(B, R, C)
+    say(f"[e5m2] batched {mode} [{B},{R},{C}]")
+    got = mx.quant_batched(W.bits_to_bf16(x, "cuda"), mode, "e5m2")
+    torch.cuda.synchronize()
+    for i in range(B):
+        for k, (g, w) in enumerate(zip(got, _oracle(np.ascontiguousarray(x[i]), mode))):
+            assert_bytes(g[i], w, f"batched {mode} e5m2 matrix {i} output {k}")
+
+
 @pytest.mark.parametrize("a_elem,b_elem", [("e5m2", "e5m2"), ("e5m2", "e4m3"), ("e4m3", "e5m2")])
 @pytest.mark.parametrize("M,N,K", [(64, 96, 128), (300, 224, 160), (512, 512, 2048)])
 def test_gemm_row_scales_mixed_elems(a_elem, b_elem, M, N, K):
