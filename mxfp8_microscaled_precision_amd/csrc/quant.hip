@@ -83,6 +83,7 @@ constexpr int TILE_THREADS = 512;
 constexpr int TILE_ROWS = 128;
 constexpr int TILE_COLS = 128;
 constexpr int TILE_MAX_RUN = 8;  // row tiles one workgroup walks (grouped column mode)
+constexpr int CHIP_CUS = 256;    // MI355X compute units (sizes the runs only)
 
 enum TileMode { TILE_COL = 1, TILE_DUAL = 2, TILE_BLOCK32 = 3, TILE_GCOL = 4 };
 
@@ -384,7 +385,7 @@ hipError_t launch_quant_row(const void* x, int64_t n, void* q, void* s, int elem
 static int tile_run(int mode, int64_t row_tiles, int64_t other_tiles) {
   if (mode != TILE_GCOL) return 1;
   int run = TILE_MAX_RUN;
-  while (run > 1 && ((row_tiles + run - 1) / run) * other_tiles < 4 * 256) run >>= 1;
+  while (run > 1 && ((row_tiles + run - 1) / run) * other_tiles < 4 * CHIP_CUS) run >>= 1;
   return run;
 }
 
