@@ -85,6 +85,8 @@ def test_quant_empty_is_noop():
     ((0, 0, 4, 4, 32, 1, 1, 1, 1, 0, 0), INVALID),     # NULL c
     ((0, 0, 4, 4, 32, 0, 1, 1, 1, 1, 0), INVALID),     # NULL a
     ((0, 0, 1 << 26, 1 << 26, 32, 1, 1, 1, 1, 1, 0), SHAPE),  # more tiles than one launch grid
+    ((0, 0, 4, 4, 1 << 23, 1, 1, 1, 1, 1, 0), SHAPE),  # K beyond 32-bit tile offsets
+    ((1, 1, 4, 256, (1 << 23) - 256, 1, 1, 1, 1, 1, 0), SHAPE),  # transposed 32x32 weight too large
 ])
 def test_gemm_validation(args, status):
     assert mx.mx_gemm(*args) == status
@@ -99,6 +101,7 @@ def test_gemm_empty_is_noop():
     ((513, 1, 4, 8, 32, 1, 1, 1, 1, 1, 0), INVALID),   # G too large
     ((4, 1, 4, 8, 40, 1, 1, 1, 1, 1, 0), SHAPE),       # K % 32
     ((4, 0, 4, 8, 32, 1, 1, 1, 1, 1, 0), INVALID),     # NULL offsets
+    ((4, 1, 4, 8, 1 << 23, 1, 1, 1, 1, 1, 0), SHAPE),  # K beyond 32-bit tile offsets
 ])
 def test_grouped_validation(args, status):
     assert mx.mx_grouped_gemm(*args) == status

@@ -31,6 +31,16 @@ def test_tiny_config_fprop():
     _run(qa, sa, qw, sw, "fprop", "1x32", oracle.BKIND_ROW, "tiny")
 
 
+def test_largest_k():
+    """The longest contraction the boundary accepts (K = 2^23 - 32, so a
+    256-row tile of an operand spans just under 2^31 bytes), with ragged M
+    and N: every element against the oracle."""
+    M, N, K = 3, 40, (1 << 23) - 32
+    qa, sa = oracle.quant_row(bits(W.normal_bf16((M, K), 1.0, 71)))
+    qb, sb = oracle.quant_row(bits(W.normal_bf16((N, K), 1.0, 72)))
+    _run(qa, sa, qb, sb, "fprop", "1x32", oracle.BKIND_ROW, "largest K")
+
+
 SHAPES = [(1, 1, 32), (64, 64, 32), (300, 200, 160), (257, 513, 96), (512, 256, 4096),
           (33, 290, 1056), (256, 256, 128),
           # K a multiple of 128 but not of 512: the pipelined kernel with a partial last
