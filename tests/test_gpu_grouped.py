@@ -46,6 +46,12 @@ def test_small_cases(sizes, N, K):
     _case(sizes, N, K, sum(sizes) + N + K, f"sizes={sizes[:6]}")
 
 
+def test_largest_k():
+    """The longest contraction the boundary accepts (K = 2^23 - 32), two
+    experts of 2 and 3 tokens, 40 features: every element."""
+    _case([2, 3], 40, (1 << 23) - 32, 91, "largest K")
+
+
 def test_scaled_moe_zipf():
     """MoE workload with tokens / 64 and features / 16: Zipf(1.1) sizes with
     forced-empty experts and sizes not multiples of 32."""
