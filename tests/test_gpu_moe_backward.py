@@ -164,6 +164,34 @@ def test_wgrad_small_cases(sizes, M, N):
             assert torch.count_nonzero(c[g]) == 0, g
 
 
+def test_largest_token_capacity():
+    """The most tokens the boundary accepts for the MoE backward (a padded
+    capacity of 8388352 columns, just under 2^23): both operands' per-group
+    column quantisation byte-exact, then the per-expert weight gradient on
+    those bytes within the GEMM tolerance."""
+    sizes = [4194311, 4193908]
+    off = _offsets(sizes)
+    T, M, N = int(off[-1]), 32, 32
+    cap = mx.grouped_col_capacity(T, len(sizes))
+    assert cap == 8388352 and 256 * cap < 2 ** 31
+    say(f"[moe-bwd] largest capacity T={T} cap={cap}")
+    dy = W.normal_bf16((T, M), 0.01, 501)
+    xx = W.normal_bf16((T, N), 1.0, 502)
+    qa, sa = mx.quant_grouped_col(dy.cuda(), dev(off))
+    qb, sb = mx.quant_grouped_col(xx.cuda(), dev(off))
+    torch.cuda.synchronize()
+    wqa, wsa = oracle.quant_col_grouped(bits(dy), off)
+    wqb, wsb = oracle.quant_col_grouped(bits(xx), off)
+    assert_bytes(qa, wqa, "largest capacity q_t (gradients)")
+    assert_bytes(sa, wsa, "largest capacity s_t (gradients)")
+    assert_bytes(qb, wqb, "largest capacity q_t (inputs)")
+    assert_bytes(sb, wsb, "largest capacity s_t (inputs)")
+    c = mx.grouped_gemm_wgrad(dev(off), T, qa, sa, qb, sb)
+    torch.cuda.synchronize()
+    ref, bound = oracle.grouped_gemm_wgrad(off, wqa, wsa, wqb, wsb)
+    assert_gemm(c, ref, bound, "wgrad at the largest capacity")
+
+
 def test_wgrad_neighbour_nan_scales_stay_out():
     """Scale words past a group's last step are not read: with every scale
     byte of the next group set to NaN (0xFF), an expert whose step count is
