@@ -305,7 +305,9 @@ __device__ __forceinline__ void quant_tile(const uint16_t* __restrict__ x, int64
 // consecutive row tiles (run <= TILE_MAX_RUN, chosen by the launcher) and
 // stores each column's 4 * run scale bytes in one piece at the end instead
 // of four bytes per tile: fewer partly written memory lines.  The other
-// modes take one tile per workgroup (a run measured slower there).
+// modes take one tile per workgroup (a run measured slower there).  At
+// least 6 waves per SIMD: holds the grouped column loop to 80 VGPRs (the
+// other modes need fewer, so it changes nothing for them).
 template <int MODE, int EL>
 __global__ void __launch_bounds__(TILE_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
 quant_tile_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C, uint8_t* __restrict__ q,
