@@ -36,3 +36,25 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_profile_commands_use_valid_bench_flags(monkeypatch):
+    """Every bench.py command recorded in profiles/ parses with bench.py's own
+    argument parser, and a counter run (--pmc) never also asks for a trace."""
+    import glob
+    import shlex
+    cmds = []
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        for line in open(path):
+            if line.startswith("rocprofv3 ") and "bench.py" in line:
+                cmds.append((os.path.basename(path), line.strip()))
+    assert cmds, "no recorded bench commands"
+    for name, line in cmds:
+        words = shlex.split(line)
+        if "--pmc" in words:
+            assert not any(w in words for w in ("--kernel-trace", "--sys-trace", "-s",
+                                                "--runtime-trace", "-r")), name
+        args = words[words.index(next(w for w in words if w.endswith("bench.py"))) + 1:]
+        monkeypatch.setattr(sys, "argv", ["bench.py"] + args)
+        a = bench.parse()
+        assert a.gpus == 1 and a.steps >= 1, name
