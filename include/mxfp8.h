@@ -78,7 +78,14 @@ typedef enum mx_elem_type {
     MX_ELEM_E5M2 = 1
 } mx_elem_type;
 
-/* Which product of a linear layer a GEMM call computes (operand roles). */
+/* Which product of a linear layer a GEMM call computes (operand roles).
+ * Each is an FP8 matmul over MX-quantised operands whose result is restored
+ * to BF16 (torchtitan-npu MXFP8/HiF8 tutorial, "MXFP8 / HiF8 architecture
+ * overview", MXFP8 bullet); the forward product takes the operands blocked
+ * along the contraction, the backward products the copies blocked along the
+ * other axis (tutorial, step-2 environment table, MXFP8_DUAL_AXIS_FORWARD;
+ * MindSpeed RFC "add MXFP8-32x32 quantisation support to FSDP", section
+ * 3.3.3: weight_fwd / weight_bwd). */
 typedef enum mx_gemm_layout {
     MX_GEMM_FPROP = 0, /* Y  = X  * W^T : a = X rows,     b = W rows            */
     MX_GEMM_DGRAD = 1, /* dX = dY * W   : a = dY rows,    b = W columns (W_col_T) */
@@ -133,7 +140,12 @@ mx_status mx_quant(mx_quant_mode mode, const void* x, int64_t rows, int64_t cols
 mx_status mx_quant_elem(mx_quant_mode mode, mx_elem_type elem, const void* x, int64_t rows,
                         int64_t cols, void* q, void* s, void* q_t, void* s_t, hipStream_t stream);
 
-/* MXFP8 GEMM C = A * B^T with FP32 accumulation and a BF16 result.
+/* MXFP8 GEMM C = A * B^T with FP32 accumulation and a BF16 result: the
+ * FP8 matmul of MX-quantised operands whose output is restored to BF16
+ * (torchtitan-npu MXFP8/HiF8 tutorial, "MXFP8 / HiF8 architecture
+ * overview", MXFP8 bullet); with 32x32 weight scales, forward and backward
+ * share one FP8 weight and differ only in the scale view (MindSpeed RFC "add
+ * MXFP8-32x32 quantisation support to FSDP", sections 3.1 and 3.3.3).
  *   a:  E4M3 [M, K] row-major, sa: E8M0 [M, K/32]
  *   b/sb by (layout, bkind):
  *     any layout, MX_BSCALE_1x32:   b [N, K], sb [N, K/32]      ("TN": both K-contiguous)
@@ -145,7 +157,10 @@ mx_status mx_quant_elem(mx_quant_mode mode, mx_elem_type elem, const void* x, in
  *   c:  BF16 [M, N] row-major.
  * C[m][n] = sum_k E4M3(a[m][k]) 2^(sa[m][k/32]-127) * E4M3(B[n][k]) 2^(sB-127).
  * Requires K % 32 == 0 (and N % 32 == 0 for 32x32 scales).  K == 0 writes
- * zeros; M == 0 or N == 0 is a no-op. */
+ * zeros (a, sa, b, sb are then not read and may be NULL); M == 0 or N == 0
+ * is a no-op.  Errors: MX_ERR_INVALID_ARG for an unknown enum value, a
+ * negative size or a NULL pointer that would be read or written;
+ * MX_ERR_UNSUPPORTED_SHAPE for the divisibility and size rules above. */
 mx_status mx_gemm(mx_gemm_layout layout, mx_bscale_kind bkind, int64_t M, int64_t N, int64_t K,
                   const void* a, const void* sa, const void* b, const void* sb, void* c,
                   hipStream_t stream);
@@ -166,7 +181,8 @@ mx_status mx_gemm_elem(mx_gemm_layout layout, mx_bscale_kind bkind, mx_elem_type
  *   the bytes equal mx_quant_elem(MX_QUANT_ROW_1x32, out_elem) applied to
  *   the BF16 result mx_gemm would write (same rounding to BF16, same rule).
  * Layouts and operand rules as mx_gemm; requires N % 32 == 0 as well.
- * M == 0 or N == 0 is a no-op; K == 0 gives zero payload and scales. */
+ * M == 0 or N == 0 is a no-op; K == 0 writes zero payload and scales
+ * (0x00 bytes: an all-zero block) without reading a, sa, b or sb. */
 mx_status mx_gemm_quant(mx_gemm_layout layout, mx_bscale_kind bkind, mx_elem_type out_elem,
                         int64_t M, int64_t N, int64_t K, const void* a, const void* sa,
                         const void* b, const void* sb, void* q, void* s, hipStream_t stream);
@@ -182,22 +198,35 @@ mx_status mx_gemm_quant(mx_gemm_layout layout, mx_bscale_kind bkind, mx_elem_typ
  *            group, so bad offsets give wrong rows but never a bad access.
  *   a: E4M3 [T, K], sa [T, K/32];  b: E4M3 [G, N, K], sb [G, N, K/32]
  *   c: BF16 [T, N]; row r of expert g is  c[r] = a[r] * b[g]^T.
+ *   workspace: DEVICE scratch of at least
+ *            mx_grouped_gemm_workspace_size(G, T, N) bytes, owned by the
+ *            caller (may be NULL when that size is 0, as it is in this
+ *            version: the kernel derives its tile list from the offsets on
+ *            the device, so it is not touched).
  * Requires K % 32 == 0 and 1 <= G <= 512.  T == 0 or N == 0 is a no-op.
- * Needs no workspace. */
+ * Errors: MX_ERR_INVALID_ARG for G outside [1, 512], a negative size, a NULL
+ * pointer that would be read or written, or workspace_bytes below the
+ * required size; MX_ERR_UNSUPPORTED_SHAPE for K % 32 != 0 or K too large. */
 mx_status mx_grouped_gemm(int64_t G, const int64_t* offsets, int64_t T, int64_t N, int64_t K,
                           const void* a, const void* sa, const void* b, const void* sb, void* c,
-                          hipStream_t stream);
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of device workspace mx_grouped_gemm and mx_grouped_gemm_elem need
+ * for G groups, T token rows and N output columns.  Pure host function, no
+ * HIP call; currently 0 for every shape. */
+size_t mx_grouped_gemm_workspace_size(int64_t G, int64_t T, int64_t N);
 
 /* mx_grouped_gemm with the payload element type of each operand chosen
  * (E4M3 or E5M2, the RFC's two FP8 dst_types, section 3.5.2.3): a_elem for
  * the token rows a (e.g. E5M2 gradients in the MoE backward-data product),
  * b_elem for the expert weights b.  Scales, layouts, rules and errors as
- * mx_grouped_gemm, which is this call with E4M3 for both; an unknown
- * element type returns MX_ERR_INVALID_ARG. */
+ * mx_grouped_gemm, which is this call with E4M3 for both (the workspace
+ * rule included); an unknown element type returns MX_ERR_INVALID_ARG. */
 mx_status mx_grouped_gemm_elem(mx_elem_type a_elem, mx_elem_type b_elem, int64_t G,
                                const int64_t* offsets, int64_t T, int64_t N, int64_t K,
                                const void* a, const void* sa, const void* b, const void* sb,
-                               void* c, hipStream_t stream);
+                               void* c, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
 
 /* mx_quant over a batch of equally shaped matrices, e.g. the per-expert
  * weights [G, rows, cols] of an MoE layer (the RFC quantises gate_up_proj /

@@ -17,14 +17,15 @@ import os
 
 __all__ = [
     "MXError", "lib", "mx_device_check", "mx_arch_supported", "mx_status_string",
-    "mx_last_error", "mx_quant", "mx_gemm", "mx_grouped_gemm", "mx_quant_elem", "mx_gemm_elem",
+    "mx_last_error", "mx_quant", "mx_gemm", "mx_grouped_gemm", "mx_grouped_gemm_workspace_size",
+    "mx_quant_elem", "mx_gemm_elem",
     "mx_grouped_gemm_elem", "mx_quant_grouped_col_elem", "mx_grouped_gemm_wgrad_elem",
     "mx_gemm_quant", "gemm_quant",
     "mx_quant_batched", "mx_quant_batched_elem",
     "mx_grouped_col_capacity", "mx_quant_grouped_col", "mx_grouped_gemm_wgrad", "quant", "gemm",
     "grouped_gemm", "quant_batched", "quant_grouped_col", "grouped_gemm_wgrad",
     "grouped_col_capacity", "process_quant_result", "QUANT_MODES", "GEMM_LAYOUTS",
-    "BSCALE_KINDS",
+    "BSCALE_KINDS", "ELEM_TYPES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxfp8.so")
@@ -54,7 +55,7 @@ def lib() -> ctypes.CDLL:
                 f"{LIB_PATH} is missing: build it with "
                 "`python -m mxfp8_microscaled_precision_amd.build` (hipcc, gfx950)")
         L = ctypes.CDLL(LIB_PATH)
-        i64, vp, c_int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        i64, vp, c_int, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
         L.mx_device_check.restype = c_int
         L.mx_device_check.argtypes = [c_int]
         L.mx_arch_supported.restype = c_int
@@ -68,13 +69,16 @@ def lib() -> ctypes.CDLL:
         L.mx_gemm.restype = c_int
         L.mx_gemm.argtypes = [c_int, c_int, i64, i64, i64, vp, vp, vp, vp, vp, vp]
         L.mx_grouped_gemm.restype = c_int
-        L.mx_grouped_gemm.argtypes = [i64, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp]
+        L.mx_grouped_gemm.argtypes = [i64, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.mx_grouped_gemm_workspace_size.restype = sz
+        L.mx_grouped_gemm_workspace_size.argtypes = [i64, i64, i64]
         L.mx_quant_elem.restype = c_int
         L.mx_quant_elem.argtypes = [c_int, c_int, vp, i64, i64, vp, vp, vp, vp, vp]
         L.mx_gemm_elem.restype = c_int
         L.mx_gemm_elem.argtypes = [c_int, c_int, c_int, c_int, i64, i64, i64, vp, vp, vp, vp, vp, vp]
         L.mx_grouped_gemm_elem.restype = c_int
-        L.mx_grouped_gemm_elem.argtypes = [c_int, c_int, i64, vp, i64, i64, i64, vp, vp, vp, vp, vp, vp]
+        L.mx_grouped_gemm_elem.argtypes = [c_int, c_int, i64, vp, i64, i64, i64, vp, vp, vp, vp, vp,
+                                           vp, sz, vp]
         L.mx_gemm_quant.restype = c_int
         L.mx_gemm_quant.argtypes = [c_int, c_int, c_int, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
         L.mx_quant_batched.restype = c_int
@@ -124,12 +128,19 @@ def mx_gemm(layout, bkind, M, N, K, a, sa, b, sb, c, stream) -> int:
     return lib().mx_gemm(layout, bkind, M, N, K, a, sa, b, sb, c, stream)
 
 
-def mx_grouped_gemm(G, offsets, T, N, K, a, sa, b, sb, c, stream) -> int:
-    return lib().mx_grouped_gemm(G, offsets, T, N, K, a, sa, b, sb, c, stream)
+def mx_grouped_gemm(G, offsets, T, N, K, a, sa, b, sb, c, workspace, workspace_bytes, stream) -> int:
+    return lib().mx_grouped_gemm(G, offsets, T, N, K, a, sa, b, sb, c, workspace, workspace_bytes,
+                                 stream)
 
 
-def mx_grouped_gemm_elem(a_elem, b_elem, G, offsets, T, N, K, a, sa, b, sb, c, stream) -> int:
-    return lib().mx_grouped_gemm_elem(a_elem, b_elem, G, offsets, T, N, K, a, sa, b, sb, c, stream)
+def mx_grouped_gemm_workspace_size(G, T, N) -> int:
+    return lib().mx_grouped_gemm_workspace_size(G, T, N)
+
+
+def mx_grouped_gemm_elem(a_elem, b_elem, G, offsets, T, N, K, a, sa, b, sb, c, workspace,
+                         workspace_bytes, stream) -> int:
+    return lib().mx_grouped_gemm_elem(a_elem, b_elem, G, offsets, T, N, K, a, sa, b, sb, c,
+                                      workspace, workspace_bytes, stream)
 
 
 def mx_quant_elem(mode, elem, x, rows, cols, q, s, q_t, s_t, stream) -> int:
@@ -348,8 +359,11 @@ def grouped_gemm(offsets, a, sa, b, sb, out=None, a_elem: str = "e4m3", b_elem: 
         out = torch.empty((T, N), dtype=torch.bfloat16, device=a.device)
     _need(out, torch.bfloat16, "out", 2)
     _shape(out, (T, N), "out")
+    nws = mx_grouped_gemm_workspace_size(G, T, N)
+    ws = torch.empty(nws, dtype=torch.uint8, device=a.device) if nws else None
     _check(mx_grouped_gemm_elem(ELEM_TYPES[a_elem], ELEM_TYPES[b_elem], G, _ptr(offsets), T, N, K,
-                                _ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(out), _stream(a.device)))
+                                _ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(out), _ptr(ws), nws,
+                                _stream(a.device)))
     return out
 
 
@@ -439,21 +453,41 @@ def grouped_gemm_wgrad(offsets, T: int, a, sa, b, sb, out=None, a_elem: str = "e
     return out
 
 
-def process_quant_result(weight, recipe: str = "mxfp8"):
+def _dst_type_name(dst_type) -> str:
+    """'e4m3' / 'e5m2' from a name or a torch FP8 dtype (the RFC passes the
+    target dtype itself)."""
+    if isinstance(dst_type, str):
+        name = dst_type.lower()
+    else:
+        name = {"torch.float8_e4m3fn": "e4m3", "torch.float8_e5m2": "e5m2"}.get(str(dst_type), "")
+    if name not in ELEM_TYPES:
+        raise ValueError(f"unsupported dst_type {dst_type!r}: expected 'e4m3' (torch.float8_e4m3fn) "
+                         f"or 'e5m2' (torch.float8_e5m2)")
+    return name
+
+
+def process_quant_result(weight, recipe: str = "mxfp8", dst_type="e4m3"):
     """Quantise a weight for both passes, in the RFC's tuple order
     (weight_fwd, scale_fwd, weight_bwd, scale_bwd).
 
-    "mxfp8"       -> dual-axis 1x32: two FP8 copies, row and column scales.
-    "mxfp8-32x32" -> 32x32 tiles: weight_bwd IS weight_fwd and the one tile
-                     scale array serves both passes (forward blocks K along
-                     the columns, backward along the rows).
+    recipe   "mxfp8"       -> dual-axis 1x32: two FP8 copies, row and column
+                              scales.
+             "mxfp8-32x32" -> 32x32 tiles: weight_bwd IS weight_fwd and the
+                              one tile scale array serves both passes (forward
+                              blocks K along the columns, backward along the
+                              rows).
+    dst_type the FP8 payload type: "e4m3" / torch.float8_e4m3fn or "e5m2" /
+             torch.float8_e5m2 (the scale rule follows the type's largest
+             finite value).
     (MindSpeed RFC "add MXFP8-32x32 quantisation support to FSDP", sections
-    3.3.3 and 3.5.2.3; an unsupported recipe raises ValueError.)
+    3.3.3 and 3.5.2.3: process_quant_result_fn(weight, dst_type, config); an
+    unsupported recipe or dst_type raises ValueError.)
     """
+    if recipe not in ("mxfp8", "mxfp8-32x32"):
+        raise ValueError(f"unsupported recipe {recipe!r}: expected 'mxfp8' or 'mxfp8-32x32'")
+    elem = _dst_type_name(dst_type)
     if recipe == "mxfp8":
-        q, s, qt, st = quant(weight, "dual")
+        q, s, qt, st = quant(weight, "dual", elem)
         return q, s, qt, st
-    if recipe == "mxfp8-32x32":
-        q, s = quant(weight, "32x32")
-        return q, s, q, s
-    raise ValueError(f"unsupported recipe {recipe!r}: expected 'mxfp8' or 'mxfp8-32x32'")
+    q, s = quant(weight, "32x32", elem)
+    return q, s, q, s

@@ -169,7 +169,7 @@ mx_status mx_gemm_elem(mx_gemm_layout layout, mx_bscale_kind bkind, mx_elem_type
   if (bkind == MX_BSCALE_32x32 && layout == MX_GEMM_WGRAD)
     return fail(MX_ERR_INVALID_ARG, "the weight-gradient GEMM has no 32x32 weight operand");
   if (M < 0 || N < 0 || K < 0) return fail(MX_ERR_INVALID_ARG, "negative GEMM shape");
-  if (mul_overflows(M, K) || mul_overflows(N, K) || mul_overflows(M, N))
+  if (mul_overflows(M, K) || mul_overflows(N, K) || mul_overflows(M, N) || M * N > INT64_MAX / 2)
     return fail(MX_ERR_INVALID_ARG, "GEMM shape too large");
   if (K % 32 != 0) return fail(MX_ERR_UNSUPPORTED_SHAPE, "K %lld is not a multiple of 32", (long long)K);
   if (K >= K_LIMIT)
@@ -191,7 +191,7 @@ mx_status mx_gemm_elem(mx_gemm_layout layout, mx_bscale_kind bkind, mx_elem_type
   if (st != MX_OK) return st;
   hipError_t e;
   if (K == 0) {
-    e = mx::launch_fill_zero_bf16(c, M * N, stream);
+    e = mx::launch_fill_zero(c, 2 * M * N, stream);
   } else {
     int bmode = mx::GEMM_B_ROW;
     if (bkind == MX_BSCALE_32x32) bmode = layout == MX_GEMM_DGRAD ? mx::GEMM_B_TILE_T : mx::GEMM_B_TILE;
@@ -220,7 +220,7 @@ mx_status mx_gemm_quant(mx_gemm_layout layout, mx_bscale_kind bkind, mx_elem_typ
   if (bkind == MX_BSCALE_32x32 && layout == MX_GEMM_WGRAD)
     return fail(MX_ERR_INVALID_ARG, "the weight-gradient GEMM has no 32x32 weight operand");
   if (M < 0 || N < 0 || K < 0) return fail(MX_ERR_INVALID_ARG, "negative GEMM shape");
-  if (mul_overflows(M, K) || mul_overflows(N, K) || mul_overflows(M, N))
+  if (mul_overflows(M, K) || mul_overflows(N, K) || mul_overflows(M, N) || M * N > INT64_MAX / 2)
     return fail(MX_ERR_INVALID_ARG, "GEMM shape too large");
   if (K % 32 != 0) return fail(MX_ERR_UNSUPPORTED_SHAPE, "K %lld is not a multiple of 32", (long long)K);
   if (N % 32 != 0)
@@ -240,25 +240,45 @@ mx_status mx_gemm_quant(mx_gemm_layout layout, mx_bscale_kind bkind, mx_elem_typ
   int dev;
   mx_status st = current_device(&dev);
   if (st != MX_OK) return st;
-  int bmode = mx::GEMM_B_ROW;
-  if (bkind == MX_BSCALE_32x32) bmode = layout == MX_GEMM_DGRAD ? mx::GEMM_B_TILE_T : mx::GEMM_B_TILE;
-  hipError_t e = mx::launch_gemm_q(bmode, (int)out_elem, M, N, K, a, sa, b, sb, q, s, stream);
+  hipError_t e;
+  if (K == 0) {
+    // an empty contraction: every block of the result is zero (payload 0x00,
+    // scale 0x00); no GEMM kernel sees a zero-length operand
+    e = mx::launch_fill_zero(q, M * N, stream);
+    if (e == hipSuccess) e = mx::launch_fill_zero(s, M * (N / 32), stream);
+  } else {
+    int bmode = mx::GEMM_B_ROW;
+    if (bkind == MX_BSCALE_32x32) bmode = layout == MX_GEMM_DGRAD ? mx::GEMM_B_TILE_T : mx::GEMM_B_TILE;
+    e = mx::launch_gemm_q(bmode, (int)out_elem, M, N, K, a, sa, b, sb, q, s, stream);
+  }
   if (e != hipSuccess) return hip_fail(e, "fused GEMM kernel launch");
   return MX_OK;
+}
+
+size_t mx_grouped_gemm_workspace_size(int64_t G, int64_t T, int64_t N) {
+  (void)G;
+  (void)T;
+  (void)N;
+  return 0;  // the persistent kernel derives its tile list from the offsets on the device
 }
 
 mx_status mx_grouped_gemm_elem(mx_elem_type a_elem, mx_elem_type b_elem, int64_t G,
                                const int64_t* offsets, int64_t T, int64_t N, int64_t K,
                                const void* a, const void* sa, const void* b, const void* sb,
-                               void* c, hipStream_t stream) {
+                               void* c, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
   g_err[0] = '\0';
   if ((a_elem != MX_ELEM_E4M3 && a_elem != MX_ELEM_E5M2) ||
       (b_elem != MX_ELEM_E4M3 && b_elem != MX_ELEM_E5M2))
     return fail(MX_ERR_INVALID_ARG, "unknown element type (a %d, b %d)", (int)a_elem, (int)b_elem);
   if (G < 1 || G > 512) return fail(MX_ERR_INVALID_ARG, "group count %lld not in [1, 512]", (long long)G);
   if (T < 0 || N < 0 || K < 0) return fail(MX_ERR_INVALID_ARG, "negative grouped GEMM shape");
-  if (mul_overflows(T, K) || mul_overflows(T, N) || mul_overflows(G, N) || mul_overflows(G * N, K))
+  if (mul_overflows(T, K) || mul_overflows(T, N) || mul_overflows(G, N) || mul_overflows(G * N, K) ||
+      T * N > INT64_MAX / 2)
     return fail(MX_ERR_INVALID_ARG, "grouped GEMM shape too large");
+  const size_t need = mx_grouped_gemm_workspace_size(G, T, N);
+  if (workspace_bytes < need || (need > 0 && !workspace))
+    return fail(MX_ERR_INVALID_ARG, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
   if (K % 32 != 0) return fail(MX_ERR_UNSUPPORTED_SHAPE, "K %lld is not a multiple of 32", (long long)K);
   if (K >= K_LIMIT)
     return fail(MX_ERR_UNSUPPORTED_SHAPE, "K %lld too large for 32-bit tile offsets", (long long)K);
@@ -270,7 +290,7 @@ mx_status mx_grouped_gemm_elem(mx_elem_type a_elem, mx_elem_type b_elem, int64_t
   if (st != MX_OK) return st;
   hipError_t e;
   if (K == 0) {
-    e = mx::launch_fill_zero_bf16(c, T * N, stream);
+    e = mx::launch_fill_zero(c, 2 * T * N, stream);
   } else {
     int cus;
     {
@@ -286,9 +306,9 @@ mx_status mx_grouped_gemm_elem(mx_elem_type a_elem, mx_elem_type b_elem, int64_t
 
 mx_status mx_grouped_gemm(int64_t G, const int64_t* offsets, int64_t T, int64_t N, int64_t K,
                           const void* a, const void* sa, const void* b, const void* sb, void* c,
-                          hipStream_t stream) {
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return mx_grouped_gemm_elem(MX_ELEM_E4M3, MX_ELEM_E4M3, G, offsets, T, N, K, a, sa, b, sb, c,
-                              stream);
+                              workspace, workspace_bytes, stream);
 }
 
 mx_status mx_quant_batched_elem(mx_quant_mode mode, mx_elem_type elem, const void* x,

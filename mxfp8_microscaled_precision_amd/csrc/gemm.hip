@@ -96,7 +96,9 @@ struct Tile {
       // chunk i%16 holding logical chunk (i%16) ^ 2(row & 7).
       // Columns past N feed only outputs that are never stored, and the
       // buffer ends with the weight, so they need no mask.
-      rb = make_rsrc(b + n0, (K - 1) * N + (N - n0));
+      // (K >= 1 here: the host writes zeros for K == 0 without a launch)
+      const int64_t bbytes = (K - 1) * N + (N - n0);
+      rb = make_rsrc(b + n0, bbytes > 0 ? bbytes : 0);
       const int krow = 4 * wave + (lane >> 4);
       const int lc = (lane & 15) ^ (2 * (krow & 7));
       voff_b = (uint32_t)(krow * N + 16 * lc);
@@ -668,13 +670,19 @@ grouped_gemm_kernel(int64_t G, const int64_t* __restrict__ offsets, int64_t T, i
   }
 }
 
-__global__ void fill_zero_kernel(uint4* __restrict__ p, int64_t n16, uint16_t* __restrict__ tail,
-                                 int64_t ntail) {
+// Zero fill of `nbytes` bytes at p (any alignment): the bytes before the
+// first 16-byte boundary and after the last are written one by one by the
+// first workgroup, the 16-byte-aligned middle with 16-byte stores.
+__global__ void fill_zero_kernel(uint8_t* __restrict__ p, int64_t head, int64_t n16,
+                                 int64_t nbytes) {
+  uint4* mid = (uint4*)(p + head);
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
        i += (int64_t)gridDim.x * blockDim.x)
-    p[i] = make_uint4(0, 0, 0, 0);
-  if (blockIdx.x == 0)
-    for (int64_t i = threadIdx.x; i < ntail; i += blockDim.x) tail[i] = 0;
+    mid[i] = make_uint4(0, 0, 0, 0);
+  if (blockIdx.x == 0) {
+    for (int64_t i = threadIdx.x; i < head; i += blockDim.x) p[i] = 0;
+    for (int64_t i = head + 16 * n16 + threadIdx.x; i < nbytes; i += blockDim.x) p[i] = 0;
+  }
 }
 
 template <int BMODE, int FAST>
@@ -807,13 +815,17 @@ hipError_t launch_grouped_gemm(int a_elem, int b_elem, int64_t G, const int64_t*
   return hipGetLastError();
 }
 
-hipError_t launch_fill_zero_bf16(void* c, int64_t n, hipStream_t stream) {
-  int64_t n16 = n / 8, ntail = n - n16 * 8;
+hipError_t launch_fill_zero(void* p, int64_t nbytes, hipStream_t stream) {
+  if (nbytes <= 0) return hipSuccess;
+  const uintptr_t a = (uintptr_t)p;
+  int64_t head = (int64_t)((16 - (a & 15)) & 15);
+  if (head > nbytes) head = nbytes;
+  const int64_t n16 = (nbytes - head) / 16;
   int64_t blocks = (n16 + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (uint4*)c, n16,
-                     (uint16_t*)c + n16 * 8, ntail);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (uint8_t*)p,
+                     head, n16, nbytes);
   return hipGetLastError();
 }
 

@@ -52,6 +52,8 @@ hipError_t launch_grouped_wgrad(int a_elem, int b_elem, int64_t G, const int64_t
                                 int64_t M, int64_t N, int64_t cap, const void* a, const void* sa,
                                 const void* b, const void* sb, void* c, hipStream_t stream);
 
-hipError_t launch_fill_zero_bf16(void* c, int64_t n, hipStream_t stream);
+// Zero `nbytes` bytes at p (any alignment), as a kernel (no hipMemsetAsync,
+// so the call can sit in a captured graph).
+hipError_t launch_fill_zero(void* p, int64_t nbytes, hipStream_t stream);
 
 }  // namespace mx

@@ -97,14 +97,51 @@ def test_gemm_empty_is_noop():
 
 
 @pytest.mark.parametrize("args,status", [
-    ((0, 1, 4, 8, 32, 1, 1, 1, 1, 1, 0), INVALID),     # G = 0
-    ((513, 1, 4, 8, 32, 1, 1, 1, 1, 1, 0), INVALID),   # G too large
-    ((4, 1, 4, 8, 40, 1, 1, 1, 1, 1, 0), SHAPE),       # K % 32
-    ((4, 0, 4, 8, 32, 1, 1, 1, 1, 1, 0), INVALID),     # NULL offsets
-    ((4, 1, 4, 8, 1 << 23, 1, 1, 1, 1, 1, 0), SHAPE),  # K beyond 32-bit tile offsets
+    ((0, 1, 4, 8, 32, 1, 1, 1, 1, 1, 0, 0, 0), INVALID),     # G = 0
+    ((513, 1, 4, 8, 32, 1, 1, 1, 1, 1, 0, 0, 0), INVALID),   # G too large
+    ((4, 1, 4, 8, 40, 1, 1, 1, 1, 1, 0, 0, 0), SHAPE),       # K % 32
+    ((4, 0, 4, 8, 32, 1, 1, 1, 1, 1, 0, 0, 0), INVALID),     # NULL offsets
+    ((4, 1, 4, 8, 1 << 23, 1, 1, 1, 1, 1, 0, 0, 0), SHAPE),  # K beyond 32-bit tile offsets
 ])
 def test_grouped_validation(args, status):
     assert mx.mx_grouped_gemm(*args) == status
+
+
+@pytest.mark.parametrize("G,T,N", [(1, 0, 0), (64, 131072, 4096), (512, 1 << 30, 1 << 16)])
+def test_grouped_workspace_size(G, T, N):
+    """The grouped GEMM's workspace query (the proposed C ABI's
+    mx_grouped_gemm_workspace_size): the persistent kernel derives its tile
+    list from the device offsets, so it needs none, and a call with no
+    workspace is valid (only the shape rules decide)."""
+    assert mx.mx_grouped_gemm_workspace_size(G, T, N) == 0
+    assert mx.mx_grouped_gemm(G, 1, T, 0, 32, 1, 1, 1, 1, 1, 0, 0, 0) == 0        # N == 0: no-op
+    assert mx.mx_grouped_gemm(G, 1, T, 8, 40, 1, 1, 1, 1, 1, 0, 0, 0) == SHAPE    # still validated
+
+
+def test_every_proposed_boundary_call_is_exported():
+    """Every call of the proposed C ABI (quantisation, the three GEMM layouts,
+    the grouped GEMM with its workspace query, the device gate and the error
+    strings) is exported under its name, with the grouped GEMM's workspace
+    arguments (13 arguments: ... c, workspace, workspace_bytes, stream)."""
+    L = ctypes.CDLL(mx.LIB_PATH)
+    for n in ("mx_device_check", "mx_status_string", "mx_last_error", "mx_quant", "mx_gemm",
+              "mx_grouped_gemm_workspace_size", "mx_grouped_gemm"):
+        assert hasattr(L, n), n
+    assert mx.lib().mx_grouped_gemm.argtypes[-3:] == [ctypes.c_void_p, ctypes.c_size_t,
+                                                      ctypes.c_void_p]
+    # the size query returns 0, so a call with no workspace at all is valid
+    assert mx.mx_grouped_gemm(2, 1, 0, 8, 32, 1, 1, 1, 1, 1, 0, 0, 0) == 0   # T == 0: no-op
+
+
+def test_process_quant_result_rejects_unknown_dst_type():
+    """The RFC's recipe call takes the FP8 target type; E4M3 and E5M2 are the
+    two it allows (section 3.5.2.3), anything else is a ValueError before any
+    device work."""
+    for bad in ("e3m4", "fp16", "int8", None):
+        with pytest.raises(ValueError):
+            mx.process_quant_result(None, "mxfp8", bad)
+    with pytest.raises(ValueError):
+        mx.process_quant_result(None, "mxfp4", "e4m3")
 
 
 def test_process_quant_result_rejects_unknown_recipe():
@@ -176,10 +213,10 @@ def test_elem_validation():
     assert mx.mx_quant_elem(0, 2, 1, 4, 32, 1, 1, 0, 0, 0) == INVALID
     assert mx.mx_gemm_elem(0, 0, 0, 5, 4, 4, 32, 1, 1, 1, 1, 1, 0) == INVALID
     assert mx.mx_gemm_elem(0, 0, 3, 0, 4, 4, 32, 1, 1, 1, 1, 1, 0) == INVALID
-    assert mx.mx_grouped_gemm_elem(2, 0, 1, 1, 4, 4, 32, 1, 1, 1, 1, 1, 0) == INVALID
-    assert mx.mx_grouped_gemm_elem(0, -1, 1, 1, 4, 4, 32, 1, 1, 1, 1, 1, 0) == INVALID
-    assert mx.mx_grouped_gemm_elem(1, 1, 1, 1, 4, 4, 48, 1, 1, 1, 1, 1, 0) == SHAPE
-    assert mx.mx_grouped_gemm_elem(1, 0, 0, 1, 4, 4, 32, 1, 1, 1, 1, 1, 0) == INVALID   # G = 0
+    assert mx.mx_grouped_gemm_elem(2, 0, 1, 1, 4, 4, 32, 1, 1, 1, 1, 1, 0, 0, 0) == INVALID
+    assert mx.mx_grouped_gemm_elem(0, -1, 1, 1, 4, 4, 32, 1, 1, 1, 1, 1, 0, 0, 0) == INVALID
+    assert mx.mx_grouped_gemm_elem(1, 1, 1, 1, 4, 4, 48, 1, 1, 1, 1, 1, 0, 0, 0) == SHAPE
+    assert mx.mx_grouped_gemm_elem(1, 0, 0, 1, 4, 4, 32, 1, 1, 1, 1, 1, 0, 0, 0) == INVALID   # G = 0
     assert mx.mx_quant_grouped_col_elem(3, 1, 64, 32, 2, 1, 1, 1, 0) == INVALID
     assert mx.mx_quant_grouped_col_elem(1, 1, 64, 33, 2, 1, 1, 1, 0) == SHAPE
     assert mx.mx_grouped_gemm_wgrad_elem(0, 7, 2, 1, 64, 32, 32, 1, 1, 1, 1, 1, 0) == INVALID

@@ -58,3 +58,24 @@ def test_profile_commands_use_valid_bench_flags(monkeypatch):
         monkeypatch.setattr(sys, "argv", ["bench.py"] + args)
         a = bench.parse()
         assert a.gpus == 1 and a.steps >= 1, name
+
+
+def test_per_kernel_medians():
+    """Per-kernel step times are sums over a step's launches of each launch's
+    median across the timed steps, so one slow step does not move them."""
+    class Ev:
+        def __init__(self, t):
+            self.t = t
+
+        def elapsed_time(self, other):
+            return other.t - self.t
+
+    events = []
+    for scale in (1.0, 5.0, 1.2):                      # the second step is an outlier
+        events.append(("gemm", 10.0, "FLOP", Ev(0.0), Ev(2.0 * scale)))
+        events.append(("quant", 4.0, "B", Ev(0.0), Ev(1.0 * scale)))
+        events.append(("gemm", 20.0, "FLOP", Ev(0.0), Ev(3.0 * scale)))
+    per = bench.per_kernel_medians(events, 3)
+    assert per["gemm"]["launches"] == 2 and per["gemm"]["work"] == 30.0
+    assert abs(per["gemm"]["ms"] - (2.0 * 1.2 + 3.0 * 1.2)) < 1e-12
+    assert per["quant"]["launches"] == 1 and abs(per["quant"]["ms"] - 1.2) < 1e-12

@@ -215,3 +215,28 @@ def test_grouped_wgrad_mixed_elems(a_elem, b_elem, sizes, M, N):
     assert_bytes(qb, ob, "wgrad operand b")
     ref, bound = oracle.grouped_gemm_wgrad(off, oa, osa, ob, osb, a_elem=ea, b_elem=eb)
     assert_gemm(c, ref, bound, f"grouped wgrad {a_elem}x{b_elem} sizes={sizes}")
+
+
+@pytest.mark.parametrize("recipe", ["mxfp8", "mxfp8-32x32"])
+@pytest.mark.parametrize("dst_type", ["e5m2", "e4m3", torch.float8_e5m2, torch.float8_e4m3fn])
+def test_process_quant_result_dst_type(recipe, dst_type):
+    """The RFC's recipe call with its FP8 target type (section 3.5.2.3):
+    process_quant_result(w, recipe, dst_type) returns (weight_fwd,
+    scale_fwd, weight_bwd, scale_bwd) equal byte for byte to the oracle's
+    quantisation of the same weight in that payload type: dual-axis for
+    "mxfp8", one 32x32-tiled weight (weight_bwd is weight_fwd) for
+    "mxfp8-32x32"."""
+    w = W.normal_bf16((288, 416), 0.02, 91)
+    elem = oracle.ELEM_E5M2 if str(dst_type) in ("e5m2", "torch.float8_e5m2") else oracle.ELEM_E4M3
+    say(f"[e5m2] process_quant_result {recipe} {dst_type}")
+    got = mx.process_quant_result(w.cuda(), recipe, dst_type)
+    torch.cuda.synchronize()
+    assert len(got) == 4
+    if recipe == "mxfp8":
+        want = oracle.quant_dual(bits(w), elem)
+    else:
+        q, s = oracle.quant_block32(bits(w), elem)
+        want = (q, s, q, s)
+        assert got[2] is got[0] and got[3] is got[1]
+    for k, (g, o) in enumerate(zip(got, want)):
+        assert_bytes(g, o, f"process_quant_result {recipe} {dst_type} output {k}")

@@ -70,6 +70,28 @@ def test_fused_equals_quantised_gemm_and_oracle_bound(M, N, K, layout, bscale, o
     assert not bad.any(), (int(bad.sum()), np.argwhere(bad)[:4])
 
 
+@pytest.mark.parametrize("layout,bscale,N", [("dgrad", "32x32", 512), ("fprop", "32x32", 544),
+                                             ("wgrad", "1x32", 320)])
+def test_fused_k_zero_every_layout(layout, bscale, N):
+    """An empty contraction through every operand layout: zero payload and
+    scale bytes (all-zero blocks), written without a GEMM launch, so the
+    transposed 32x32 weight (N > 256, several n-tiles) is never addressed."""
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    M = 96
+    a, sa = torch.empty((M, 0), **u8), torch.empty((M, 0), **u8)
+    if bscale == "32x32" and layout == "dgrad":
+        b, sb = torch.empty((0, N), **u8), torch.empty((0, N // 32), **u8)
+    elif bscale == "32x32":
+        b, sb = torch.empty((N, 0), **u8), torch.empty((N // 32, 0), **u8)
+    else:
+        b, sb = torch.empty((N, 0), **u8), torch.empty((N, 0), **u8)
+    say(f"[fused] K=0 {layout} {bscale} N={N}")
+    q, s = mx.gemm_quant(a, sa, b, sb, layout, bscale)
+    torch.cuda.synchronize()
+    assert tuple(q.shape) == (M, N) and tuple(s.shape) == (M, N // 32)
+    assert torch.count_nonzero(q) == 0 and torch.count_nonzero(s) == 0
+
+
 def test_fused_k_zero_gives_zero_blocks():
     q, s = mx.gemm_quant(torch.empty((64, 0), dtype=torch.uint8, device="cuda"),
                          torch.empty((64, 0), dtype=torch.uint8, device="cuda"),

@@ -202,36 +202,66 @@ def test_block32_full_four_products():
                 _sample(T, 40, rng), _groups32(W2.shape[1], 2, rng))
 
 
-def _corners(n):
-    """The first and last 32 indices: with the matching columns, the four
-    corner 32x32 tiles of a product."""
-    return np.concatenate([np.arange(min(32, n)), np.arange(max(n - 32, 0), n)])
+def _nan_filled(M, N):
+    return torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
 
 
-def _linear_layer_products(name, X, Wt, dY, rng, k):
+def _assert_every_tile_written(c, what):
+    """The output started as NaN: none left means every tile of the grid
+    was written (the workgroup-to-tile map covers the whole output)."""
+    torch.cuda.synchronize()
+    assert not torch.isnan(c).any().item(), f"{what}: an output tile was never written"
+
+
+def _contract_sample(what, c, qa, sa, qb, sb, bkind, qbr, sbr, rng):
+    """The stack products' sample: 32 seeded rows of C over all N, 32 seeded
+    columns of C over all M, and the four corner 32x32 tiles, each against
+    the oracle's binary64 product of the oracle's own quantisation of the
+    same BF16 sources.  (qa, sa) is A; (qb, sb, bkind) is B as the GEMM takes
+    it; (qbr, sbr) is the same B in row form ([N, K] with per-row scales),
+    which selects any set of columns: for 32x32 weights the tile scale
+    expanded over its 32 rows (and the weight transposed for the dgrad), a
+    relayout of the oracle's bytes that the oracle's own pins show equal."""
+    M, N = c.shape
+    rows = np.sort(rng.choice(M, 32, replace=False)).astype(np.int64)
+    cols = np.sort(rng.choice(N, 32, replace=False)).astype(np.int64)
+    say(f"[gemm] {what}: 32 full rows, 32 full columns, 4 corner tiles of {M}x{N}")
+    ri, ci = torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()
+    ref, bound = oracle.gemm(qa[rows], sa[rows], qb, sb, bkind)
+    assert_gemm(c.index_select(0, ri), ref, bound, f"{what}: rows {rows.tolist()}")
+    ref, bound = oracle.gemm(qa, sa, qbr[cols], sbr[cols], oracle.BKIND_ROW)
+    assert_gemm(c.index_select(1, ci), ref, bound, f"{what}: columns {cols.tolist()}")
+    for r0 in (0, M - 32):
+        for c0 in (0, N - 32):
+            ref, bound = oracle.gemm(qa[r0:r0 + 32], sa[r0:r0 + 32], qbr[c0:c0 + 32],
+                                     sbr[c0:c0 + 32], oracle.BKIND_ROW)
+            assert_gemm(c[r0:r0 + 32, c0:c0 + 32], ref, bound, f"{what}: corner tile ({r0}, {c0})")
+
+
+def _linear_layer_products(name, X, Wt, dY, rng):
     """fprop, dgrad and wgrad of one linear layer at full size, each checked
-    on a sampled grid of rows x columns (random ones, the first and last, and
-    the four corner 32x32 tiles) against the oracle quantising and
-    multiplying the same BF16 sources."""
-    T, H = X.shape
-    F = Wt.shape[0]
+    on the contract sample against the oracle's dual-axis quantisation of
+    the same BF16 sources and its binary64 product."""
     qx, sx, qxt, sxt = mx.quant(X, "dual")
     qw, sw, qwt, swt = mx.quant(Wt, "dual")
     qd, sd, qdt, sdt = mx.quant(dY, "dual")
-    Y = mx.gemm(qx, sx, qw, sw, "fprop")
-    torch.cuda.synchronize()
-    _end_to_end(f"stack {name} fprop", Y, X, "row", Wt, "row", oracle.BKIND_ROW,
-                _sample(T, k, rng, _corners(T)), _sample(F, k, rng, _corners(F)))
+    T, H = X.shape
+    F = Wt.shape[0]
+    ox, osx, oxt, osxt = oracle.quant_dual(bits(X))
+    ow, osw, owt, oswt = oracle.quant_dual(bits(Wt))
+    od, osd, odt, osdt = oracle.quant_dual(bits(dY))
+    row = oracle.BKIND_ROW
+    Y = mx.gemm(qx, sx, qw, sw, "fprop", out=_nan_filled(T, F))
+    _assert_every_tile_written(Y, f"stack {name} fprop")
+    _contract_sample(f"stack {name} fprop", Y, ox, osx, ow, osw, row, ow, osw, rng)
     del Y
-    dX = mx.gemm(qd, sd, qwt, swt, "dgrad")
-    torch.cuda.synchronize()
-    _end_to_end(f"stack {name} dgrad", dX, dY, "row", Wt, "col", oracle.BKIND_ROW,
-                _sample(T, k, rng, _corners(T)), _sample(H, k, rng, _corners(H)))
+    dX = mx.gemm(qd, sd, qwt, swt, "dgrad", out=_nan_filled(T, H))
+    _assert_every_tile_written(dX, f"stack {name} dgrad")
+    _contract_sample(f"stack {name} dgrad", dX, od, osd, owt, oswt, row, owt, oswt, rng)
     del dX
-    dW = mx.gemm(qdt, sdt, qxt, sxt, "wgrad")
-    torch.cuda.synchronize()
-    _end_to_end(f"stack {name} wgrad", dW, dY, "col", X, "col", oracle.BKIND_ROW,
-                _sample(F, k // 2, rng, _corners(F)), _sample(H, k // 2, rng, _corners(H)))
+    dW = mx.gemm(qdt, sdt, qxt, sxt, "wgrad", out=_nan_filled(F, H))
+    _assert_every_tile_written(dW, f"stack {name} wgrad")
+    _contract_sample(f"stack {name} wgrad", dW, odt, osdt, oxt, osxt, row, oxt, osxt, rng)
     del dW
 
 
@@ -242,8 +272,8 @@ def test_stack_layer_full_six_products():
     Xu, Xd, dYu, dYd, Wu, Wd = (d[k] for k in ("X_up", "X_dn", "dY_up", "dY_dn", "W_up", "W_dn"))
     say(f"[gemm] stack layer T={Xu.shape[0]} H={Xu.shape[1]} F={Wu.shape[0]}")
     rng = np.random.default_rng(41)
-    _linear_layer_products("up", Xu, Wu, dYu, rng, 24)
-    _linear_layer_products("down", Xd, Wd, dYd, rng, 24)
+    _linear_layer_products("up", Xu, Wu, dYu, rng)
+    _linear_layer_products("down", Xd, Wd, dYd, rng)
 
 
 def test_stack_layer_full_32x32_variant():
@@ -251,27 +281,34 @@ def test_stack_layer_full_32x32_variant():
     quantised once in 32x32 tiles, fprop with the tile scales and dgrad
     reading the same FP8 weight transposed, for both projections (N up to
     18432, i.e. more than 32 n-tiles: the other workgroup-to-tile map than
-    the 16384-token weight configuration uses)."""
+    the 16384-token weight configuration uses), on the contract sample."""
     d = W.stack_layer(0, "cuda")
-    T = d["X_up"].shape[0]
     rng = np.random.default_rng(43)
     for name, X, Wt, dY in (("up", d["X_up"], d["W_up"], d["dY_up"]),
                             ("down", d["X_dn"], d["W_dn"], d["dY_dn"])):
         F, H = Wt.shape
         say(f"[gemm] stack 32x32 {name}: W {F}x{H}")
         q32, s32 = mx.quant(Wt, "32x32")
+        o32, os32 = oracle.quant_block32(bits(Wt))
         qx, sx = mx.quant(X, "row")
-        Y = mx.gemm(qx, sx, q32, s32, "fprop", "32x32")
-        torch.cuda.synchronize()
-        _end_to_end(f"stack 32x32 {name} fprop", Y, X, "row", Wt, "tile", oracle.BKIND_TILE,
-                    _sample(T, 24, rng, _corners(T)), _groups32(F, 2, rng))
-        del Y, qx, sx
+        ox, osx = oracle.quant_row(bits(X))
+        T = X.shape[0]
+        Y = mx.gemm(qx, sx, q32, s32, "fprop", "32x32", out=_nan_filled(T, F))
+        _assert_every_tile_written(Y, f"stack 32x32 {name} fprop")
+        # forward: B = W [F, H], tile row n/32 scales output column n
+        _contract_sample(f"stack 32x32 {name} fprop", Y, ox, osx, o32, os32, oracle.BKIND_TILE,
+                         o32, np.repeat(os32, 32, axis=0), rng)
+        del Y, qx, sx, ox, osx
         qd, sd = mx.quant(dY, "row")
-        dX = mx.gemm(qd, sd, q32, s32, "dgrad", "32x32")
-        torch.cuda.synchronize()
-        _end_to_end(f"stack 32x32 {name} dgrad", dX, dY, "row", Wt, "tile_t", oracle.BKIND_TILE_T,
-                    _sample(T, 24, rng, _corners(T)), _groups32(H, 2, rng))
-        del dX, qd, sd
+        od, osd = oracle.quant_row(bits(dY))
+        dX = mx.gemm(qd, sd, q32, s32, "dgrad", "32x32", out=_nan_filled(T, H))
+        _assert_every_tile_written(dX, f"stack 32x32 {name} dgrad")
+        # backward: output column n is input feature n of W [F, H]; in row
+        # form B = W^T [H, F] with tile column n/32's scales along F
+        _contract_sample(f"stack 32x32 {name} dgrad", dX, od, osd, o32, os32, oracle.BKIND_TILE_T,
+                         np.ascontiguousarray(o32.T), np.repeat(np.ascontiguousarray(os32.T), 32, axis=0),
+                         rng)
+        del dX, qd, sd, od, osd
 
 
 # --------------------------------------------------------------------------
