@@ -429,8 +429,13 @@ mx_status mx_grouped_gemm_wgrad_elem(mx_elem_type a_elem, mx_elem_type b_elem, i
   int dev;
   mx_status st = current_device(&dev);
   if (st != MX_OK) return st;
+  int cus;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    cus = g_num_cus[dev];
+  }
   hipError_t e = mx::launch_grouped_wgrad((int)a_elem, (int)b_elem, G, offsets, T, M, N, cap, a, sa,
-                                          b, sb, c, stream);
+                                          b, sb, c, cus, stream);
   if (e != hipSuccess) return hip_fail(e, "grouped wgrad kernel launch");
   return MX_OK;
 }

@@ -106,6 +106,16 @@ __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F7
 // (the L2 prefetches, which nobody waits for) has completed.
 __device__ __forceinline__ void wait_vm_but_prefetch() { __builtin_amdgcn_s_waitcnt(0x0F72); }
 
+// s_waitcnt vmcnt(N) for any N < 64 (gfx9 encoding: the count's low four
+// bits in [3:0], its high two in [15:14]; expcnt and lgkmcnt at their maxima).
+// Vector-memory loads and stores retire in order, so this waits for every
+// vector-memory op but the N most recent.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
 // L2 prefetch: one dword per lane (one 128-byte line per row) dropped into a
 // scratch LDS area that is never read.  LDS-DMA has no register destination,
 // so nothing in the kernel can race with the late arrival.
@@ -205,6 +215,75 @@ __device__ __forceinline__ void store_tile_bf16(const v16f (&acc)[4][4], uint16_
       }
     }
   }
+}
+
+// Epilogue of a 256x256 tile through LDS: the BF16 tile is first written to
+// the two (idle) stage buffers as 256 rows of 512 bytes, rows 0..127 in lo
+// and 128..255 in hi, 16-byte chunk c of row r at chunk c ^ (r & 31), and
+// then stored with each group of 32 lanes writing one whole 512-byte row
+// (four full cache lines) per instruction, instead of 32-byte pieces of 32
+// rows.  The caller has made every load of the stage buffers land and every
+// wave pass a barrier since its last read of them.  Ends with a barrier
+// (the stage buffers are free again afterwards).
+__device__ __forceinline__ void store_tile_bf16_lds(const v16f (&acc)[4][4], lds_u8* lo, lds_u8* hi,
+                                                    uint16_t* __restrict__ c, int64_t ldc, int64_t m0,
+                                                    int64_t m_end, int64_t n0, int64_t N, int wm,
+                                                    int wn, int wave, int lane) {
+  const int g = lane >> 5, i = lane & 31;
+  lds_u8* buf = wm ? hi : lo;
+#pragma unroll
+  for (int fn = 0; fn < 4; fn++) {
+#pragma unroll
+    for (int fm = 0; fm < 4; fm++) {
+      const v16f& v = acc[fn][fm];
+      uint32_t p[4][2];
+#pragma unroll
+      for (int r4 = 0; r4 < 4; r4++) {
+        p[r4][0] = cvt_pk_bf16(v[4 * r4 + 0], v[4 * r4 + 1]);
+        p[r4][1] = cvt_pk_bf16(v[4 * r4 + 2], v[4 * r4 + 3]);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; h++)
+#pragma unroll
+        for (int d = 0; d < 2; d++) {
+          const auto sw = __builtin_amdgcn_permlane32_swap(p[2 * h][d], p[2 * h + 1][d], false, false);
+          p[2 * h][d] = sw[0];
+          p[2 * h + 1][d] = sw[1];
+        }
+      // local row 32 fm + i of this wave's half; chunk (8 columns) 16 wn + 4 fn + 2 h + g
+      const int row = 32 * fm + i;
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+        const int chunk = 16 * wn + 4 * fn + 2 * h + g;
+        *(lds_v4i*)(buf + row * 512 + ((chunk ^ (row & 31)) << 4)) =
+            (v4i){(int)p[2 * h][0], (int)p[2 * h][1], (int)p[2 * h + 1][0], (int)p[2 * h + 1][1]};
+      }
+    }
+  }
+  __syncthreads();
+  // wave w stores rows 64 w .. 64 w + 63, two rows per instruction: lane l
+  // takes chunk l & 31 of row 64 w + 2 j + (l >> 5)
+  const bool vec_ok = (ldc & 7) == 0;
+  const int k = lane & 31;
+  const int64_t n = n0 + 8 * k;
+#pragma unroll 4
+  for (int j = 0; j < 32; j++) {
+    const int r = 64 * wave + 2 * j + (lane >> 5);  // tile row
+    const lds_u8* src = (r < 128 ? lo : hi) + (r & 127) * 512 + ((k ^ (r & 31)) << 4);
+    const v4i w = *(const lds_v4i*)src;
+    const int64_t m = m0 + r;
+    if (m >= m_end || n >= N) continue;
+    uint16_t* dst = c + m * ldc + n;
+    if (vec_ok && n + 8 <= N) {
+      *(uint4*)dst = make_uint4((uint32_t)w.x, (uint32_t)w.y, (uint32_t)w.z, (uint32_t)w.w);
+    } else {
+      const uint32_t ww[4] = {(uint32_t)w.x, (uint32_t)w.y, (uint32_t)w.z, (uint32_t)w.w};
+#pragma unroll
+      for (int e = 0; e < 8; e++)
+        if (n + e < N) dst[e] = (uint16_t)(ww[e >> 1] >> (16 * (e & 1)));
+    }
+  }
+  __syncthreads();
 }
 
 // Fused producer epilogue: the tile's BF16 result (the same values
