@@ -536,12 +536,15 @@ struct Tile {
       if (kt < nk)
         step(st0, st1, kt, wave, wm, wn, lane, sc_a, sc_b, nx_a, nx_b, f0a, f0b, f1a, f1b, acc);
     }
-    // no load may still be writing this workgroup's LDS when it ends
+    // no load may still be writing this workgroup's LDS when it ends (or
+    // when the stage buffers take the result)
     wait_vm_all();
-    if (OUT == 0)
-      store_tile_bf16(acc, c, N, m0, m_end, n0, N, wm, wn, lane);
-    else
+    if (OUT == 0) {
+      __syncthreads();  // every wave is past its last read of the stages
+      store_tile_bf16_lds(acc, st0, st1, c, N, m0, m_end, n0, N, wm, wn, wave, lane);
+    } else {
       store_tile_q<OUT - 1>(acc, q_out, s_out, N, m0, m_end, n0, N, wm, wn, lane);
+    }
   }
 };
 

@@ -11,7 +11,8 @@ namespace mx {
 hipError_t launch_quant_row(const void* x, int64_t n, void* q, void* s, int elem,
                             hipStream_t stream);
 
-// mode 1 = column (q_t, s_t), 2 = dual (q, s, q_t, s_t), 3 = 32x32 tiles (q, s);
+// mode 1 = column (q_t, s_t), 2 = dual (q, s, q_t, s_t), 3 = 32x32 tiles (q, s,
+// batch 1 only: a stack of tiled matrices is one taller matrix);
 // `batch` contiguous [R, C] matrices with contiguous outputs (grid.z).
 hipError_t launch_quant_tile(int mode, const void* x, int64_t R, int64_t C, void* q, void* s,
                              void* qt, void* st, int64_t batch, int elem, hipStream_t stream);

@@ -65,14 +65,53 @@ quant_row_kernel(const uint4* __restrict__ x, uint2* __restrict__ q, uint8_t* __
 }
 
 // ---------------------------------------------------------------------------
-// 2-D tile kernel for the column, dual-axis and 32x32 modes.
+// 32x32 tiles.  A wave owns 32 rows x 128 columns (four tiles side by side):
+// lane l = 16 r + c holds 16-byte chunk c of rows r, r + 4, ..., r + 28, so
+// every load instruction reads 256 contiguous bytes of each of four rows and
+// every store writes whole 128-byte lines of four payload rows.  A tile is
+// the 16 lanes with the same c / 4; its amax is a quad reduction (DPP) and
+// one exchange each with the lanes 16 and 32 away.  A workgroup of four
+// waves covers 128 rows x 128 columns.
+// ---------------------------------------------------------------------------
+constexpr int B32_THREADS = 256;
+
+template <int EL>
+__global__ void __launch_bounds__(B32_THREADS)
+quant_block32_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C, uint8_t* __restrict__ q,
+                     uint8_t* __restrict__ s) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15, rg = lane >> 4;
+  const int64_t r0 = (int64_t)blockIdx.x * 128 + 32 * wave;
+  const int64_t col = (int64_t)blockIdx.y * 128 + 8 * c;
+  // R and C are multiples of 32: a wave's 32 rows are all in or all out, and
+  // so are a tile's four chunks
+  if (r0 >= R) return;
+  const bool live = col < C;
+  uint4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++)
+    v[i] = live ? load_stream16(x + (r0 + rg + 4 * i) * C + col) : make_uint4(0, 0, 0, 0);
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) m = umax(m, chunk_absmax(v[i]));
+  m = quad_max(m);
+  m = xor_max(m, 16);
+  m = xor_max(m, 32);
+  const uint32_t sb = scale_byte_t<EL>(m);
+  if (!live) return;
+#pragma unroll
+  for (int i = 0; i < 8; i++) *(uint2*)(q + (r0 + rg + 4 * i) * C + col) = cvt8_t<EL>(v[i], sb);
+  if (rg == 0 && (c & 3) == 0) s[(r0 >> 5) * (C >> 5) + (col >> 5)] = (uint8_t)sb;
+}
+
+// ---------------------------------------------------------------------------
+// 2-D tile kernel for the column, dual-axis and grouped column modes.
 //
 // A workgroup of 8 waves covers 128 rows x 128 columns; wave w takes rows
 // 32*(w/2) .. +32 and columns 64*(w%2) .. +64.  In a wave, lane l = 8g + h
 // holds rows 4g .. 4g+3 and columns 8h .. 8h+7 as four 16-byte chunks, so
 // - a row block (32 columns) spans the 4 lanes h = 4b .. 4b+3 of one quad,
-// - a column block (32 rows) spans lanes h, h+8, ..., h+56 (xor 8, 16, 32),
-// - a 32x32 tile is one half of the wave (h < 4 or h >= 4).
+// - a column block (32 rows) spans lanes h, h+8, ..., h+56 (xor 8, 16, 32).
 // The column and dual modes stage their outputs in LDS (row payload
 // [128 rows][128 B], column payload [128 columns][128 B], 16-byte chunks
 // XOR-swizzled against bank conflicts, and both scale blocks) and then write
@@ -180,23 +219,6 @@ __device__ __forceinline__ void quant_tile(const uint16_t* __restrict__ x, int64
 #pragma unroll
     for (int i = 0; i < 4; i++)
       v[i] = live ? load_stream16(x + (r0 + 4 * g + i) * C + c) : make_uint4(0, 0, 0, 0);
-  }
-
-  if (MODE == TILE_BLOCK32) {
-    if (r0 >= R) return;  // no barrier below
-    uint32_t m = umax(umax(chunk_absmax(v[0]), chunk_absmax(v[1])),
-                      umax(chunk_absmax(v[2]), chunk_absmax(v[3])));
-    m = quad_max(m);
-    m = xor_max(m, 8);
-    m = xor_max(m, 16);
-    m = xor_max(m, 32);
-    uint32_t sb = scale_byte_t<EL>(m);
-    if (live) {
-#pragma unroll
-      for (int i = 0; i < 4; i++) *(uint2*)(q + (r0 + 4 * g + i) * C + c) = cvt8_t<EL>(v[i], sb);
-      if (g == 0 && (h & 3) == 0) s[(r0 >> 5) * (C >> 5) + (c >> 5)] = (uint8_t)sb;
-    }
-    return;
   }
 
   const int rl = 32 * wr + 4 * g;        // local row of this lane's first row
@@ -317,7 +339,7 @@ quant_tile_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C, uint8_t*
     const int64_t z = blockIdx.z, n = R * C;
     x += z * n;
     q += q ? z * n : 0;
-    s += s ? (MODE == TILE_BLOCK32 ? z * (n >> 10) : z * (n >> 5)) : 0;
+    s += s ? z * (n >> 5) : 0;
     qt += qt ? z * n : 0;
     st += st ? z * (n >> 5) : 0;
   }
@@ -423,9 +445,18 @@ hipError_t launch_quant_tile(int mode, const void* x, int64_t R, int64_t C, void
     case TILE_DUAL:
       launch_tile_elem<TILE_DUAL>(elem, grid, x, R, C, q, s, qt, st, 0, nullptr, 0, stream);
       break;
-    case TILE_BLOCK32:
-      launch_tile_elem<TILE_BLOCK32>(elem, grid, x, R, C, q, s, qt, st, 0, nullptr, 0, stream);
+    case TILE_BLOCK32: {
+      // one 256-thread workgroup per 128 x 128 block (grid.z == 1: a batch of
+      // 32x32-tiled matrices is one stacked matrix)
+      if (batch != 1) return hipErrorInvalidValue;
+      if (elem == ELEM_E5M2)
+        hipLaunchKernelGGL(quant_block32_kernel<ELEM_E5M2>, dim3(grid.x, grid.y), dim3(B32_THREADS), 0,
+                           stream, (const uint16_t*)x, R, C, (uint8_t*)q, (uint8_t*)s);
+      else
+        hipLaunchKernelGGL(quant_block32_kernel<ELEM_E4M3>, dim3(grid.x, grid.y), dim3(B32_THREADS), 0,
+                           stream, (const uint16_t*)x, R, C, (uint8_t*)q, (uint8_t*)s);
       break;
+    }
     default:
       return hipErrorInvalidValue;
   }
