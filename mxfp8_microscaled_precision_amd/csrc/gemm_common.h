@@ -263,9 +263,40 @@ __device__ __forceinline__ void store_tile_bf16_lds(const v16f (&acc)[4][4], lds
   __syncthreads();
   // wave w stores rows 64 w .. 64 w + 63, two rows per instruction: lane l
   // takes chunk l & 31 of row 64 w + 2 j + (l >> 5)
-  const bool vec_ok = (ldc & 7) == 0;
   const int k = lane & 31;
   const int64_t n = n0 + 8 * k;
+  if (((ldc | N) & 7) == 0 && (int64_t)BM * ldc * 2 < (int64_t)OOB) {
+    // Rows 16-byte aligned and whole 8-column chunks: eight LDS reads, then
+    // eight buffer stores, with no branches; rows past m_end and chunks past
+    // N get an offset past the descriptor's range and store nothing.  (One
+    // read, wait and store per row costs an LDS round trip per row.)
+    const int64_t mrows = m_end - m0;
+    const uint64_t base = (uint64_t)(uintptr_t)(c + m0 * ldc);
+    const uint32_t blo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base);
+    const uint32_t bhi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32));
+    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(uintptr_t)(((uint64_t)bhi << 32) | blo), 0,
+        __builtin_amdgcn_readfirstlane((int)(mrows * ldc * 2)), 0x00020000);
+    const bool col_ok = n < N;
+#pragma unroll
+    for (int jb = 0; jb < 32; jb += 8) {
+      v4i w[8];
+#pragma unroll
+      for (int u = 0; u < 8; u++) {
+        const int r = 64 * wave + 2 * (jb + u) + (lane >> 5);
+        w[u] = *(const lds_v4i*)((r < 128 ? lo : hi) + (r & 127) * 512 + ((k ^ (r & 31)) << 4));
+      }
+#pragma unroll
+      for (int u = 0; u < 8; u++) {
+        const int r = 64 * wave + 2 * (jb + u) + (lane >> 5);
+        const uint32_t off = (r < mrows && col_ok) ? (uint32_t)(((int64_t)r * ldc + 8 * k + n0) * 2) : OOB;
+        __builtin_amdgcn_raw_buffer_store_b128(w[u], rc, (int)off, 0, 0);
+      }
+    }
+    __syncthreads();
+    return;
+  }
+  const bool vec_ok = (ldc & 7) == 0;
 #pragma unroll 4
   for (int j = 0; j < 32; j++) {
     const int r = 64 * wave + 2 * j + (lane >> 5);  // tile row
