@@ -26,8 +26,10 @@
  *     offsets, so the contraction length is limited: K < 2^23 for mx_gemm,
  *     mx_gemm_elem, mx_gemm_quant and mx_grouped_gemm(_elem), (K + 256) * N
  *     < 2^31 for the 32x32 dgrad's transposed weight, and 256 * cap < 2^31
- *     for the per-group token capacity of the MoE backward; beyond that
- *     they return MX_ERR_UNSUPPORTED_SHAPE.
+ *     for the per-group token capacity of the MoE backward; the grouped
+ *     GEMM numbers its 256x256 output tiles with 32-bit indices, so
+ *     (ceil(T / 256) + G) * ceil(N / 256) < 2^31.  Beyond that they return
+ *     MX_ERR_UNSUPPORTED_SHAPE.
  *   - The current device must be gfx950; otherwise calls return
  *     MX_ERR_UNSUPPORTED_DEVICE (the pages' init-time hardware gate:
  *     torchtitan-npu MXFP8/HiF8 tutorial, "hardware requirement").

@@ -282,6 +282,9 @@ mx_status mx_grouped_gemm_elem(mx_elem_type a_elem, mx_elem_type b_elem, int64_t
   if (K % 32 != 0) return fail(MX_ERR_UNSUPPORTED_SHAPE, "K %lld is not a multiple of 32", (long long)K);
   if (K >= K_LIMIT)
     return fail(MX_ERR_UNSUPPORTED_SHAPE, "K %lld too large for 32-bit tile offsets", (long long)K);
+  if (((T + 255) / 256 + G) * ((N + 255) / 256) >= ((int64_t)1 << 31))
+    return fail(MX_ERR_UNSUPPORTED_SHAPE, "grouped GEMM of %lld x %lld needs 2^31 tiles or more",
+                (long long)T, (long long)N);
   if (T == 0 || N == 0) return MX_OK;
   if (!offsets || !c) return fail(MX_ERR_INVALID_ARG, "offsets or c is NULL");
   if (K > 0 && (!a || !sa || !b || !sb)) return fail(MX_ERR_INVALID_ARG, "an operand is NULL");

@@ -632,22 +632,30 @@ grouped_gemm_kernel(int64_t G, const int64_t* __restrict__ offsets, int64_t T, i
   // contiguous tile runs per XCD
   const int64_t nwg = gridDim.x, bid = blockIdx.x;
   const int64_t wg = (bid & 7) * (nwg >> 3) + (bid >> 3);
-  for (int64_t t = wg; t < total; t += nwg) {
-    int64_t lo = 0, hi = G;  // largest g with s_pre[g] <= t
-    while (hi - lo > 1) {
-      int64_t mid = (lo + hi) >> 1;
-      if (s_pre[mid] <= t) lo = mid; else hi = mid;
+  // tile indices fit in 32 bits (the host checks the tile count), so the
+  // per-tile arithmetic below is 32-bit
+  const uint32_t span = GM_TILES * (uint32_t)nn;
+  int64_t g = 0;  // largest g with s_pre[g] <= t: searched once, then advanced
+  {
+    int64_t hi = G;
+    while (hi - g > 1) {
+      const int64_t mid = (g + hi) >> 1;
+      if (s_pre[mid] <= wg) g = mid; else hi = mid;
     }
-    const int64_t g = lo;
+  }
+  for (int64_t t = wg; t < total; t += nwg) {
+    while (s_pre[g + 1] <= t) g++;  // s_pre[G] = total > t stops it
     // inside group g, the same grouped order as the dense kernel: runs of
     // GM_TILES m-tiles, n-tiles outer, so 32 consecutive tiles cover
     // GM_TILES m-tiles x (32 / GM_TILES) n-tiles
-    const int64_t local = t - s_pre[g];
-    const int64_t nmg = (s_off[g + 1] - s_off[g] + BM - 1) / BM;
-    const int64_t first = local / (GM_TILES * nn) * GM_TILES;
-    const int64_t gsz = (nmg - first) < GM_TILES ? (nmg - first) : GM_TILES;
-    const int64_t in = local % (GM_TILES * nn);
-    const int64_t mt = first + in % gsz, nt = in / gsz;
+    const uint32_t local = (uint32_t)(t - s_pre[g]);
+    const uint32_t nmg = (uint32_t)((s_off[g + 1] - s_off[g] + BM - 1) / BM);
+    const uint32_t run = local / span;
+    const uint32_t first = run * GM_TILES;
+    const uint32_t gsz = (nmg - first) < (uint32_t)GM_TILES ? (nmg - first) : (uint32_t)GM_TILES;
+    const uint32_t in = local - run * span;
+    const uint32_t nt = in / gsz;
+    const int64_t mt = first + (in - nt * gsz);
     Tile<GEMM_B_ROW, FAST, FA, FB, 0, false> tl;
     tl.a = a;
     tl.sa = sa;
@@ -656,7 +664,7 @@ grouped_gemm_kernel(int64_t G, const int64_t* __restrict__ offsets, int64_t T, i
     tl.c = c;
     tl.m0 = s_off[g] + mt * BM;
     tl.m_end = (tl.m0 + BM) < s_off[g + 1] ? tl.m0 + BM : s_off[g + 1];
-    tl.n0 = nt * BN;
+    tl.n0 = (int64_t)nt * BN;
     tl.N = N;
     tl.K = K;
     tl.nkb = K >> 5;
@@ -794,6 +802,7 @@ hipError_t launch_grouped_gemm(int a_elem, int b_elem, int64_t G, const int64_t*
   if ((a_elem != 0 && a_elem != 1) || (b_elem != 0 && b_elem != 1)) return hipErrorInvalidValue;
   const int64_t nn = (N + BN - 1) / BN;
   const int64_t upper = ((T + BM - 1) / BM + G) * nn;
+  if (upper >= ((int64_t)1 << 31)) return hipErrorInvalidValue;  // the host rejects it first
   int64_t wgs = num_cus > 0 ? num_cus : 256;
   wgs = (wgs + 7) / 8 * 8;
   if (upper < wgs) wgs = (upper + 7) / 8 * 8;

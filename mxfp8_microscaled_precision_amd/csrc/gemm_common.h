@@ -379,25 +379,29 @@ __device__ __forceinline__ void store_tile_q(const v16f (&acc)[4][4], uint8_t* _
 // respectively than the other choice on the workload shapes).
 __device__ __forceinline__ void tile_of(int64_t bid, int64_t nm, int64_t nn, int64_t& mt,
                                         int64_t& nt) {
-  const int64_t total = nm * nn;
-  const int64_t x = bid & 7, local = bid >> 3;
-  int64_t t;
-  if (nn <= 32) {
+  // a grid has fewer than 2^24 workgroups of 256 threads (the host rejects
+  // grids of 2^32 work-items), so tile indices fit in 32 bits
+  const uint32_t b = (uint32_t)bid, m = (uint32_t)nm, n = (uint32_t)nn;
+  const uint32_t total = m * n;
+  const uint32_t x = b & 7, local = b >> 3;
+  uint32_t t;
+  if (n <= 32) {
     // runs of 32 round-robin over the XCDs; the tail past the last whole
     // 256 tiles keeps its position, so the map stays a bijection
-    const int64_t full = total & ~(int64_t)255;
-    t = bid < full ? (((local >> 5) << 3) + x) * 32 + (local & 31) : bid;
+    const uint32_t full = total & ~255u;
+    t = b < full ? (((local >> 5) << 3) + x) * 32 + (local & 31) : b;
   } else {
-    const int64_t per = total >> 3, rem = total & 7;
+    const uint32_t per = total >> 3, rem = total & 7;
     t = x * per + (x < rem ? x : rem) + local;
   }
-  constexpr int64_t GM = GM_TILES;
-  const int64_t group = t / (GM * nn);
-  const int64_t first = group * GM;
-  const int64_t gsz = (nm - first) < GM ? (nm - first) : GM;
-  const int64_t in = t % (GM * nn);
-  mt = first + in % gsz;
-  nt = in / gsz;
+  const uint32_t span = GM_TILES * n;
+  const uint32_t group = t / span;
+  const uint32_t first = group * GM_TILES;
+  const uint32_t gsz = (m - first) < (uint32_t)GM_TILES ? (m - first) : (uint32_t)GM_TILES;
+  const uint32_t in = t - group * span;
+  const uint32_t q = in / gsz;
+  mt = first + (in - q * gsz);
+  nt = q;
 }
 
 }  // namespace mx

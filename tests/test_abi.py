@@ -102,6 +102,8 @@ def test_gemm_empty_is_noop():
     ((4, 1, 4, 8, 40, 1, 1, 1, 1, 1, 0, 0, 0), SHAPE),       # K % 32
     ((4, 0, 4, 8, 32, 1, 1, 1, 1, 1, 0, 0, 0), INVALID),     # NULL offsets
     ((4, 1, 4, 8, 1 << 23, 1, 1, 1, 1, 1, 0, 0, 0), SHAPE),  # K beyond 32-bit tile offsets
+    ((4, 1, 1 << 40, 1 << 15, 32, 1, 1, 1, 1, 1, 0, 0, 0), SHAPE),  # 2^31 or more output tiles
+    ((4, 1, (1 << 31) - 4 * 256, 1 << 16, 32, 1, 1, 1, 1, 1, 0, 0, 0), SHAPE),  # exactly 2^31 tiles
 ])
 def test_grouped_validation(args, status):
     assert mx.mx_grouped_gemm(*args) == status
