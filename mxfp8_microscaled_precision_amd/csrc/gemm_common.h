@@ -277,19 +277,28 @@ __device__ __forceinline__ void store_tile_bf16_lds(const v16f (&acc)[4][4], lds
     const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(uintptr_t)(((uint64_t)bhi << 32) | blo), 0,
         __builtin_amdgcn_readfirstlane((int)(mrows * ldc * 2)), 0x00020000);
-    const bool col_ok = n < N;
+    // row r = r0 + 2 j of this lane: byte offset off0 + j * step2, stored
+    // while 2 j < lim.  off0 is made opaque so that nothing derived from it
+    // is hoisted out of a caller's loop over tiles (32 row offsets held
+    // across the K loop would spill).
+    const int r0 = 64 * wave + (lane >> 5);
+    uint32_t row2 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(ldc * 2));
+    uint32_t off0 = (uint32_t)r0 * row2 + (uint32_t)(8 * k) * 2 + (uint32_t)__builtin_amdgcn_readfirstlane((int)(n0 * 2));
+    int lim = n < N ? (int)mrows - r0 : 0;
+    asm volatile("" : "+s"(row2), "+v"(off0), "+v"(lim));
+    const uint32_t step2 = 2 * row2;
 #pragma unroll
     for (int jb = 0; jb < 32; jb += 8) {
       v4i w[8];
 #pragma unroll
       for (int u = 0; u < 8; u++) {
-        const int r = 64 * wave + 2 * (jb + u) + (lane >> 5);
+        const int r = r0 + 2 * (jb + u);
         w[u] = *(const lds_v4i*)((r < 128 ? lo : hi) + (r & 127) * 512 + ((k ^ (r & 31)) << 4));
       }
 #pragma unroll
       for (int u = 0; u < 8; u++) {
-        const int r = 64 * wave + 2 * (jb + u) + (lane >> 5);
-        const uint32_t off = (r < mrows && col_ok) ? (uint32_t)(((int64_t)r * ldc + 8 * k + n0) * 2) : OOB;
+        const int j = jb + u;
+        const uint32_t off = 2 * j < lim ? off0 + (uint32_t)j * step2 : OOB;
         __builtin_amdgcn_raw_buffer_store_b128(w[u], rc, (int)off, 0, 0);
       }
     }
@@ -315,6 +324,97 @@ __device__ __forceinline__ void store_tile_bf16_lds(const v16f (&acc)[4][4], lds
     }
   }
   __syncthreads();
+}
+
+// The tile's BF16 result through ONE 64 KB LDS buffer, half at a time, so
+// that the other stage buffer can take the next tile's first loads while the
+// result leaves.  Half h holds fragment rows fm = 2h, 2h + 1 of every wave,
+// i.e. tile rows 128 wm + 64 h .. + 63 for wm = 0, 1 (all four waves convert
+// in both halves); its local row lr is tile row 128 (lr / 64) + 64 h +
+// lr % 64.  Every wave issues exactly 32 buffer stores, none skipped (rows
+// past m_end and chunks past N take an offset past the descriptor's range),
+// so a caller can count them in vmcnt.  Requires ldc % 8 == 0, N % 8 == 0
+// and 256 * ldc * 2 < 2^31 (the caller checks).  Ends with a barrier.
+__device__ __forceinline__ void store_tile_bf16_lds_halves(const v16f (&acc)[4][4], lds_u8* buf,
+                                                           uint16_t* __restrict__ c, int64_t ldc,
+                                                           int64_t m0, int64_t m_end, int64_t n0,
+                                                           int64_t N, int wm, int wn, int wave,
+                                                           int lane) {
+  const int g = lane >> 5, i = lane & 31;
+  const int k = lane & 31;
+  const int64_t mrows = m_end - m0;
+  const uint64_t base = (uint64_t)(uintptr_t)(c + m0 * ldc);
+  const uint32_t blo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base);
+  const uint32_t bhi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32));
+  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(uintptr_t)(((uint64_t)bhi << 32) | blo), 0,
+      __builtin_amdgcn_readfirstlane((int)(mrows * ldc * 2)), 0x00020000);
+  // store j (< 16) of half h: local row lr = 32 wave + 2 j + lane / 32, tile
+  // row tr = 128 (wave / 2) + 64 h + (lr % 64); the byte offset is
+  // off0 + (64 h + 2 j) row2 and the row is stored while 64 h + 2 j < lim
+  const int lr0 = 32 * wave + (lane >> 5);
+  const int tr0 = 128 * (wave >> 1) + (lr0 & 63);
+  uint32_t row2 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(ldc * 2));
+  uint32_t off0 = (uint32_t)tr0 * row2 + (uint32_t)(8 * k) * 2 +
+                  (uint32_t)__builtin_amdgcn_readfirstlane((int)(n0 * 2));
+  int lim = n0 + 8 * k < N ? (int)mrows - tr0 : 0;
+  // opaque: a caller's loop over tiles must not hoist the 32 row offsets
+  // derived from these (they would be held across its K loop and spill)
+  asm volatile("" : "+s"(row2), "+v"(off0), "+v"(lim));
+#pragma unroll
+  for (int h = 0; h < 2; h++) {
+#pragma unroll
+    for (int fn = 0; fn < 4; fn++) {
+#pragma unroll
+      for (int f2 = 0; f2 < 2; f2++) {
+        const v16f& v = acc[fn][2 * h + f2];
+        uint32_t p[4][2];
+#pragma unroll
+        for (int r4 = 0; r4 < 4; r4++) {
+          p[r4][0] = cvt_pk_bf16(v[4 * r4 + 0], v[4 * r4 + 1]);
+          p[r4][1] = cvt_pk_bf16(v[4 * r4 + 2], v[4 * r4 + 3]);
+        }
+#pragma unroll
+        for (int hh = 0; hh < 2; hh++)
+#pragma unroll
+          for (int d = 0; d < 2; d++) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(p[2 * hh][d], p[2 * hh + 1][d], false, false);
+            p[2 * hh][d] = sw[0];
+            p[2 * hh + 1][d] = sw[1];
+          }
+        const int row = 64 * wm + 32 * f2 + i;  // local row
+#pragma unroll
+        for (int hh = 0; hh < 2; hh++) {
+          const int chunk = 16 * wn + 4 * fn + 2 * hh + g;
+          *(lds_v4i*)(buf + row * 512 + ((chunk ^ (row & 31)) << 4)) =
+              (v4i){(int)p[2 * hh][0], (int)p[2 * hh][1], (int)p[2 * hh + 1][0], (int)p[2 * hh + 1][1]};
+        }
+        // one fragment at a time: reading every fragment's accumulators
+        // ahead would hold them all in vector registers
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int jb = 0; jb < 16; jb += 4) {
+      v4i w[4];
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const int lr = lr0 + 2 * (jb + u);
+        w[u] = *(const lds_v4i*)(buf + lr * 512 + ((k ^ (lr & 31)) << 4));
+      }
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const int j = jb + u;
+        uint32_t off = 64 * h + 2 * j < lim ? off0 + (uint32_t)(64 * h + 2 * j) * row2 : OOB;
+        // an opaque offset: the store is issued on every lane, never turned
+        // into a masked (possibly skipped) one
+        asm volatile("" : "+v"(off));
+        __builtin_amdgcn_raw_buffer_store_b128(w[u], rc, (int)off, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
 }
 
 // Fused producer epilogue: the tile's BF16 result (the same values

@@ -18,13 +18,12 @@
 // staged per group of four K steps: a [256 rows][16 B] tile for A and one for
 // B (four bytes per row per step), double-buffered, loaded with
 // buffer_load_dword ... lds where one instruction covers 16 rows x 4 steps
-// (16 cache lines instead of 64 for one step of 64 rows).  A workgroup runs
-// one tile; groups differ in length, so
-// the experts are taken longest first (up to 128 groups; the rank of each is
-// counted in LDS) and the hardware's in-order dispatch balances the rest by
-// giving the short tiles to the CUs that free up last; consecutive
-// workgroups (dealt round-robin to the 8 XCDs) take contiguous runs of one
-// expert's tile order per XCD so that tiles sharing rows share an L2.
+// (16 cache lines instead of 64 for one step of 64 rows).  The kernel is
+// persistent (one workgroup per compute unit walks its tiles): groups differ
+// in length, so the experts are dealt longest first to groups of
+// workgroups, each to the group with the least work so far; the workgroups
+// on one XCD take contiguous runs of an expert's tile order so that tiles
+// sharing rows share an L2.
 #include "gemm_common.h"
 
 namespace mx {
@@ -32,7 +31,6 @@ namespace mx {
 constexpr int W_STAGE = A_TILE + B_TILE;   // 64 KB of payload per K step
 constexpr int W_SCALES = (BM + BN) * 16;   // A then B scales of four K steps: 8 KB
 constexpr int W_MAX_GROUPS = 512;
-constexpr int W_LPT_GROUPS = 128;           // longest-first expert order up to this many groups
 
 // FA / FB: element formats of A (the gradient) and B (the input).
 template <int FA, int FB>
@@ -40,13 +38,13 @@ struct WTile {
   u32x4 ra, rb;                     // the tile's whole rows of A and B
   u32x4 rsa, rsb;                   // their scale rows from the group's first column
   uint32_t kb;                      // the group's first column P
-  uint32_t kb2;                     // the first column of the expert prefetched for
+  uint32_t kb2;                     // the first column of the next tile's expert
   uint32_t voff_a, voff_b, rows32;  // chunk offset of this lane; offset of 32 rows
   uint32_t rows16;                  // scale offset of one row
   uint32_t svoff;                   // scale offset of this lane: row 64 wave + lane/4, step lane%4
   uint32_t pf_row, pf_a, pf_b;      // L2 prefetch: row offset, enable (0) or OOB
   int64_t nk;                       // K steps of the group
-  uint32_t nk2;                     // K steps of the expert prefetched for (0: none)
+  uint32_t nk2;                     // K steps of the next tile's expert (0: none)
   lds_u8* st0;
   lds_u8* st1;
   lds_u8* ss;                       // two scale tiles of W_SCALES bytes
@@ -106,10 +104,10 @@ struct WTile {
   }
 
   // L2 prefetch of K step kt (one line per row of this wave's 64 rows of A
-  // and of B).  Past the group's end, the slots serve the expert whose tiles
-  // the workgroups after this one on the XCD take over: steps kt = nk,
-  // nk + 1, nk + 2 fetch its first three steps, so its first stages come
-  // from L2.  Either way two ops per call.
+  // and of B).  Past the group's end, the slots serve the workgroup's next
+  // tile when it covers the same rows for a later expert (nk2 > 0): steps
+  // kt = nk, nk + 1, nk + 2 fetch its first three steps, so its first
+  // stages come from L2.  Either way two ops per call.
   __device__ __forceinline__ void prefetch(int64_t kt, int wave) {
     const bool cur = kt < nk;
     const uint32_t j = (uint32_t)(kt - nk);  // step of the next expert
@@ -195,25 +193,38 @@ struct WTile {
     }
   }
 
-  __device__ __forceinline__ void run(v16f (&acc)[4][4], int wave, int lane) {
+  // Stages 0 and 1 are requested together (a tile here runs only a few K
+  // steps, so the second stage's latency would otherwise be paid once more
+  // per tile): issue_first() loads stage 0 and the first scale group (24
+  // ops per wave), issue_second() stage 1 and the next scale part (18 ops).
+  __device__ __forceinline__ void issue_first(int wave, int lane) {
+    issue(st0, 0, wave);
+#pragma unroll
+    for (int u = 0; u < 4; u++) issue_scales(0, u, wave, lane);
+  }
+  __device__ __forceinline__ void issue_second(int wave, int lane) {
+    issue(st1, 1, wave);
+    issue_scales(1, 0, wave, lane);  // the part step -1 would load
+  }
+
+  // The tile after issue_first() and issue_second(); `stored`: 32 stores
+  // per wave were issued between the two.  Waits for stage 0 only (all but
+  // the ops issued after it).  Steps past the group's end (nk == 0
+  // included) touch no memory.
+  __device__ __forceinline__ void run_issued(v16f (&acc)[4][4], int wave, int lane, bool stored) {
     const int wm = wave & 1, wn = wave >> 1;
 #pragma unroll
     for (int x = 0; x < 4; x++)
 #pragma unroll
       for (int y = 0; y < 4; y++) acc[x][y] = (v16f){};
+    if (stored)
+      wait_vm<32 + 2 * CHUNKS + 2>();
+    else
+      wait_vm<2 * CHUNKS + 2>();
+    __syncthreads();
     if (nk == 0) return;
     uint32_t sc_a[4], sc_b[4];
     v8i f0a[4], f0b[4], f1a[4], f1b[4];
-    // Stages 0 and 1 are requested together (a tile here runs only a few
-    // K steps, so the second stage's latency would otherwise be paid once
-    // more per tile); the wait lets stage 1's 18 loads stay in flight.
-    issue(st0, 0, wave);
-#pragma unroll
-    for (int u = 0; u < 4; u++) issue_scales(0, u, wave, lane);
-    issue(st1, 1, wave);
-    issue_scales(1, 0, wave, lane);  // the part step -1 would load
-    wait_vm<2 * CHUNKS + 2>();  // all but stage 1's 16 payload and 2 scale loads
-    __syncthreads();
     read_scales(0, wm, wn, lane, sc_a, sc_b);
     prefetch(2, wave);  // the steps' vmcnt(2) waits assume the latest two ops are prefetches
     read_frags<0>(st0, wm, wn, lane, f0a, f0b);
@@ -227,11 +238,10 @@ struct WTile {
   }
 };
 
-// Largest of the wave's keys below `below` (0 if none): the maximum within
-// each row of 16 lanes by DPP (quad permutations, then rotations by 4 and 8
-// lanes), then over the four rows' lanes 0, 16, 32, 48.
-__device__ __forceinline__ uint32_t wave_max_below(const uint32_t (&key)[2], uint32_t below) {
-  uint32_t m = umax(key[0] < below ? key[0] : 0u, key[1] < below ? key[1] : 0u);
+// Largest of the wave's values: the maximum within each row of 16 lanes by
+// DPP (quad permutations, then rotations by 4 and 8 lanes), then over the
+// four rows' lanes 0, 16, 32, 48.
+__device__ __forceinline__ uint32_t wave_max(uint32_t m) {
   m = umax(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false));   // [1,0,3,2]
   m = umax(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, false));   // [2,3,0,1]
   m = umax(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x124, 0xF, 0xF, false));  // row_ror:4
@@ -240,142 +250,178 @@ __device__ __forceinline__ uint32_t wave_max_below(const uint32_t (&key)[2], uin
               umax((uint32_t)__builtin_amdgcn_readlane((int)m, 32), (uint32_t)__builtin_amdgcn_readlane((int)m, 48)));
 }
 
-// The expert at position pos of the longest-first order (K steps
-// descending, ties by index) and the one `ahead` positions further on, with
-// their token ranges [lo, hi), found by each wave on its own without LDS or
-// barriers: lane l holds experts l and 64 + l (G <= 128) as 24-bit keys
-// (steps << 8 | 255 - index, all distinct, larger first).  A radix select
-// walks the key bits, from the top bit of the largest key down, one ballot
-// per bit, to the key with exactly `pos` larger keys; each later position is
-// the largest key below the previous one.  Past the last expert, or with
-// ahead == 0, g2 = -1.
-// Offsets are clamped into [0, T] (a decrease reads as an empty group); T
-// is below 2^23 (the token capacity limit), so steps fit 16 bits and ranges
-// 32 bits.
-__device__ __forceinline__ void lpt_experts(const int64_t* __restrict__ offsets, int64_t G, int64_t T,
-                                            int64_t pos, int64_t ahead, int lane, int64_t& g,
-                                            int64_t& lo, int64_t& hi, int64_t& g2, int64_t& lo2,
-                                            int64_t& hi2) {
-  int l[2], r[2];
-  uint32_t key[2];
-#pragma unroll
-  for (int h = 0; h < 2; h++) {
-    const int64_t gg = 64 * h + lane;
-    int64_t a = 0, b = 0;
-    if (gg < G) {
-      a = offsets[gg];
-      b = offsets[gg + 1];
-    }
-    a = a < 0 ? 0 : (a > T ? T : a);
-    b = b < a ? a : (b > T ? T : b);
-    l[h] = (int)a;
-    r[h] = (int)b;
-    // experts past G get key 0, below every real key (those are >= 128)
-    key[h] = gg < G ? ((uint32_t)((b - a + BK - 1) / BK) << 8) | (uint32_t)(255 - gg) : 0u;
-  }
-  // the answer's bits above bit b are `prefix`; `want` keys larger than the
-  // answer are still to be passed among the keys that share that prefix
-  const uint32_t top = wave_max_below(key, 0xFFFFFFFFu);
-  uint32_t prefix = 0;
-  int want = (int)pos;
-  for (int b = 31 - __builtin_clz(top | 1u); b >= 0; b--) {
-    const uint32_t hi_half = (prefix >> b) | 1u;  // prefix with bit b set, shifted down
-    const int cnt = __popcll(__ballot((key[0] >> b) == hi_half)) +
-                    __popcll(__ballot((key[1] >> b) == hi_half));
-    if (cnt > want)
-      prefix |= 1u << b;
-    else
-      want -= cnt;
-  }
-  uint32_t next = ahead ? prefix : 0u;
-  for (int64_t k = 0; k < ahead && next; k++) next = wave_max_below(key, next);
-  const int idx = 255 - (int)(prefix & 255u), idx2 = 255 - (int)(next & 255u);
-  g = idx;
-  lo = __builtin_amdgcn_readlane(idx >> 6 ? l[1] : l[0], idx & 63);
-  hi = __builtin_amdgcn_readlane(idx >> 6 ? r[1] : r[0], idx & 63);
-  g2 = next ? idx2 : -1;
-  lo2 = __builtin_amdgcn_readlane(idx2 >> 6 ? l[1] : l[0], idx2 & 63);
-  hi2 = __builtin_amdgcn_readlane(idx2 >> 6 ? r[1] : r[0], idx2 & 63);
-}
+// Work of one tile in K steps when experts are dealt to groups: its steps
+// plus the fixed cost of starting and storing a tile.
+constexpr uint32_t W_TILE_COST = 4;
 
-template <int FA, int FB>
+// Persistent: the grid's workgroups walk the tiles (G experts x `per`
+// output tiles of 256 x 256), so the expert order is worked out once per
+// workgroup, no workgroup launch sits between two tiles, and the next tile
+// of a workgroup is known while the current one runs (its first K steps are
+// prefetched into L2 by the current tile's last steps).
+//   groups > 0: the grid is groups x per workgroups; workgroup w keeps
+//     output tile u = w % per of every expert dealt to its group w / per.
+//     The experts, longest first (K steps descending, index ascending), go
+//     one by one to the group with the least work so far (lowest index on
+//     ties), which balances the groups the way list scheduling would.  Every
+//     workgroup computes the same deal and keeps its own group's list.
+//   groups == 0: workgroup w takes tiles w, w + grid, ... of the
+//     expert-major tile order.
+// Tile u of an expert: with per % 8 == 0 the workgroups on XCD x (w % 8)
+// take the contiguous run x * per/8 .. of the expert's grouped tile order
+// (GM_TILES m-tiles, n-tiles outer), so tiles that share rows share an L2.
+template <int FA, int FB, bool OVERLAP>
 __global__ void __launch_bounds__(NT)
 grouped_wgrad_kernel(int64_t G, const int64_t* __restrict__ offsets, int64_t T, int64_t M,
                      int64_t N, int64_t ld, const uint8_t* __restrict__ a,
                      const uint8_t* __restrict__ sa, const uint8_t* __restrict__ b,
-                     const uint8_t* __restrict__ sb, uint16_t* __restrict__ c, int xcd_cus) {
+                     const uint8_t* __restrict__ sb, uint16_t* __restrict__ c, int groups) {
   __shared__ __attribute__((aligned(16))) uint8_t smem0[W_STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t smem1[W_STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t sscale[2 * W_SCALES];
   __shared__ __attribute__((aligned(16))) uint8_t spf[2048];
+  __shared__ int s_lo[W_MAX_GROUPS], s_hi[W_MAX_GROUPS];  // token ranges
+  __shared__ uint32_t s_key[W_MAX_GROUPS];  // K steps << 9 | 511 - expert: distinct, larger first
+  __shared__ short s_order[W_MAX_GROUPS];   // expert at each position of the longest-first order
+  __shared__ short s_list[W_MAX_GROUPS];    // this workgroup's experts, in the order it runs them
+  __shared__ int s_cnt;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nm = (M + BM - 1) / BM, nn = (N + BN - 1) / BN, per = nm * nn;
-  const int64_t t = blockIdx.x, pos_g = t / per, u = t % per;
-  // Which expert: with at most W_LPT_GROUPS groups and fewer tiles per expert
-  // than compute units, position pos_g of the experts ordered by K steps,
-  // longest first (ties by index), so the longest tiles start first and the
-  // short ones fill in at the end; otherwise expert pos_g.  lo, hi: its
-  // token range.
-  // XCD x = u % 8 takes the contiguous run x * per/8 .. of the group's order
-  const int64_t run = per >> 3;
-  // The workgroups that replace this one on its XCD's compute units take the
-  // same run of the expert xcd_cus / run positions further on (an XCD runs
-  // that many experts' runs at once); its first K steps are prefetched when
-  // that is at most four positions on (0: no prefetch).
-  int64_t ahead = (per & 7) == 0 ? (xcd_cus / run > 1 ? xcd_cus / run : 1) : 0;
-  ahead = ahead <= 4 ? ahead : 0;
-  int64_t g = pos_g, lo, hi, g2 = ahead ? pos_g + ahead : G, lo2 = 0, hi2 = 0;
-  // When one expert's tiles occupy every compute unit at least once, each
-  // expert is a round of its own and the order does not change the balance:
-  // index order, no search.
-  if (G <= W_LPT_GROUPS && per < 8 * (int64_t)xcd_cus) {
-    lpt_experts(offsets, G, T, pos_g, ahead, lane, g, lo, hi, g2, lo2, hi2);
-  } else {
-    lo = offsets[g];
-    hi = offsets[g + 1];
+  const int64_t w = blockIdx.x, nwg = gridDim.x, tiles = G * per;
+  // offsets clamped into [0, T]; a decrease reads as an empty group.  T is
+  // below 2^23 (the token capacity limit), so ranges fit 32 bits and steps
+  // 16 bits.
+  for (int64_t g = threadIdx.x; g < G; g += NT) {
+    int64_t lo = offsets[g], hi = offsets[g + 1];
     lo = lo < 0 ? 0 : (lo > T ? T : lo);
     hi = hi < lo ? lo : (hi > T ? T : hi);
-    if (g2 < G) {
-      lo2 = offsets[g2];
-      hi2 = offsets[g2 + 1];
-      lo2 = lo2 < 0 ? 0 : (lo2 > T ? T : lo2);
-      hi2 = hi2 < lo2 ? lo2 : (hi2 > T ? T : hi2);
-    } else {
-      g2 = -1;
-    }
+    s_lo[g] = (int)lo;
+    s_hi[g] = (int)hi;
+    s_key[g] = ((uint32_t)((hi - lo + BK - 1) / BK) << 9) | (uint32_t)(511 - g);
   }
-  const int64_t L = (per & 7) == 0 ? (u & 7) * run + (u >> 3) : u;
-  // grouped order inside the expert: GM_TILES m-tiles, n-tiles outer
-  const int64_t first = L / (GM_TILES * nn) * GM_TILES;
-  const int64_t gsz = (nm - first) < GM_TILES ? (nm - first) : GM_TILES;
-  const int64_t in = L % (GM_TILES * nn);
-  const int64_t mt = first + in % gsz, nt = in / gsz;
-  const int64_t P = 128 * (lo / 128 + g);
-  WTile<FA, FB> w;
-  w.nk = (hi - lo + BK - 1) / BK;
-  w.nk2 = g2 >= 0 ? (uint32_t)((hi2 - lo2 + BK - 1) / BK) : 0u;
-  const int64_t P2 = g2 >= 0 ? 128 * (lo2 / 128 + g2) : 0;
-  w.st0 = (lds_u8*)smem0;
-  w.st1 = (lds_u8*)smem1;
-  w.ss = (lds_u8*)sscale;
-  w.pf_scratch = (lds_u8*)spf;
-  const int64_t m0 = mt * BM, n0 = nt * BN;
-  const int64_t m_end = (m0 + BM) < M ? m0 + BM : M, n_end = (n0 + BN) < N ? n0 + BN : N;
-  w.setup(a, sa, b, sb, ld, m0, m_end - m0, n0, n_end - n0, P, P2, wave, lane);
-  // prefetch only where a run first needs a slice: A by the run's first
-  // n-tile column, B by the first m-tile of each GM_TILES group
-  const int64_t pos = (per & 7) == 0 ? (L % run) : L;
-  w.pf_a = pos < gsz ? 0u : OOB;
-  w.pf_b = mt == first ? 0u : OOB;
-  v16f acc[4][4];
-  w.run(acc, wave, lane);
-  // every load has landed (none may still be writing LDS) and every wave is
-  // past its last read of the stage buffers before they hold the result
-  wait_vm_all();
   __syncthreads();
-  store_tile_bf16_lds(acc, (lds_u8*)smem0, (lds_u8*)smem1, c + g * M * N, N, m0, m_end, n0, N,
-                      wave & 1, wave >> 1, wave, lane);
+  int cnt = 0;
+  if (groups > 0) {
+    for (int64_t g = threadIdx.x; g < G; g += NT) {
+      const uint32_t k = s_key[g];
+      int r = 0;
+      for (int64_t h = 0; h < G; h++) r += s_key[h] > k ? 1 : 0;
+      s_order[r] = (short)g;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // lane j < groups holds group j's work; the least loaded is the
+      // smallest (work << 6 | j), found as the complement of a maximum
+      const int mine = (int)(w / per);
+      uint32_t load = 0;
+      for (int64_t p = 0; p < G; p++) {
+        const int g = s_order[p];
+        const uint32_t key = lane < groups ? (load << 6) | (uint32_t)lane : 0xFFFFFFFFu;
+        const int j = (int)(~wave_max(~key) & 63u);
+        if (lane == j) load += (s_key[g] >> 9) + W_TILE_COST;
+        if (j == mine) {
+          if (lane == 0) s_list[cnt] = (short)g;
+          cnt++;
+        }
+      }
+      if (lane == 0) s_cnt = cnt;
+    }
+    __syncthreads();
+    cnt = s_cnt;
+  }
+  const int64_t run = per >> 3;
+  // tile k of this workgroup: its expert g and output tile, the workgroup's
+  // next tile's expert g2 when that covers the same rows (for the L2
+  // prefetch), the WTile set up over them; false past the last
+  struct Cur {
+    int g;
+    int64_t m0, m_end, n0;
+  };
+  // LDS values read at uniform addresses come back in vector registers;
+  // readfirstlane keeps the tile's bookkeeping in scalar ones
+  auto rfl = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
+  auto make = [&](int64_t k, WTile<FA, FB>& wt, Cur& cu) -> bool {
+    int g, g2 = -1;
+    int64_t u;
+    if (groups > 0) {
+      if (k >= cnt) return false;
+      g = rfl(s_list[k]);
+      u = w % per;
+      if (k + 1 < cnt) g2 = rfl(s_list[k + 1]);
+    } else {
+      const int64_t t = w + k * nwg, tn = t + nwg;
+      if (t >= tiles) return false;
+      g = (int)(t / per);
+      u = t - (int64_t)g * per;
+      // the next tile reuses this one's rows when it is the same output tile
+      if (tn < tiles && tn % per == u) g2 = (int)(tn / per);
+    }
+    const int64_t lo = rfl(s_lo[g]), hi = rfl(s_hi[g]);
+    const int64_t lo2 = g2 >= 0 ? rfl(s_lo[g2]) : 0, hi2 = g2 >= 0 ? rfl(s_hi[g2]) : 0;
+    const int64_t L = (per & 7) == 0 ? (u & 7) * run + (u >> 3) : u;
+    // grouped order inside the expert: GM_TILES m-tiles, n-tiles outer
+    const int64_t first = L / (GM_TILES * nn) * GM_TILES;
+    const int64_t gsz = (nm - first) < GM_TILES ? (nm - first) : GM_TILES;
+    const int64_t in = L % (GM_TILES * nn);
+    const int64_t mt = first + in % gsz, nt = in / gsz;
+    const int64_t P = 128 * (lo / 128 + g);
+    const int64_t P2 = g2 >= 0 ? 128 * (lo2 / 128 + g2) : 0;
+    wt.nk = (hi - lo + BK - 1) / BK;
+    wt.nk2 = g2 >= 0 ? (uint32_t)((hi2 - lo2 + BK - 1) / BK) : 0u;
+    wt.st0 = (lds_u8*)smem0;
+    wt.st1 = (lds_u8*)smem1;
+    wt.ss = (lds_u8*)sscale;
+    wt.pf_scratch = (lds_u8*)spf;
+    cu.g = g;
+    cu.m0 = mt * BM;
+    cu.n0 = nt * BN;
+    cu.m_end = (cu.m0 + BM) < M ? cu.m0 + BM : M;
+    const int64_t n_end = (cu.n0 + BN) < N ? cu.n0 + BN : N;
+    wt.setup(a, sa, b, sb, ld, cu.m0, cu.m_end - cu.m0, cu.n0, n_end - cu.n0, P, P2, wave, lane);
+    // prefetch only where a run first needs a slice: A by the run's first
+    // n-tile column, B by the first m-tile of each GM_TILES group
+    const int64_t pos = (per & 7) == 0 ? (L % run) : L;
+    wt.pf_a = pos < gsz ? 0u : OOB;
+    wt.pf_b = mt == first ? 0u : OOB;
+    return true;
+  };
+  // one WTile: after a tile's K loop it is set up over the next tile (the
+  // store needs only the finished tile's place, kept in cc)
+  WTile<FA, FB> wt;
+  Cur cc;
+  if (!make(0, wt, cc)) return;
+  wt.issue_first(wave, lane);
+  bool stored = false;
+  for (int64_t k = 1;; k++) {
+    wt.issue_second(wave, lane);
+    v16f acc[4][4];
+    wt.run_issued(acc, wave, lane, stored);
+    // every load has landed (none may still be writing LDS) and every wave is
+    // past its last read of the stage and scale buffers
+    wait_vm_all();
+    __syncthreads();
+    Cur cn;
+    const bool more = make(k, wt, cn);
+    uint16_t* const ct = c + (int64_t)cc.g * M * N;
+    if (OVERLAP) {
+      // the next tile's stage 0 goes to stage buffer 0 while the result
+      // leaves through buffer 1 (32 stores per wave); its stage 1 follows,
+      // and it waits for stage 0 only: the stores drain under its first K
+      // step
+      if (more) wt.issue_first(wave, lane);
+      store_tile_bf16_lds_halves(acc, (lds_u8*)smem1, ct, N, cc.m0, cc.m_end, cc.n0, N, wave & 1,
+                                 wave >> 1, wave, lane);
+      stored = true;
+    } else {
+      // (the store ends with a barrier: the next tile may reuse the stages)
+      store_tile_bf16_lds(acc, (lds_u8*)smem0, (lds_u8*)smem1, ct, N, cc.m0, cc.m_end, cc.n0, N,
+                          wave & 1, wave >> 1, wave, lane);
+      if (more) wt.issue_first(wave, lane);
+    }
+    if (!more) break;
+    cc = cn;
+  }
 }
 
 hipError_t launch_grouped_wgrad(int a_elem, int b_elem, int64_t G, const int64_t* offsets, int64_t T,
@@ -384,17 +430,38 @@ hipError_t launch_grouped_wgrad(int a_elem, int b_elem, int64_t G, const int64_t
                                 hipStream_t stream) {
   if (G < 1 || G > W_MAX_GROUPS || cap % BK != 0) return hipErrorInvalidValue;
   if ((a_elem != 0 && a_elem != 1) || (b_elem != 0 && b_elem != 1)) return hipErrorInvalidValue;
-  const int64_t tiles = G * ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int64_t per = ((M + BM - 1) / BM) * ((N + BN - 1) / BN), tiles = G * per;
   if (tiles == 0) return hipSuccess;
-  const int xcd_cus = (num_cus > 0 ? num_cus : 256) / 8;  // compute units per XCD
-#define MX_WGRAD_LAUNCH(FA_, FB_)                                                                 \
-  hipLaunchKernelGGL((grouped_wgrad_kernel<FA_, FB_>), dim3((unsigned)tiles), dim3(NT), 0, stream, \
-                     G, offsets, T, M, N, cap, (const uint8_t*)a, (const uint8_t*)sa,            \
-                     (const uint8_t*)b, (const uint8_t*)sb, (uint16_t*)c, xcd_cus)
-  if (a_elem == 0 && b_elem == 0) MX_WGRAD_LAUNCH(0, 0);
-  else if (a_elem == 1 && b_elem == 0) MX_WGRAD_LAUNCH(1, 0);
-  else if (a_elem == 0 && b_elem == 1) MX_WGRAD_LAUNCH(0, 1);
-  else MX_WGRAD_LAUNCH(1, 1);
+  const int64_t cus = num_cus > 0 ? num_cus : 256;
+  // groups of `per` workgroups when a whole number of them fits the chip
+  // (and one wave can hold the groups' work); otherwise a plain walk
+  int groups = 0;
+  int64_t wgs;
+  if (per <= cus && cus / per <= 64) {
+    const int64_t m = (cus / per) < G ? cus / per : G;
+    groups = (int)m;
+    wgs = m * per;
+  } else {
+    wgs = cus < tiles ? cus : tiles;
+    if (wgs >= 8) wgs = wgs / 8 * 8;  // keeps tile t on XCD t % 8
+  }
+  // the result leaves through one stage buffer while the other loads the
+  // next tile (whole 8-column chunks, 32-bit store offsets)
+  const bool overlap = N % 8 == 0 && (int64_t)BM * N * 2 < ((int64_t)1 << 31);
+#define MX_WGRAD_LAUNCH(FA_, FB_, OV_)                                                            \
+  hipLaunchKernelGGL((grouped_wgrad_kernel<FA_, FB_, OV_>), dim3((unsigned)wgs), dim3(NT), 0,     \
+                     stream, G, offsets, T, M, N, cap, (const uint8_t*)a, (const uint8_t*)sa,    \
+                     (const uint8_t*)b, (const uint8_t*)sb, (uint16_t*)c, groups)
+#define MX_WGRAD_FMT(OV_)                                                                         \
+  do {                                                                                            \
+    if (a_elem == 0 && b_elem == 0) MX_WGRAD_LAUNCH(0, 0, OV_);                                   \
+    else if (a_elem == 1 && b_elem == 0) MX_WGRAD_LAUNCH(1, 0, OV_);                              \
+    else if (a_elem == 0 && b_elem == 1) MX_WGRAD_LAUNCH(0, 1, OV_);                              \
+    else MX_WGRAD_LAUNCH(1, 1, OV_);                                                              \
+  } while (0)
+  if (overlap) MX_WGRAD_FMT(true);
+  else MX_WGRAD_FMT(false);
+#undef MX_WGRAD_FMT
 #undef MX_WGRAD_LAUNCH
   return hipGetLastError();
 }

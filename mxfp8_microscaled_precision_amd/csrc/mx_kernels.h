@@ -49,8 +49,8 @@ hipError_t launch_grouped_gemm(int a_elem, int b_elem, int64_t G, const int64_t*
 
 // Per-expert weight gradient c[g] [M, N] over group g's token columns of
 // a [M, cap] and b [N, cap] (grouped column layout above).
-// num_cus: compute units of the device (sizes the L2 prefetch of the expert
-// that follows on each XCD).
+// num_cus: compute units of the device (the persistent grid has at most one
+// workgroup per compute unit).
 hipError_t launch_grouped_wgrad(int a_elem, int b_elem, int64_t G, const int64_t* offsets, int64_t T,
                                 int64_t M, int64_t N, int64_t cap, const void* a, const void* sa,
                                 const void* b, const void* sb, void* c, int num_cus,

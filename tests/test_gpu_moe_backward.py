@@ -152,7 +152,7 @@ def _wgrad_case(sizes, M, N, seed):
     ([130, 128, 129, 127], 256, 256),            # odd and even step counts
     ([600, 700, 850, 1100], 96, 96),             # 5, 6, 7, 9 steps: partial groups of four steps
     ([128, 1000, 128, 1000, 0, 5, 1000], 64, 64),  # equal step counts: longest-first order ties
-    ([(7 * g) % 45 for g in range(130)], 64, 32),  # more groups than the longest-first order takes
+    ([(7 * g) % 45 for g in range(130)], 64, 32),  # 130 groups dealt to 64 groups of workgroups
 ])
 def test_wgrad_small_cases(sizes, M, N):
     say(f"[moe-bwd] wgrad sizes={sizes} M={M} N={N}")
@@ -190,6 +190,28 @@ def test_largest_token_capacity():
     torch.cuda.synchronize()
     ref, bound = oracle.grouped_gemm_wgrad(off, wqa, wsa, wqb, wsb)
     assert_gemm(c, ref, bound, "wgrad at the largest capacity")
+
+
+@pytest.mark.parametrize("sizes,M,N", [
+    ([5, 0, 33, 64, 1], 64, 100),       # N % 8 != 0: the result leaves through both stage buffers
+    ([300, 257, 1, 511], 288, 36),
+])
+def test_wgrad_ragged_n(sizes, M, N):
+    """Output columns N that are not whole 8-column chunks (the C ABI takes
+    any N; the rows of b are independent, so the first N rows of a grouped
+    column quantisation are a valid b)."""
+    say(f"[moe-bwd] wgrad ragged N sizes={sizes} M={M} N={N}")
+    off = _offsets(sizes)
+    T = int(off[-1])
+    dy = W.normal_bf16((T, M), 0.01, 7 + N)
+    xx = W.normal_bf16((T, 128), 1.0, 8 + N)
+    qa, sa = oracle.quant_col_grouped(bits(dy), off)
+    qb, sb = oracle.quant_col_grouped(bits(xx), off)
+    qb, sb = np.ascontiguousarray(qb[:N]), np.ascontiguousarray(sb[:N])
+    c = mx.grouped_gemm_wgrad(dev(off), T, dev(qa), dev(sa), dev(qb), dev(sb))
+    torch.cuda.synchronize()
+    ref, bound = oracle.grouped_gemm_wgrad(off, qa, sa, qb, sb)
+    assert_gemm(c, ref, bound, f"wgrad ragged N={N}")
 
 
 def test_wgrad_neighbour_nan_scales_stay_out():
