@@ -81,8 +81,12 @@ quant_block32_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C, uint8
                      uint8_t* __restrict__ s) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, rg = lane >> 4;
-  const int64_t r0 = (int64_t)blockIdx.x * 128 + 32 * wave;
-  const int64_t col = (int64_t)blockIdx.y * 128 + 8 * c;
+  // 128 x 128 blocks, column blocks fastest (along the rows of x: measured
+  // faster than down its columns)
+  const int64_t lin = (int64_t)blockIdx.x + (int64_t)blockIdx.y * gridDim.x;
+  const int64_t br = lin / gridDim.y, bc = lin - br * gridDim.y;
+  const int64_t r0 = br * 128 + 32 * wave;
+  const int64_t col = bc * 128 + 8 * c;
   // R and C are multiples of 32: a wave's 32 rows are all in or all out, and
   // so are a tile's four chunks
   if (r0 >= R) return;
@@ -186,7 +190,7 @@ __device__ __forceinline__ void gcol_block(const int64_t* __restrict__ offsets, 
   nreal = left <= 0 ? 0 : (left >= 32 ? 32 : (int)left);
 }
 
-// One 128 x 128 tile at rows R0.., columns of column tile blockIdx.y.  The
+// One 128 x 128 tile at rows R0.., columns C0...  The
 // tile's column scales go to LST at blocks 4p .. 4p+3 of each column's
 // 4 * LRUN; with LRUN == 1 the tile also stores them (a run stores them
 // once for all its tiles).
@@ -196,11 +200,10 @@ __device__ __forceinline__ void quant_tile(const uint16_t* __restrict__ x, int64
                                            uint8_t* __restrict__ qt, uint8_t* __restrict__ st,
                                            int64_t G, const int64_t* __restrict__ offsets,
                                            int64_t T, int64_t R0, int p, lds8* LQ, lds8* LQT,
-                                           lds8* LS, lds8* LST) {
+                                           lds8* LS, lds8* LST, int64_t C0) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 3, h = lane & 7;
   const int wr = wave >> 1, wc = wave & 1;
-  const int64_t C0 = (int64_t)blockIdx.y * TILE_COLS;
   const int64_t r0 = R0 + 32 * wr;
   const int64_t c = C0 + 64 * wc + 8 * h;
   // R, C are multiples of 32: a wave's 32 rows are all in or all out, and
@@ -353,8 +356,17 @@ quant_tile_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C, uint8_t*
   lds8* LS = (lds8*)ls;
   lds8* LST = (lds8*)lst;
   if (LRUN == 1) {
-    quant_tile<MODE, EL, 1>(x, R, C, q, s, qt, st, G, offsets, T, (int64_t)blockIdx.x * TILE_ROWS,
-                            0, LQ, LQT, LS, LST);
+    // dispatch order (measured): the column mode goes along the rows of x,
+    // column tiles fastest; the dual mode down its columns, row tiles
+    // fastest (as the grid is laid out)
+    int64_t tr = blockIdx.x, tc = blockIdx.y;
+    if (MODE == TILE_COL) {
+      const int64_t lin = (int64_t)blockIdx.x + (int64_t)blockIdx.y * gridDim.x;
+      tr = lin / gridDim.y;
+      tc = lin - tr * gridDim.y;
+    }
+    quant_tile<MODE, EL, 1>(x, R, C, q, s, qt, st, G, offsets, T, tr * TILE_ROWS, 0, LQ, LQT, LS, LST,
+                            tc * TILE_COLS);
     return;
   }
   const int64_t RUN0 = (int64_t)blockIdx.x * run * TILE_ROWS;
@@ -362,7 +374,8 @@ quant_tile_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C, uint8_t*
     const int64_t R0 = RUN0 + (int64_t)p * TILE_ROWS;
     if (R0 >= R) break;      // uniform over the workgroup
     if (p) __syncthreads();  // the previous tile's LDS reads are done
-    quant_tile<MODE, EL, LRUN>(x, R, C, q, s, qt, st, G, offsets, T, R0, p, LQ, LQT, LS, LST);
+    quant_tile<MODE, EL, LRUN>(x, R, C, q, s, qt, st, G, offsets, T, R0, p, LQ, LQT, LS, LST,
+                               (int64_t)blockIdx.y * TILE_COLS);
   }
   // the run's column scales (the last tile's barrier made them visible)
   const int t = threadIdx.x;
