@@ -2,9 +2,9 @@
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  The product library never calls it and
-shares no code with it.  The arithmetic lives in ``mx_oracle.c`` (plain C,
-binary64, built with gcc); this module only compiles it and marshals numpy
-arrays through ctypes.
+shares no code with it.  The arithmetic lives in ``mx_oracle.cpp`` (plain
+C++ functions over arrays, binary64, built with g++); this module only
+compiles it and marshals numpy arrays through ctypes.
 
 Parity pins: every function here is pinned by ``tests/test_oracle_*.py``
 against closed forms, exhaustive brute force and library routines (torch's
@@ -19,16 +19,17 @@ import subprocess
 import numpy as np
 
 _DIR = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_DIR, "mx_oracle.c")
+_SRC = os.path.join(_DIR, "mx_oracle.cpp")
 # MX_ORACLE_LIB points the wrappers at another build of the oracle (the
 # mutation tests load deliberately broken copies this way); it is never
 # rebuilt from here.
 _ALT = os.environ.get("MX_ORACLE_LIB")
 _LIB = _ALT or os.path.join(_DIR, "liboracle.so")
 
-# gcc flags: no fast-math and no FMA contraction, so every binary64 operation
+# g++ flags: no fast-math and no FMA contraction, so every binary64 operation
 # is the plain IEEE operation written in the source.
-CFLAGS = ["-O2", "-std=c11", "-Wall", "-Wextra", "-ffp-contract=off", "-fno-fast-math",
+CXX = "g++"
+CFLAGS = ["-O2", "-std=c++17", "-Wall", "-Wextra", "-ffp-contract=off", "-fno-fast-math",
           "-fopenmp", "-shared", "-fPIC"]
 
 BKIND_ROW = 0        # B [N][K], scales [N][K/32]
@@ -41,12 +42,12 @@ ELEMS = {"e4m3": ELEM_E4M3, "e5m2": ELEM_E5M2}
 
 
 def build(force: bool = True) -> str:
-    """Compile mx_oracle.c into liboracle.so (always, when force)."""
+    """Compile mx_oracle.cpp into liboracle.so (always, when force)."""
     if _ALT:
         return _LIB
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", *CFLAGS, "-o", tmp, _SRC, "-lm"])
+        subprocess.check_call([CXX, *CFLAGS, "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
 

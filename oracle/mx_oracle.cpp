@@ -1,5 +1,9 @@
 /*
- * mx_oracle.c -- plain, slow CPU oracle for the MXFP8 microscaled hot path.
+ * mx_oracle.cpp -- plain, slow CPU oracle for the MXFP8 microscaled hot path.
+ *
+ * C++ kept to plain functions over arrays (no classes, templates or library
+ * algorithms), so that each step reads as the definition it follows; the
+ * functions have C linkage for the ctypes wrappers in oracle/__init__.py.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, loads or
  * calls this file; only the tests, the package's smoke check and the bench's
@@ -66,6 +70,8 @@
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
+
+extern "C" {
 #endif
 
 /* ------------------------------------------------------------------------ */
@@ -563,3 +569,5 @@ int orc_num_threads(void)
     return 1;
 #endif
 }
+
+}  // extern "C"

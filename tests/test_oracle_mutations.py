@@ -1,6 +1,6 @@
 """The oracle's pins catch plausible mistakes (CPU only).
 
-Each case plants one mistake in a copy of oracle/mx_oracle.c, builds it, and
+Each case plants one mistake in a copy of oracle/mx_oracle.cpp, builds it, and
 runs the named pin tests against that build (through MX_ORACLE_LIB) in a
 subprocess; the pins must fail.  A control build of the unchanged source must
 pass the same tests.  The mistakes: a wrong rounding rule, a wrong
@@ -20,7 +20,7 @@ import pytest
 import oracle
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SRC = os.path.join(ROOT, "oracle", "mx_oracle.c")
+SRC = os.path.join(ROOT, "oracle", "mx_oracle.cpp")
 F = "tests/test_oracle_formats.py"
 Q = "tests/test_oracle_quant.py"
 G = "tests/test_oracle_gemm.py"
@@ -89,10 +89,10 @@ MUTATIONS = [
 
 
 def _build(tmp_path, name, text):
-    src = tmp_path / f"{name}.c"
+    src = tmp_path / f"{name}.cpp"
     src.write_text(text)
     lib = tmp_path / f"{name}.so"
-    subprocess.check_call(["gcc", *oracle.CFLAGS, "-o", str(lib), str(src), "-lm"])
+    subprocess.check_call([oracle.CXX, *oracle.CFLAGS, "-o", str(lib), str(src), "-lm"])
     return str(lib)
 
 
