@@ -409,12 +409,18 @@ def fused_producer(torch, mx, t, reps=5):
     return out
 
 
-def other_configs(torch, mx, W, warm=5, reps=20):
+def other_configs(torch, mx, W, warm=5, reps=20, queue=8):
     """The dense (8192 x 4096 x 4096, dual-axis) and 32x32-weight (16384
     tokens, 7168 <-> 2048) configurations, outside the timed step.  Every
     kernel is launched warm + reps times with a 1 GiB buffer fill before each
     launch, so no operand stays in L2 or the Infinity Cache; the median
-    launch (HIP events on the launch stream) is reported."""
+    launch (HIP events on the launch stream) is reported.  Beside it,
+    `ms_queued` / `frac_peak_queued`: `queue` launches back to back on as
+    many distinct copies of the operands (all cold after the fill) between
+    two events, per launch, median over the reps -- the rate when launches
+    follow one another as in a step, without the fixed cost of bracketing
+    one launch with events (an empty launch measures several microseconds
+    that way, a large share of these short kernels)."""
     import statistics
     u8, bf = torch.uint8, torch.bfloat16
     dev = "cuda"
@@ -422,7 +428,7 @@ def other_configs(torch, mx, W, warm=5, reps=20):
     L = Launcher(torch, mx)
     L.record = True
 
-    def med(call):
+    def med(call, calls=None):
         L.events.clear()
         for i in range(warm + reps):
             flush.fill_(i & 255)
@@ -431,12 +437,32 @@ def other_configs(torch, mx, W, warm=5, reps=20):
         ev = L.events[warm:]
         ms = statistics.median(s.elapsed_time(e) for _, _, _, s, e in ev)
         work, unit = ev[0][1], ev[0][2]
-        rate = work / (ms * 1e-3)
-        if unit == "FLOP":
-            return {"tflops": round(rate / 1e12, 1), "frac_peak": round(rate / 1e12 / PEAK_FP8_TFLOPS, 4),
-                    "ms": round(ms, 4)}
-        return {"gbps": round(rate / 1e9, 1), "frac_peak": round(rate / 1e9 / PEAK_HBM_GBPS, 4),
-                "ms": round(ms, 4)}
+        big = unit == "FLOP"
+        scale, peak, key = (1e12, PEAK_FP8_TFLOPS, "tflops") if big else (1e9, PEAK_HBM_GBPS, "gbps")
+        rate = work / (ms * 1e-3) / scale
+        r = {key: round(rate, 1), "frac_peak": round(rate / peak, 4), "ms": round(ms, 4)}
+        if calls:
+            L.record = False
+            marks = []
+            for i in range(warm + reps):
+                flush.fill_(i & 255)
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for c in calls:
+                    c()
+                e1.record()
+                marks.append((e0, e1))
+            torch.cuda.synchronize()
+            L.record = True
+            msq = statistics.median(a.elapsed_time(b) for a, b in marks[warm:]) / len(calls)
+            rq = work / (msq * 1e-3) / scale
+            r.update({"ms_queued": round(msq, 4), "frac_peak_queued": round(rq / peak, 4)})
+        return r
+
+    def copies(*ts):
+        """queue sets of the tensors ts: the originals, then clones."""
+        return [ts] + [tuple(t.clone() for t in ts) for _ in range(queue - 1)]
 
     def dual(R, C):
         return (torch.empty((R, C), dtype=u8, device=dev), torch.empty((R, C // 32), dtype=u8, device=dev),
@@ -449,6 +475,26 @@ def other_configs(torch, mx, W, warm=5, reps=20):
     def tile(R, C):
         return (torch.empty((R, C), dtype=u8, device=dev),
                 torch.empty((R // 32, C // 32), dtype=u8, device=dev), None, None)
+
+    def quant_op(mode, x, shape_out):
+        """Median of one launch, and of `queue` launches on distinct copies."""
+        R, C = x.shape
+        xs = copies(x)
+        outs = [shape_out(R, C) for _ in range(queue)]
+        one = lambda: L.quant("q", mode, x, outs[0])
+        many = [(lambda i=i: L.quant("q", mode, xs[i][0], outs[i])) for i in range(queue)]
+        r = med(one, many)
+        del xs, outs
+        return r
+
+    def gemm_op(layout, bkind, M, N, K, a, sa, b, sb, c_shape):
+        ops = copies(a, sa, b, sb)
+        cs = [torch.empty(c_shape, dtype=bf, device=dev) for _ in range(queue)]
+        one = lambda: L.gemm("g", layout, bkind, M, N, K, a, sa, b, sb, cs[0])
+        many = [(lambda i=i: L.gemm("g", layout, bkind, M, N, K, *ops[i], cs[i])) for i in range(queue)]
+        r = med(one, many)
+        del ops, cs
+        return r
 
     out = {}
     # the tiny linear: launch-latency-bound, so microseconds are the figure
@@ -468,39 +514,48 @@ def other_configs(torch, mx, W, warm=5, reps=20):
     M, K = X.shape
     N = Wt.shape[0]
     bx, bw, bd = dual(M, K), dual(N, K), dual(M, N)
-    Y = torch.empty((M, N), dtype=bf, device=dev)
-    dX = torch.empty((M, K), dtype=bf, device=dev)
-    dW = torch.empty((N, K), dtype=bf, device=dev)
+    # operands of the GEMMs (the dual quantisations of X, W and dY)
+    L.record = False
+    L.quant("q", 2, X, bx)
+    L.quant("q", 2, Wt, bw)
+    L.quant("q", 2, dY, bd)
+    L.record = True
     r = {
-        "quant_dual_X": med(lambda: L.quant("q", 2, X, bx)),
-        "quant_dual_W": med(lambda: L.quant("q", 2, Wt, bw)),
-        "quant_dual_dY": med(lambda: L.quant("q", 2, dY, bd)),
-        "fprop": med(lambda: L.gemm("g", 0, 0, M, N, K, bx[0], bx[1], bw[0], bw[1], Y)),
-        "dgrad": med(lambda: L.gemm("g", 1, 0, M, K, N, bd[0], bd[1], bw[2], bw[3], dX)),
-        "wgrad": med(lambda: L.gemm("g", 2, 0, N, K, M, bd[2], bd[3], bx[2], bx[3], dW)),
+        "quant_dual_X": quant_op(2, X, dual),
+        "quant_dual_W": quant_op(2, Wt, dual),
+        "quant_dual_dY": quant_op(2, dY, dual),
+        "fprop": gemm_op(0, 0, M, N, K, bx[0], bx[1], bw[0], bw[1], (M, N)),
+        "dgrad": gemm_op(1, 0, M, K, N, bd[0], bd[1], bw[2], bw[3], (M, K)),
+        "wgrad": gemm_op(2, 0, N, K, M, bd[2], bd[3], bx[2], bx[3], (N, K)),
     }
     out[f"dense {M}x{K} -> {N}"] = r
-    del d, X, Wt, dY, bx, bw, bd, Y, dX, dW
+    del d, X, Wt, dY, bx, bw, bd
+    torch.cuda.empty_cache()
     d = W.block32(dev)
     W1, W2, X1, X2 = d["W1"], d["W2"], d["X1"], d["X2"]
     T, H = X1.shape
     F = W1.shape[0]
     b1, b2, bx1, bx2 = tile(F, H), tile(H, F), row(T, H), row(T, F)
-    Y1 = torch.empty((T, F), dtype=bf, device=dev)
-    Y2 = torch.empty((T, H), dtype=bf, device=dev)
+    L.record = False
+    L.quant("q", 3, W1, b1)
+    L.quant("q", 3, W2, b2)
+    L.quant("q", 0, X1, bx1)
+    L.quant("q", 0, X2, bx2)
+    L.record = True
     r = {
-        "quant_32x32_W1": med(lambda: L.quant("q", 3, W1, b1)),
-        "quant_32x32_W2": med(lambda: L.quant("q", 3, W2, b2)),
-        "quant_row_X1": med(lambda: L.quant("q", 0, X1, bx1)),
-        "quant_row_X2": med(lambda: L.quant("q", 0, X2, bx2)),
-        "fprop1": med(lambda: L.gemm("g", 0, 1, T, F, H, bx1[0], bx1[1], b1[0], b1[1], Y1)),
-        "fprop2": med(lambda: L.gemm("g", 0, 1, T, H, F, bx2[0], bx2[1], b2[0], b2[1], Y2)),
-        "dgrad1": med(lambda: L.gemm("g", 1, 1, T, H, F, bx2[0], bx2[1], b1[0], b1[1], Y2)),
-        "dgrad2": med(lambda: L.gemm("g", 1, 1, T, F, H, bx1[0], bx1[1], b2[0], b2[1], Y1)),
+        "quant_32x32_W1": quant_op(3, W1, tile),
+        "quant_32x32_W2": quant_op(3, W2, tile),
+        "quant_row_X1": quant_op(0, X1, row),
+        "quant_row_X2": quant_op(0, X2, row),
+        "fprop1": gemm_op(0, 1, T, F, H, bx1[0], bx1[1], b1[0], b1[1], (T, F)),
+        "fprop2": gemm_op(0, 1, T, H, F, bx2[0], bx2[1], b2[0], b2[1], (T, H)),
+        "dgrad1": gemm_op(1, 1, T, H, F, bx2[0], bx2[1], b1[0], b1[1], (T, H)),
+        "dgrad2": gemm_op(1, 1, T, F, H, bx1[0], bx1[1], b2[0], b2[1], (T, F)),
     }
     out[f"32x32 weights, {T} tokens, {H} <-> {F}"] = r
     del flush
     torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     return out
 
 
