@@ -252,6 +252,44 @@ def test_wgrad_equals_dense_gemm_per_expert():
         assert torch.equal(c[g], dense), g
 
 
+@pytest.mark.parametrize("sizes,M,N", [
+    # 16 output tiles per expert: 16 groups of 16 workgroups, several
+    # experts dealt to each (longest first), empty and one-token experts
+    ([1900, 0, 7, 640, 1, 1200, 333, 2048, 129, 0, 900, 77, 1500, 260, 31, 1024, 555, 12, 2100, 400],
+     1024, 1024),
+    ([3000, 129, 2500, 600, 0, 1800, 64, 1100, 4000], 2048, 2048),   # 64 per expert: 4 groups
+    ([5000, 300, 2600, 1, 700], 4096, 2048),                          # 128 per expert: 2 groups
+    ([700, 260], 4608, 4608),        # 324 tiles per expert, more than the grid: a strided walk
+    ([(37 * g) % 300 for g in range(100)], 768, 256),                # 3 per expert: a strided walk
+])
+def test_wgrad_schedules_equal_dense_gemm(sizes, M, N):
+    """The persistent weight gradient's tile walk, in each of its forms (the
+    experts dealt to groups of workgroups, or a strided walk over all
+    tiles), against the dense GEMM of every expert over its padded column
+    range: the same K-step order, so the same bits; every output tile of
+    every expert is compared."""
+    say(f"[moe-bwd] wgrad schedule G={len(sizes)} M={M} N={N}")
+    off = _offsets(sizes)
+    T = int(off[-1])
+    offd = dev(off)
+    dy = W.normal_bf16((T, M), 0.01, 900 + M, "cuda")
+    xx = W.normal_bf16((T, N), 1.0, 901 + N, "cuda")
+    qa, sa = mx.quant_grouped_col(dy, offd)
+    qb, sb = mx.quant_grouped_col(xx, offd)
+    c = mx.grouped_gemm_wgrad(offd, T, qa, sa, qb, sb)
+    torch.cuda.synchronize()
+    for g, m in enumerate(sizes):
+        if m == 0:
+            assert torch.count_nonzero(c[g]) == 0, g
+            continue
+        P = oracle.group_col(g, off[g])
+        Kg = 128 * ((m + 127) // 128)
+        dense = mx.gemm(qa[:, P:P + Kg].contiguous(), sa[:, P // 32:(P + Kg) // 32].contiguous(),
+                        qb[:, P:P + Kg].contiguous(), sb[:, P // 32:(P + Kg) // 32].contiguous(), "wgrad")
+        torch.cuda.synchronize()
+        assert torch.equal(c[g], dense), f"expert {g} of {len(sizes)}"
+
+
 def test_moe_backward_full_sampled():
     """The whole MoE backward at the workload's size: gate_up and down,
     dgrad through the batched column quantisation of the expert weights and
