@@ -331,16 +331,16 @@ grouped_wgrad_kernel(int64_t G, const int64_t* __restrict__ offsets, int64_t T, 
     cnt = s_cnt;
   }
   const int64_t run = per >> 3;
-  // tile k of this workgroup: its expert g and output tile, the workgroup's
-  // next tile's expert g2 when that covers the same rows (for the L2
-  // prefetch), the WTile set up over them; false past the last
-  struct Cur {
+  struct Cur {  // where a tile's result goes: expert, rows, first column
     int g;
     int64_t m0, m_end, n0;
   };
   // LDS values read at uniform addresses come back in vector registers;
   // readfirstlane keeps the tile's bookkeeping in scalar ones
   auto rfl = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
+  // tile k of this workgroup: its expert g and output tile, and the
+  // workgroup's next tile's expert g2 when that covers the same rows (for
+  // the L2 prefetch); sets up wt over them and cu; false past the last
   auto make = [&](int64_t k, WTile<FA, FB>& wt, Cur& cu) -> bool {
     int g, g2 = -1;
     int64_t u;
