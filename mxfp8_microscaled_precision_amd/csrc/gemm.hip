@@ -464,6 +464,78 @@ struct Tile {
     prefetch_lines(pf_scratch + wave * 512 + 256, (pf_row + (uint32_t)kp) | pf_b | live, rb);
   }
 
+  // The K loop of the LDS_SCALES pipeline after its prologue: step 0's scale
+  // words in sc_a / sc_b and its half-0 fragments in f0a / f0b.
+  __device__ __forceinline__ void kloop_ls(v16f (&acc)[4][4], int wave, int lane, uint32_t* sc_a,
+                                           uint32_t* sc_b, v8i* f0a, v8i* f0b) {
+    const int wm = wave & 1, wn = wave >> 1;
+    const int64_t nk = (K + BK - 1) / BK;
+    uint32_t nx_a[4], nx_b[4];
+    v8i f1a[4], f1b[4];
+    // with PARTIAL && TAIL the last group runs only its real steps (the
+    // loads the skipped ones would issue lie past the end)
+    const int64_t kend = (PARTIAL && TAIL) ? 4 * last_g : nk;
+    for (int64_t j = 0; 4 * j < kend; j++) {
+      const int64_t kt = 4 * j;
+      lds_u8* scur = (j & 1) ? ss1 : ss0;
+      lds_u8* snxt = (j & 1) ? ss0 : ss1;
+      step_ls<0>(st0, st1, scur, snxt, kt, wave, wm, wn, lane, sc_a, sc_b, nx_a, nx_b, f0a, f0b,
+                 f1a, f1b, acc);
+      step_ls<1>(st1, st0, scur, snxt, kt + 1, wave, wm, wn, lane, sc_a, sc_b, nx_a, nx_b, f0a,
+                 f0b, f1a, f1b, acc);
+      step_ls<2>(st0, st1, scur, snxt, kt + 2, wave, wm, wn, lane, sc_a, sc_b, nx_a, nx_b, f0a,
+                 f0b, f1a, f1b, acc);
+      step_ls<3>(st1, st0, snxt, snxt, kt + 3, wave, wm, wn, lane, sc_a, sc_b, nx_a, nx_b, f0a,
+                 f0b, f1a, f1b, acc);
+    }
+    if (PARTIAL && TAIL) {
+      const int64_t j = last_g, kt = 4 * j, r = nk - kt;  // 1 .. 3 real steps
+      lds_u8* scur = (j & 1) ? ss1 : ss0;
+      lds_u8* snxt = (j & 1) ? ss0 : ss1;
+      step_ls<0>(st0, st1, scur, snxt, kt, wave, wm, wn, lane, sc_a, sc_b, nx_a, nx_b, f0a, f0b,
+                 f1a, f1b, acc);
+      if (r > 1)
+        step_ls<1>(st1, st0, scur, snxt, kt + 1, wave, wm, wn, lane, sc_a, sc_b, nx_a, nx_b, f0a,
+                   f0b, f1a, f1b, acc);
+      if (r > 2)
+        step_ls<2>(st0, st1, scur, snxt, kt + 2, wave, wm, wn, lane, sc_a, sc_b, nx_a, nx_b, f0a,
+                   f0b, f1a, f1b, acc);
+    }
+  }
+
+  // The LDS_SCALES prologue in two parts, for a persistent caller that
+  // issues the next tile's first loads before it stores the current result:
+  // issue_first() loads stage 0 and the first scale group (18 ops per wave
+  // with per-row B scales), issue_second() stage 1 (16 ops); run_issued()
+  // waits for stage 0 only (all but the ops issued after it: stage 1's,
+  // and with `stored` the 32 result stores of the halves epilogue issued
+  // between the two) and runs the K loop into acc.
+  __device__ __forceinline__ void issue_first(int wave, int lane) {
+    issue_stage(st0, 0, wave, lane);
+    dma_scales(ss0, 0, wave);
+  }
+  __device__ __forceinline__ void issue_second(int wave, int lane) { issue_stage(st1, BK, wave, lane); }
+  __device__ __forceinline__ void run_issued(v16f (&acc)[4][4], int wave, int lane, bool stored) {
+    static_assert(LDS_SCALES && BMODE == GEMM_B_ROW, "op counts assume per-row B scales");
+    const int wm = wave & 1, wn = wave >> 1;
+#pragma unroll
+    for (int x = 0; x < 4; x++)
+#pragma unroll
+      for (int y = 0; y < 4; y++) acc[x][y] = (v16f){};
+    if (stored)
+      wait_vm<32 + 2 * CHUNKS>();
+    else
+      wait_vm<2 * CHUNKS>();
+    __syncthreads();
+    uint32_t sc_a[4], sc_b[4];
+    v8i f0a[4], f0b[4];
+    read_scales(ss0, 0, 0, wm, wn, lane, sc_a, sc_b);
+    // the steps' vmcnt(2) waits assume the latest two ops are prefetches
+    prefetch(2, wave);
+    read_frags<0>(st0, wm, wn, lane, f0a, f0b);
+    kloop_ls(acc, wave, lane, sc_a, sc_b, f0a, f0b);
+  }
+
   __device__ __forceinline__ void run() {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -491,35 +563,7 @@ struct Tile {
       // prologue ends with the two prefetches of stage 2.
       prefetch(2, wave);
       read_frags<0>(st0, wm, wn, lane, f0a, f0b);
-      // with PARTIAL && TAIL the last group runs only its real steps (the
-      // loads the skipped ones would issue lie past the end)
-      const int64_t kend = (PARTIAL && TAIL) ? 4 * last_g : nk;
-      for (int64_t j = 0; 4 * j < kend; j++) {
-        const int64_t kt = 4 * j;
-        lds_u8* scur = (j & 1) ? ss1 : ss0;
-        lds_u8* snxt = (j & 1) ? ss0 : ss1;
-        step_ls<0>(st0, st1, scur, snxt, kt, wave, wm, wn, lane, sc_a, sc_b, nx_a, nx_b, f0a, f0b,
-                   f1a, f1b, acc);
-        step_ls<1>(st1, st0, scur, snxt, kt + 1, wave, wm, wn, lane, sc_a, sc_b, nx_a, nx_b, f0a,
-                   f0b, f1a, f1b, acc);
-        step_ls<2>(st0, st1, scur, snxt, kt + 2, wave, wm, wn, lane, sc_a, sc_b, nx_a, nx_b, f0a,
-                   f0b, f1a, f1b, acc);
-        step_ls<3>(st1, st0, snxt, snxt, kt + 3, wave, wm, wn, lane, sc_a, sc_b, nx_a, nx_b, f0a,
-                   f0b, f1a, f1b, acc);
-      }
-      if (PARTIAL && TAIL) {
-        const int64_t j = last_g, kt = 4 * j, r = nk - kt;  // 1 .. 3 real steps
-        lds_u8* scur = (j & 1) ? ss1 : ss0;
-        lds_u8* snxt = (j & 1) ? ss0 : ss1;
-        step_ls<0>(st0, st1, scur, snxt, kt, wave, wm, wn, lane, sc_a, sc_b, nx_a, nx_b, f0a, f0b,
-                   f1a, f1b, acc);
-        if (r > 1)
-          step_ls<1>(st1, st0, scur, snxt, kt + 1, wave, wm, wn, lane, sc_a, sc_b, nx_a, nx_b, f0a,
-                     f0b, f1a, f1b, acc);
-        if (r > 2)
-          step_ls<2>(st0, st1, scur, snxt, kt + 2, wave, wm, wn, lane, sc_a, sc_b, nx_a, nx_b, f0a,
-                     f0b, f1a, f1b, acc);
-      }
+      kloop_ls(acc, wave, lane, sc_a, sc_b, f0a, f0b);
     } else {
       issue_stage(st0, 0, wave, lane);
       load_scales(0, nx_a, nx_b);
@@ -596,7 +640,7 @@ gemm_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa,
 // offsets can never address outside the operands) and walks it with a static
 // stride.  Tile t -> (group g, m tile within g, n tile).
 // FA / FB: element formats of the token rows and of the expert weights.
-template <int FAST, int FA = 0, int FB = 0>
+template <int FAST, int FA = 0, int FB = 0, bool OVERLAP = false>
 __global__ void __launch_bounds__(NT)
 grouped_gemm_kernel(int64_t G, const int64_t* __restrict__ offsets, int64_t T, int64_t N,
                     int64_t K, const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa,
@@ -643,7 +687,8 @@ grouped_gemm_kernel(int64_t G, const int64_t* __restrict__ offsets, int64_t T, i
       if (s_pre[mid] <= wg) g = mid; else hi = mid;
     }
   }
-  for (int64_t t = wg; t < total; t += nwg) {
+  // tile t (t >= wg, non-decreasing along the walk) into tl
+  auto make_tile = [&](int64_t t, Tile<GEMM_B_ROW, FAST, FA, FB, 0, false>& tl) {
     while (s_pre[g + 1] <= t) g++;  // s_pre[G] = total > t stops it
     // inside group g, the same grouped order as the dense kernel: runs of
     // GM_TILES m-tiles, n-tiles outer, so 32 consecutive tiles cover
@@ -656,7 +701,6 @@ grouped_gemm_kernel(int64_t G, const int64_t* __restrict__ offsets, int64_t T, i
     const uint32_t in = local - run * span;
     const uint32_t nt = in / gsz;
     const int64_t mt = first + (in - nt * gsz);
-    Tile<GEMM_B_ROW, FAST, FA, FB, 0, false> tl;
     tl.a = a;
     tl.sa = sa;
     tl.b = b + g * N * K;
@@ -677,6 +721,48 @@ grouped_gemm_kernel(int64_t G, const int64_t* __restrict__ offsets, int64_t T, i
     tl.pf_scratch = (lds_u8*)spf;
     tl.pf_a = (nt % (32 / GM_TILES) == 0) ? 0u : OOB;
     tl.pf_b = (mt == first) ? 0u : OOB;
+  };
+  if constexpr (OVERLAP) {
+    // The next tile's stage 0 goes to stage buffer 0 while the result
+    // leaves through buffer 1 (32 stores per wave); its stage 1 follows, and
+    // it waits for stage 0 only, so the stores drain under its first K step.
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int64_t t = wg;
+    if (t >= total) return;
+    Tile<GEMM_B_ROW, FAST, FA, FB, 0, false> tl;
+    make_tile(t, tl);
+    tl.setup(wave, lane);
+    tl.issue_first(wave, lane);
+    bool stored = false;
+    for (;;) {
+      tl.issue_second(wave, lane);
+      v16f acc[4][4];
+      tl.run_issued(acc, wave, lane, stored);
+      const int64_t m0 = tl.m0, m_end = tl.m_end, n0 = tl.n0;
+      // every load has landed (none may still be writing LDS) and every wave
+      // is past its last read of the stage and scale buffers
+      wait_vm_all();
+      __syncthreads();
+      t += nwg;
+      // uniform, and said so: a branch the compiler took for divergent would
+      // carry the next tile's descriptors out of it in vector registers
+      const bool more = __builtin_amdgcn_readfirstlane((int)(t < total)) != 0;
+      if (more) {
+        make_tile(t, tl);
+        tl.setup(wave, lane);
+        tl.issue_first(wave, lane);
+      }
+      store_tile_bf16_lds_halves(acc, (lds_u8*)smem1, c, N, m0, m_end, n0, N, wave & 1, wave >> 1,
+                                 wave, lane);
+      stored = true;
+      if (!more) break;
+    }
+    return;
+  }
+  for (int64_t t = wg; t < total; t += nwg) {
+    Tile<GEMM_B_ROW, FAST, FA, FB, 0, false> tl;
+    make_tile(t, tl);
     tl.run();
   }
 }
@@ -808,20 +894,27 @@ hipError_t launch_grouped_gemm(int a_elem, int b_elem, int64_t G, const int64_t*
   if (upper < wgs) wgs = (upper + 7) / 8 * 8;
   if (wgs < 8) wgs = 8;
   const int pipe = pipe_of(GEMM_B_ROW, N, K);
-#define MX_GROUPED_LAUNCH(P_, FA_, FB_)                                                           \
-  hipLaunchKernelGGL((grouped_gemm_kernel<P_, FA_, FB_>), dim3((unsigned)wgs), dim3(NT), 0, stream, \
-                     G, offsets, T, N, K, (const uint8_t*)a, (const uint8_t*)sa,                    \
+  // the persistent walk overlaps a tile's result stores with the next tile's
+  // first loads when the stores can be counted (whole 8-column chunks,
+  // 32-bit store offsets: the halves epilogue)
+  const bool overlap = N % 8 == 0 && (int64_t)BM * N * 2 < ((int64_t)1 << 31);
+#define MX_GROUPED_LAUNCH(P_, FA_, FB_, OV_)                                                      \
+  hipLaunchKernelGGL((grouped_gemm_kernel<P_, FA_, FB_, OV_>), dim3((unsigned)wgs), dim3(NT), 0,  \
+                     stream, G, offsets, T, N, K, (const uint8_t*)a, (const uint8_t*)sa,          \
                      (const uint8_t*)b, (const uint8_t*)sb, (uint16_t*)c)
-#define MX_GROUPED_FMT(P_)                                                                        \
+#define MX_GROUPED_FMT(P_, OV_)                                                                   \
   do {                                                                                            \
-    if (a_elem == 0 && b_elem == 0) MX_GROUPED_LAUNCH(P_, 0, 0);                                  \
-    else if (a_elem == 1 && b_elem == 0) MX_GROUPED_LAUNCH(P_, 1, 0);                             \
-    else if (a_elem == 0 && b_elem == 1) MX_GROUPED_LAUNCH(P_, 0, 1);                             \
-    else MX_GROUPED_LAUNCH(P_, 1, 1);                                                             \
+    if (a_elem == 0 && b_elem == 0) MX_GROUPED_LAUNCH(P_, 0, 0, OV_);                             \
+    else if (a_elem == 1 && b_elem == 0) MX_GROUPED_LAUNCH(P_, 1, 0, OV_);                        \
+    else if (a_elem == 0 && b_elem == 1) MX_GROUPED_LAUNCH(P_, 0, 1, OV_);                        \
+    else MX_GROUPED_LAUNCH(P_, 1, 1, OV_);                                                        \
   } while (0)
-  if (pipe == 1) MX_GROUPED_FMT(1);
-  else if (pipe == 2) MX_GROUPED_FMT(2);
-  else MX_GROUPED_FMT(0);
+  // (the partial-group pipeline keeps the plain walk: overlapped, it needs
+  // more registers than it has)
+  if (pipe == 1 && overlap) MX_GROUPED_FMT(1, true);
+  else if (pipe == 1) MX_GROUPED_FMT(1, false);
+  else if (pipe == 2) MX_GROUPED_FMT(2, false);
+  else MX_GROUPED_FMT(0, false);
 #undef MX_GROUPED_FMT
 #undef MX_GROUPED_LAUNCH
   return hipGetLastError();
