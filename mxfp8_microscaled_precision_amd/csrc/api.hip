@@ -195,7 +195,12 @@ mx_status mx_gemm_elem(mx_gemm_layout layout, mx_bscale_kind bkind, mx_elem_type
   } else {
     int bmode = mx::GEMM_B_ROW;
     if (bkind == MX_BSCALE_32x32) bmode = layout == MX_GEMM_DGRAD ? mx::GEMM_B_TILE_T : mx::GEMM_B_TILE;
-    e = mx::launch_gemm(bmode, (int)a_elem, (int)b_elem, M, N, K, a, sa, b, sb, c, stream);
+    int cus;
+    {
+      std::lock_guard<std::mutex> lk(g_mu);
+      cus = g_num_cus[dev];
+    }
+    e = mx::launch_gemm(bmode, (int)a_elem, (int)b_elem, M, N, K, a, sa, b, sb, c, cus, stream);
   }
   if (e != hipSuccess) return hip_fail(e, "GEMM kernel launch");
   return MX_OK;

@@ -635,6 +635,79 @@ gemm_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa,
   t.run();
 }
 
+// Persistent form of the 1x32 GEMM (per-row B scales, K a multiple of 512,
+// BF16 result, N a multiple of 8): one workgroup per compute unit walks
+// tiles bid, bid + grid, ... of gemm_kernel's tile map (a grid that is a
+// multiple of 8 keeps every tile on the XCD it has there, index mod 8, so
+// an XCD still runs the same 32-tile groups at a time), and each tile's
+// stage 0 loads while the previous tile's result is stored.
+template <int FA, int FB>
+__global__ void __launch_bounds__(NT)
+gemm_persistent_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa,
+                       const uint8_t* __restrict__ b, const uint8_t* __restrict__ sb,
+                       uint16_t* __restrict__ c, int64_t M, int64_t N, int64_t K) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem0[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t smem1[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t sscale[2 * SCALE_TILE];
+  __shared__ __attribute__((aligned(16))) uint8_t spf[2048];
+  const int64_t nm = (M + BM - 1) / BM, nn = (N + BN - 1) / BN, tiles = nm * nn;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  typedef Tile<GEMM_B_ROW, 1, FA, FB, 0> T1;
+  auto make = [&](int64_t t, T1& tl) {
+    int64_t mt, nt;
+    tile_of(t, nm, nn, mt, nt);
+    tl.a = a;
+    tl.sa = sa;
+    tl.b = b;
+    tl.sb = sb;
+    tl.c = c;
+    tl.q_out = nullptr;
+    tl.s_out = nullptr;
+    tl.m0 = mt * BM;
+    tl.m_end = (mt + 1) * BM < M ? (mt + 1) * BM : M;
+    tl.n0 = nt * BN;
+    tl.N = N;
+    tl.K = K;
+    tl.nkb = K >> 5;
+    tl.st0 = (lds_u8*)smem0;
+    tl.st1 = (lds_u8*)smem1;
+    tl.ss0 = (lds_u8*)sscale;
+    tl.ss1 = (lds_u8*)sscale + SCALE_TILE;
+    tl.pf_scratch = (lds_u8*)spf;
+    tl.pf_a = (nt % (32 / GM_TILES) == 0) ? 0u : OOB;
+    tl.pf_b = (mt % GM_TILES == 0) ? 0u : OOB;
+  };
+  int64_t t = blockIdx.x;
+  if (t >= tiles) return;
+  T1 tl;
+  make(t, tl);
+  tl.setup(wave, lane);
+  tl.issue_first(wave, lane);
+  bool stored = false;
+  for (;;) {
+    tl.issue_second(wave, lane);
+    v16f acc[4][4];
+    tl.run_issued(acc, wave, lane, stored);
+    const int64_t m0 = tl.m0, m_end = tl.m_end, n0 = tl.n0;
+    // every load has landed (none may still be writing LDS) and every wave
+    // is past its last read of the stage and scale buffers
+    wait_vm_all();
+    __syncthreads();
+    t += gridDim.x;
+    const bool more = __builtin_amdgcn_readfirstlane((int)(t < tiles)) != 0;
+    if (more) {
+      make(t, tl);
+      tl.setup(wave, lane);
+      tl.issue_first(wave, lane);
+    }
+    store_tile_bf16_lds_halves(acc, (lds_u8*)smem1, c, N, m0, m_end, n0, N, wave & 1, wave >> 1,
+                               wave, lane);
+    stored = true;
+    if (!more) break;
+  }
+}
+
 // Persistent grouped GEMM: every workgroup derives the tile list from the
 // device-side offsets (clamped into [0, T] and made non-decreasing, so bad
 // offsets can never address outside the operands) and walks it with a static
@@ -806,7 +879,7 @@ static int pipe_of(int bmode, int64_t N, int64_t K) {
 
 hipError_t launch_gemm(int bmode, int a_elem, int b_elem, int64_t M, int64_t N, int64_t K,
                        const void* a, const void* sa, const void* b, const void* sb, void* c,
-                       hipStream_t stream) {
+                       int num_cus, hipStream_t stream) {
   if ((a_elem != 0 && a_elem != 1) || (b_elem != 0 && b_elem != 1)) return hipErrorInvalidValue;
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   dim3 grid((unsigned)tiles);
@@ -814,6 +887,23 @@ hipError_t launch_gemm(int bmode, int a_elem, int b_elem, int64_t M, int64_t N, 
                 *SB = (const uint8_t*)sb;
   uint16_t* C = (uint16_t*)c;
   const int pipe = pipe_of(bmode, N, K);
+  // the 1x32 GEMM with more tiles than compute units runs persistent, one
+  // tile's stores overlapping the next tile's first loads (the halves
+  // epilogue: whole 8-column chunks, 32-bit store offsets)
+  const int64_t cus = (num_cus > 0 ? num_cus : 256) / 8 * 8;
+  if (bmode == GEMM_B_ROW && pipe == 1 && N % 8 == 0 && (int64_t)BM * N * 2 < ((int64_t)1 << 31) &&
+      cus >= 8 && tiles > cus) {
+    dim3 pg((unsigned)cus);
+#define MX_GEMMP_LAUNCH(FA_, FB_)                                                                 \
+  hipLaunchKernelGGL((gemm_persistent_kernel<FA_, FB_>), pg, dim3(NT), 0, stream, A, SA, B, SB, C, M, \
+                     N, K)
+    if (a_elem == 0 && b_elem == 0) MX_GEMMP_LAUNCH(0, 0);
+    else if (a_elem == 1 && b_elem == 0) MX_GEMMP_LAUNCH(1, 0);
+    else if (a_elem == 0 && b_elem == 1) MX_GEMMP_LAUNCH(0, 1);
+    else MX_GEMMP_LAUNCH(1, 1);
+#undef MX_GEMMP_LAUNCH
+    return hipGetLastError();
+  }
 #define MX_GEMM_MODE(BM_)                                                                         \
   do {                                                                                            \
     if (pipe == 1) launch_gemm_fmt<BM_, 1>(a_elem, b_elem, grid, A, SA, B, SB, C, M, N, K, stream); \

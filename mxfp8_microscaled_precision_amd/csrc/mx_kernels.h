@@ -30,10 +30,11 @@ enum GemmB {
   GEMM_B_TILE_T = 2,  // b [K][N] contracted over its rows, sb tiles [K/32][N/32]
 };
 
-// a_elem / b_elem: payload element types of A and B.
+// a_elem / b_elem: payload element types of A and B; num_cus: compute units
+// of the device (the persistent grid of the 1x32 GEMM).
 hipError_t launch_gemm(int bmode, int a_elem, int b_elem, int64_t M, int64_t N, int64_t K,
                        const void* a, const void* sa, const void* b, const void* sb, void* c,
-                       hipStream_t stream);
+                       int num_cus, hipStream_t stream);
 
 // The same GEMM (E4M3 operands) with its BF16 result quantised in 1x32
 // blocks along N (out_elem 0 = E4M3, 1 = E5M2): q [M, N], s [M, N/32].

@@ -332,6 +332,35 @@ def test_every_tile_written(M, N, K):
     assert_gemm(out, ref, bound, f"tile coverage {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [
+    (10168, 5096, 512),   # 40 x 20 = 800 tiles (at most 32 n-tiles): 3 or 4 per workgroup
+    (1180, 28144, 1024),  # 5 x 110 = 550 tiles: a contiguous eighth per XCD, 2 or 3 each
+    (3032, 7672, 512),    # 12 x 30 = 360: the tiles past the first 256 keep their place
+])
+def test_persistent_walk(M, N, K):
+    """The 1x32 GEMM with more tiles than compute units runs one workgroup
+    per unit walking several tiles, each tile's first loads overlapping the
+    previous tile's stores.  Every tile is written, and one full row of every
+    row of tiles and one full column of every column of tiles (so a row and
+    a column of every tile, edge tiles included) equal the oracle's product."""
+    say(f"[gemm] persistent walk M={M} N={N} K={K}")
+    rng = np.random.default_rng(M + N + K)
+    qa, sa = oracle.quant_row(bits(W.normal_bf16((M, K), 1.0, 53)))
+    qb, sb = oracle.quant_row(bits(W.normal_bf16((N, K), 1.0, 54)))
+    out = _nan_filled(M, N)
+    mx.gemm(dev(qa), dev(sa), dev(qb), dev(sb), "fprop", out=out)
+    _assert_every_tile_written(out, f"persistent {M}x{N}x{K}")
+    rows = np.minimum(np.arange(0, M, 256) + rng.integers(0, 256, (M + 255) // 256), M - 1)
+    cols = np.minimum(np.arange(0, N, 256) + rng.integers(0, 256, (N + 255) // 256), N - 1)
+    rows = np.unique(np.concatenate([rows, [M - 1]])).astype(np.int64)
+    cols = np.unique(np.concatenate([cols, [N - 1]])).astype(np.int64)
+    ri, ci = torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()
+    ref, bound = oracle.gemm(qa[rows], sa[rows], qb, sb, oracle.BKIND_ROW)
+    assert_gemm(out.index_select(0, ri), ref, bound, f"persistent {M}x{N}x{K}: rows")
+    ref, bound = oracle.gemm(qa, sa, qb[cols], sb[cols], oracle.BKIND_ROW)
+    assert_gemm(out.index_select(1, ci), ref, bound, f"persistent {M}x{N}x{K}: columns")
+
+
 @pytest.mark.parametrize("product", ["fprop", "dgrad", "wgrad"])
 def test_dense_config_every_element(product):
     """The dense configuration (8192 x 4096 x 4096): every output element of
