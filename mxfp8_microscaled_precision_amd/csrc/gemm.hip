@@ -505,18 +505,18 @@ struct Tile {
 
   // The LDS_SCALES prologue in two parts, for a persistent caller that
   // issues the next tile's first loads before it stores the current result:
-  // issue_first() loads stage 0 and the first scale group (18 ops per wave
-  // with per-row B scales), issue_second() stage 1 (16 ops); run_issued()
-  // waits for stage 0 only (all but the ops issued after it: stage 1's,
-  // and with `stored` the 32 result stores of the halves epilogue issued
-  // between the two) and runs the K loop into acc.
+  // issue_first() loads stage 0 and the first scale group (17 or 18 ops
+  // per wave), issue_second() stage 1 (16 ops); run_issued() waits for
+  // stage 0 only (all but the ops issued after it: stage 1's, and with
+  // `stored` the 32 result stores of the halves epilogue issued between the
+  // two) and runs the K loop into acc.
   __device__ __forceinline__ void issue_first(int wave, int lane) {
     issue_stage(st0, 0, wave, lane);
     dma_scales(ss0, 0, wave);
   }
   __device__ __forceinline__ void issue_second(int wave, int lane) { issue_stage(st1, BK, wave, lane); }
   __device__ __forceinline__ void run_issued(v16f (&acc)[4][4], int wave, int lane, bool stored) {
-    static_assert(LDS_SCALES && BMODE == GEMM_B_ROW, "op counts assume per-row B scales");
+    static_assert(LDS_SCALES, "the split prologue is the LDS-staged-scale pipeline's");
     const int wm = wave & 1, wn = wave >> 1;
 #pragma unroll
     for (int x = 0; x < 4; x++)
@@ -635,13 +635,13 @@ gemm_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa,
   t.run();
 }
 
-// Persistent form of the 1x32 GEMM (per-row B scales, K a multiple of 512,
-// BF16 result, N a multiple of 8): one workgroup per compute unit walks
-// tiles bid, bid + grid, ... of gemm_kernel's tile map (a grid that is a
-// multiple of 8 keeps every tile on the XCD it has there, index mod 8, so
-// an XCD still runs the same 32-tile groups at a time), and each tile's
-// stage 0 loads while the previous tile's result is stored.
-template <int FA, int FB>
+// Persistent form of the GEMM (K a multiple of 512, BF16 result, N a
+// multiple of 8): one workgroup per compute unit walks tiles bid, bid +
+// grid, ... of gemm_kernel's tile map (a grid that is a multiple of 8 keeps
+// every tile on the XCD it has there, index mod 8, so an XCD still runs the
+// same 32-tile groups at a time), and each tile's stage 0 loads while the
+// previous tile's result is stored.
+template <int BMODE, int FA, int FB>
 __global__ void __launch_bounds__(NT)
 gemm_persistent_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa,
                        const uint8_t* __restrict__ b, const uint8_t* __restrict__ sb,
@@ -653,7 +653,7 @@ gemm_persistent_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict_
   const int64_t nm = (M + BM - 1) / BM, nn = (N + BN - 1) / BN, tiles = nm * nn;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  typedef Tile<GEMM_B_ROW, 1, FA, FB, 0> T1;
+  typedef Tile<BMODE, 1, FA, FB, 0> T1;
   auto make = [&](int64_t t, T1& tl) {
     int64_t mt, nt;
     tile_of(t, nm, nn, mt, nt);
@@ -676,7 +676,7 @@ gemm_persistent_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict_
     tl.ss1 = (lds_u8*)sscale + SCALE_TILE;
     tl.pf_scratch = (lds_u8*)spf;
     tl.pf_a = (nt % (32 / GM_TILES) == 0) ? 0u : OOB;
-    tl.pf_b = (mt % GM_TILES == 0) ? 0u : OOB;
+    tl.pf_b = (mt % GM_TILES == 0 && BMODE != GEMM_B_TILE_T) ? 0u : OOB;
   };
   int64_t t = blockIdx.x;
   if (t >= tiles) return;
@@ -696,13 +696,20 @@ gemm_persistent_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict_
     __syncthreads();
     t += gridDim.x;
     const bool more = __builtin_amdgcn_readfirstlane((int)(t < tiles)) != 0;
+    // 32x32 weights: the lane index through an empty asm, so that what the
+    // next tile's setup and this tile's store derive from it is computed
+    // here, not hoisted out of the loop and held in registers across the K
+    // loop (it was, and they spilled); the 1x32 form fits without it and
+    // measured 1-2% faster on the long-K shapes that way
+    int ln = lane;
+    if constexpr (BMODE != GEMM_B_ROW) asm volatile("" : "+v"(ln));
     if (more) {
       make(t, tl);
-      tl.setup(wave, lane);
-      tl.issue_first(wave, lane);
+      tl.setup(wave, ln);
+      tl.issue_first(wave, ln);
     }
     store_tile_bf16_lds_halves(acc, (lds_u8*)smem1, c, N, m0, m_end, n0, N, wave & 1, wave >> 1,
-                               wave, lane);
+                               wave, ln);
     stored = true;
     if (!more) break;
   }
@@ -887,20 +894,30 @@ hipError_t launch_gemm(int bmode, int a_elem, int b_elem, int64_t M, int64_t N, 
                 *SB = (const uint8_t*)sb;
   uint16_t* C = (uint16_t*)c;
   const int pipe = pipe_of(bmode, N, K);
-  // the 1x32 GEMM with more tiles than compute units runs persistent, one
+  // with more tiles than compute units the GEMM runs persistent, one
   // tile's stores overlapping the next tile's first loads (the halves
-  // epilogue: whole 8-column chunks, 32-bit store offsets)
+  // epilogue: whole 8-column chunks, 32-bit store offsets).  With a 32x32
+  // weight only for K up to 4096: there the overlap gains 3-4% (K = 2048),
+  // while the transposed weight at K = 7168-18432 measured 9% slower
+  // persistent than one tile per workgroup
   const int64_t cus = (num_cus > 0 ? num_cus : 256) / 8 * 8;
-  if (bmode == GEMM_B_ROW && pipe == 1 && N % 8 == 0 && (int64_t)BM * N * 2 < ((int64_t)1 << 31) &&
-      cus >= 8 && tiles > cus) {
+  if (pipe == 1 && N % 8 == 0 && (int64_t)BM * N * 2 < ((int64_t)1 << 31) && cus >= 8 &&
+      tiles > cus && (bmode == GEMM_B_ROW || K <= 4096)) {
     dim3 pg((unsigned)cus);
-#define MX_GEMMP_LAUNCH(FA_, FB_)                                                                 \
-  hipLaunchKernelGGL((gemm_persistent_kernel<FA_, FB_>), pg, dim3(NT), 0, stream, A, SA, B, SB, C, M, \
-                     N, K)
-    if (a_elem == 0 && b_elem == 0) MX_GEMMP_LAUNCH(0, 0);
-    else if (a_elem == 1 && b_elem == 0) MX_GEMMP_LAUNCH(1, 0);
-    else if (a_elem == 0 && b_elem == 1) MX_GEMMP_LAUNCH(0, 1);
-    else MX_GEMMP_LAUNCH(1, 1);
+#define MX_GEMMP_LAUNCH(BM_, FA_, FB_)                                                            \
+  hipLaunchKernelGGL((gemm_persistent_kernel<BM_, FA_, FB_>), pg, dim3(NT), 0, stream, A, SA, B, SB, \
+                     C, M, N, K)
+#define MX_GEMMP_FMT(BM_)                                            \
+  do {                                                               \
+    if (a_elem == 0 && b_elem == 0) MX_GEMMP_LAUNCH(BM_, 0, 0);      \
+    else if (a_elem == 1 && b_elem == 0) MX_GEMMP_LAUNCH(BM_, 1, 0); \
+    else if (a_elem == 0 && b_elem == 1) MX_GEMMP_LAUNCH(BM_, 0, 1); \
+    else MX_GEMMP_LAUNCH(BM_, 1, 1);                                 \
+  } while (0)
+    if (bmode == GEMM_B_ROW) MX_GEMMP_FMT(GEMM_B_ROW);
+    else if (bmode == GEMM_B_TILE) MX_GEMMP_FMT(GEMM_B_TILE);
+    else MX_GEMMP_FMT(GEMM_B_TILE_T);
+#undef MX_GEMMP_FMT
 #undef MX_GEMMP_LAUNCH
     return hipGetLastError();
   }

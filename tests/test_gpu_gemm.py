@@ -361,6 +361,45 @@ def test_persistent_walk(M, N, K):
     assert_gemm(out.index_select(1, ci), ref, bound, f"persistent {M}x{N}x{K}: columns")
 
 
+@pytest.mark.parametrize("layout,M,N,K", [
+    ("fprop", 10168, 5088, 512),   # 40 x 20 = 800 tiles; the last n-tile 224 columns wide
+    ("fprop", 1180, 28160, 512),   # 5 x 110 = 550 tiles: a contiguous eighth per XCD
+    ("dgrad", 3032, 7552, 1024),   # 12 x 30 = 360 tiles; the last n-tile 128 columns wide
+    ("dgrad", 10168, 5120, 512),   # 40 x 20 = 800 tiles
+])
+def test_persistent_walk_block32(layout, M, N, K):
+    """The persistent GEMM with a 32x32-tile weight: fprop takes W [N, K] in
+    tiles, dgrad the transposed weight W [K, N].  Every tile is written, and
+    one full row of every row of tiles and one full column of every column of
+    tiles equal the oracle's product; the columns use W's bytes in row form
+    (the tile scale repeated over its 32 rows, transposed for dgrad), a
+    relayout of the oracle's own quantisation."""
+    say(f"[gemm] persistent walk, 32x32 weight, {layout} M={M} N={N} K={K}")
+    rng = np.random.default_rng(M + N + K + 1)
+    qa, sa = oracle.quant_row(bits(W.normal_bf16((M, K), 1.0, 55)))
+    if layout == "fprop":
+        qb, sb = oracle.quant_block32(bits(W.normal_bf16((N, K), 0.02, 56)))
+        bkind = oracle.BKIND_TILE
+        qbr, sbr = qb, np.repeat(sb, 32, axis=0)
+    else:
+        qb, sb = oracle.quant_block32(bits(W.normal_bf16((K, N), 0.02, 57)))
+        bkind = oracle.BKIND_TILE_T
+        qbr = np.ascontiguousarray(qb.T)
+        sbr = np.repeat(np.ascontiguousarray(sb.T), 32, axis=0)
+    out = _nan_filled(M, N)
+    mx.gemm(dev(qa), dev(sa), dev(qb), dev(sb), layout, "32x32", out=out)
+    _assert_every_tile_written(out, f"persistent 32x32 {layout} {M}x{N}x{K}")
+    rows = np.minimum(np.arange(0, M, 256) + rng.integers(0, 256, (M + 255) // 256), M - 1)
+    cols = np.minimum(np.arange(0, N, 256) + rng.integers(0, 256, (N + 255) // 256), N - 1)
+    rows = np.unique(np.concatenate([rows, [M - 1]])).astype(np.int64)
+    cols = np.unique(np.concatenate([cols, [N - 1]])).astype(np.int64)
+    ri, ci = torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()
+    ref, bound = oracle.gemm(qa[rows], sa[rows], qb, sb, bkind)
+    assert_gemm(out.index_select(0, ri), ref, bound, f"persistent 32x32 {layout}: rows")
+    ref, bound = oracle.gemm(qa, sa, qbr[cols], sbr[cols], oracle.BKIND_ROW)
+    assert_gemm(out.index_select(1, ci), ref, bound, f"persistent 32x32 {layout}: columns")
+
+
 @pytest.mark.parametrize("product", ["fprop", "dgrad", "wgrad"])
 def test_dense_config_every_element(product):
     """The dense configuration (8192 x 4096 x 4096): every output element of
