@@ -696,7 +696,7 @@ def main():
             "traffic_unit": "HBM bytes read + written per launch (mean over the step's launches)",
             "timing": "per launch, the median over the timed steps; rate = work / sum of medians",
             "algorithmic_bytes_per_launch": alg_bytes,
-            "kernel": "gemm_kernel<B_ROW> (1x32 fprop/dgrad/wgrad)",
+            "kernel": "gemm_persistent_kernel<B_ROW> (1x32 fprop/dgrad/wgrad)",
         },
         "quant": {"gbps": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
                   "frac_hbm_peak": round(quant_bytes / (quant_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
