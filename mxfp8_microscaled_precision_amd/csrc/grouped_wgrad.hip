@@ -44,6 +44,7 @@ struct WTile {
   uint32_t svoff;                   // scale offset of this lane: row 64 wave + lane/4, step lane%4
   uint32_t pf_row, pf_a, pf_b;      // L2 prefetch: row offset, enable (0) or OOB
   int64_t nk;                       // K steps of the group
+  bool odd;                         // nk odd: stage s lives in stage buffer (s + 1) % 2
   uint32_t nk2;                     // K steps of the next tile's expert (0: none)
   lds_u8* st0;
   lds_u8* st1;
@@ -198,12 +199,12 @@ struct WTile {
   // per tile): issue_first() loads stage 0 and the first scale group (24
   // ops per wave), issue_second() stage 1 and the next scale part (18 ops).
   __device__ __forceinline__ void issue_first(int wave, int lane) {
-    issue(st0, 0, wave);
+    issue(odd ? st1 : st0, 0, wave);
 #pragma unroll
     for (int u = 0; u < 4; u++) issue_scales(0, u, wave, lane);
   }
   __device__ __forceinline__ void issue_second(int wave, int lane) {
-    issue(st1, 1, wave);
+    issue(odd ? st0 : st1, 1, wave);
     issue_scales(1, 0, wave, lane);  // the part step -1 would load
   }
 
@@ -227,12 +228,13 @@ struct WTile {
     v8i f0a[4], f0b[4], f1a[4], f1b[4];
     read_scales(0, wm, wn, lane, sc_a, sc_b);
     prefetch(2, wave);  // the steps' vmcnt(2) waits assume the latest two ops are prefetches
-    read_frags<0>(st0, wm, wn, lane, f0a, f0b);
-    // an even number of steps: a step past the end multiplies the zero
-    // payload its out-of-range loads left in LDS (scale bytes 0x00, finite),
-    // which is cheaper than a second copy of the step for the odd tail
-    for (int64_t kt = 0; kt < nk; kt += 2) {
-      step(st0, st1, kt, wave, wm, wn, lane, sc_a, sc_b, f0a, f0b, f1a, f1b, acc);
+    read_frags<0>(odd ? st1 : st0, wm, wn, lane, f0a, f0b);
+    // two copies of the step (a third for an odd tail would not fit the
+    // registers): an odd step count enters the pair at its second step,
+    // with the stages one buffer along (the prologue did what the skipped
+    // step -1 would: stage 1's loads, the scale part, the prefetch)
+    for (int64_t kt = odd ? -1 : 0; kt < nk; kt += 2) {
+      if (kt >= 0) step(st0, st1, kt, wave, wm, wn, lane, sc_a, sc_b, f0a, f0b, f1a, f1b, acc);
       step(st1, st0, kt + 1, wave, wm, wn, lane, sc_a, sc_b, f0a, f0b, f1a, f1b, acc);
     }
   }
@@ -368,6 +370,7 @@ grouped_wgrad_kernel(int64_t G, const int64_t* __restrict__ offsets, int64_t T, 
     const int64_t P = 128 * (lo / 128 + g);
     const int64_t P2 = g2 >= 0 ? 128 * (lo2 / 128 + g2) : 0;
     wt.nk = (hi - lo + BK - 1) / BK;
+    wt.odd = (wt.nk & 1) != 0;
     wt.nk2 = g2 >= 0 ? (uint32_t)((hi2 - lo2 + BK - 1) / BK) : 0u;
     wt.st0 = (lds_u8*)smem0;
     wt.st1 = (lds_u8*)smem1;
@@ -410,8 +413,10 @@ grouped_wgrad_kernel(int64_t G, const int64_t* __restrict__ offsets, int64_t T, 
       // and it waits for stage 0 only: the stores drain under its first K
       // step
       if (more) wt.issue_first(wave, lane);
-      store_tile_bf16_lds_halves(acc, (lds_u8*)smem1, ct, N, cc.m0, cc.m_end, cc.n0, N, wave & 1,
-                                 wave >> 1, wave, lane);
+      // through the stage buffer the next tile's stage 0 does not use
+      lds_u8* const sbuf = (more && wt.odd) ? (lds_u8*)smem0 : (lds_u8*)smem1;
+      store_tile_bf16_lds_halves(acc, sbuf, ct, N, cc.m0, cc.m_end, cc.n0, N, wave & 1, wave >> 1,
+                                 wave, lane);
       stored = true;
     } else {
       // (the store ends with a barrier: the next tile may reuse the stages)

@@ -261,6 +261,10 @@ def test_wgrad_equals_dense_gemm_per_expert():
     ([5000, 300, 2600, 1, 700], 4096, 2048),                          # 128 per expert: 2 groups
     ([700, 260], 4608, 4608),        # 324 tiles per expert, more than the grid: a strided walk
     ([(37 * g) % 300 for g in range(100)], 768, 256),                # 3 per expert: a strided walk
+    # every step count from 1 to 24: a workgroup's consecutive tiles have odd
+    # and even counts (an odd count starts in the other stage buffer, and
+    # the previous result then leaves through the first)
+    ([125 * s for s in range(1, 25)], 1024, 1024),
 ])
 def test_wgrad_schedules_equal_dense_gemm(sizes, M, N):
     """The persistent weight gradient's tile walk, in each of its forms (the
