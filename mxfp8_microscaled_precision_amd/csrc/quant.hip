@@ -125,8 +125,6 @@ quant_block32_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C, uint8
 constexpr int TILE_THREADS = 512;
 constexpr int TILE_ROWS = 128;
 constexpr int TILE_COLS = 128;
-constexpr int TILE_MAX_RUN = 8;  // row tiles one workgroup walks (grouped column mode)
-constexpr int CHIP_CUS = 256;    // MI355X compute units (sizes the runs only)
 
 enum TileMode { TILE_COL = 1, TILE_DUAL = 2, TILE_BLOCK32 = 3, TILE_GCOL = 4 };
 
@@ -190,16 +188,13 @@ __device__ __forceinline__ void gcol_block(const int64_t* __restrict__ offsets, 
   nreal = left <= 0 ? 0 : (left >= 32 ? 32 : (int)left);
 }
 
-// One 128 x 128 tile at rows R0.., columns C0...  The
-// tile's column scales go to LST at blocks 4p .. 4p+3 of each column's
-// 4 * LRUN; with LRUN == 1 the tile also stores them (a run stores them
-// once for all its tiles).
-template <int MODE, int EL, int LRUN>
+// One 128 x 128 tile at rows R0.., columns C0.. (one tile per workgroup).
+template <int MODE, int EL>
 __device__ __forceinline__ void quant_tile(const uint16_t* __restrict__ x, int64_t R, int64_t C,
                                            uint8_t* __restrict__ q, uint8_t* __restrict__ s,
                                            uint8_t* __restrict__ qt, uint8_t* __restrict__ st,
                                            int64_t G, const int64_t* __restrict__ offsets,
-                                           int64_t T, int64_t R0, int p, lds8* LQ, lds8* LQT,
+                                           int64_t T, int64_t R0, lds8* LQ, lds8* LQT,
                                            lds8* LS, lds8* LST, int64_t C0) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 3, h = lane & 7;
@@ -280,7 +275,7 @@ __device__ __forceinline__ void quant_tile(const uint16_t* __restrict__ x, int64
   uint32_t mine = sbc[0];
 #pragma unroll
   for (int j = 1; j < 8; j++) mine = (g == j) ? sbc[j] : mine;
-  LST[(cl + g) * (4 * LRUN) + 4 * p + wr] = (uint8_t)mine;
+  LST[(cl + g) * 4 + wr] = (uint8_t)mine;
   __syncthreads();
 
   // write out: 16-byte chunks, 8 lanes per 128-byte output row
@@ -303,7 +298,7 @@ __device__ __forceinline__ void quant_tile(const uint16_t* __restrict__ x, int64
     }
   }
   // scales: four consecutive blocks per row / column
-  if (LRUN == 1 && t < TILE_COLS && t < cols_here) {
+  if (t < TILE_COLS && t < cols_here) {
     uint8_t* dst = st + (C0 + t) * (R >> 5) + (R0 >> 5);
     const int nb = (int)(rows_here >> 5);
     if (nb == 4 && ((uintptr_t)dst & 3) == 0) {
@@ -326,18 +321,12 @@ __device__ __forceinline__ void quant_tile(const uint16_t* __restrict__ x, int64
 
 // grid.z indexes a batch of equally shaped matrices (contiguous inputs and
 // outputs); the grouped column mode uses G, offsets and T (x has T rows, R is
-// the padded capacity).  In the grouped column mode a workgroup walks `run`
-// consecutive row tiles (run <= TILE_MAX_RUN, chosen by the launcher) and
-// stores each column's 4 * run scale bytes in one piece at the end instead
-// of four bytes per tile: fewer partly written memory lines.  The other
-// modes take one tile per workgroup (a run measured slower there).  At
-// least 6 waves per SIMD: holds the grouped column loop to 80 VGPRs (the
-// other modes need fewer, so it changes nothing for them).
+// the padded capacity).  One tile per workgroup in every mode.
 template <int MODE, int EL>
-__global__ void __launch_bounds__(TILE_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
+__global__ void __launch_bounds__(TILE_THREADS)
 quant_tile_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C, uint8_t* __restrict__ q,
                   uint8_t* __restrict__ s, uint8_t* __restrict__ qt, uint8_t* __restrict__ st,
-                  int64_t G, const int64_t* __restrict__ offsets, int64_t T, int run) {
+                  int64_t G, const int64_t* __restrict__ offsets, int64_t T) {
   if (blockIdx.z) {
     const int64_t z = blockIdx.z, n = R * C;
     x += z * n;
@@ -346,56 +335,22 @@ quant_tile_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t C, uint8_t*
     qt += qt ? z * n : 0;
     st += st ? z * (n >> 5) : 0;
   }
-  constexpr int LRUN = MODE == TILE_GCOL ? TILE_MAX_RUN : 1;
   __shared__ __attribute__((aligned(16))) uint8_t lq[TILE_ROWS * 128];   // row payload
   __shared__ __attribute__((aligned(16))) uint8_t lqt[TILE_COLS * 128];  // column payload
   __shared__ __attribute__((aligned(16))) uint8_t ls[TILE_ROWS * 4];     // row scales
-  __shared__ __attribute__((aligned(16))) uint8_t lst[TILE_COLS * 4 * LRUN];  // column scales
-  lds8* LQ = (lds8*)lq;
-  lds8* LQT = (lds8*)lqt;
-  lds8* LS = (lds8*)ls;
-  lds8* LST = (lds8*)lst;
-  if (LRUN == 1) {
-    // dispatch order (measured): the column mode goes along the rows of x,
-    // column tiles fastest; the dual mode down its columns, row tiles
-    // fastest (as the grid is laid out)
-    int64_t tr = blockIdx.x, tc = blockIdx.y;
-    if (MODE == TILE_COL) {
-      const int64_t lin = (int64_t)blockIdx.x + (int64_t)blockIdx.y * gridDim.x;
-      tr = lin / gridDim.y;
-      tc = lin - tr * gridDim.y;
-    }
-    quant_tile<MODE, EL, 1>(x, R, C, q, s, qt, st, G, offsets, T, tr * TILE_ROWS, 0, LQ, LQT, LS, LST,
-                            tc * TILE_COLS);
-    return;
+  __shared__ __attribute__((aligned(16))) uint8_t lst[TILE_COLS * 4];    // column scales
+  // dispatch order (measured): the column modes go along the rows of x,
+  // column tiles fastest, so that the 32 row tiles sharing each line of the
+  // column-scale array run close together and the line leaves L2 whole; the
+  // dual mode down its columns, row tiles fastest (as the grid is laid out)
+  int64_t tr = blockIdx.x, tc = blockIdx.y;
+  if (MODE == TILE_COL || MODE == TILE_GCOL) {
+    const int64_t lin = (int64_t)blockIdx.x + (int64_t)blockIdx.y * gridDim.x;
+    tr = lin / gridDim.y;
+    tc = lin - tr * gridDim.y;
   }
-  const int64_t RUN0 = (int64_t)blockIdx.x * run * TILE_ROWS;
-  for (int p = 0; p < run; p++) {
-    const int64_t R0 = RUN0 + (int64_t)p * TILE_ROWS;
-    if (R0 >= R) break;      // uniform over the workgroup
-    if (p) __syncthreads();  // the previous tile's LDS reads are done
-    quant_tile<MODE, EL, LRUN>(x, R, C, q, s, qt, st, G, offsets, T, R0, p, LQ, LQT, LS, LST,
-                               (int64_t)blockIdx.y * TILE_COLS);
-  }
-  // the run's column scales (the last tile's barrier made them visible)
-  const int t = threadIdx.x;
-  const int64_t C0 = (int64_t)blockIdx.y * TILE_COLS;
-  const int64_t cols_here = (C - C0) < TILE_COLS ? (C - C0) : TILE_COLS;
-  if (RUN0 < R && t < cols_here) {
-    const int64_t span = (int64_t)run * TILE_ROWS;
-    const int nb = (int)(((R - RUN0) < span ? (R - RUN0) : span) >> 5);
-    uint8_t* dst = st + (C0 + t) * (R >> 5) + (RUN0 >> 5);
-    const lds8* src = LST + t * (4 * LRUN);
-    if ((nb & 15) == 0 && ((uintptr_t)dst & 15) == 0) {
-      for (int b = 0; b < nb; b += 16)
-        *(u32x4*)(dst + b) = *(const __attribute__((address_space(3))) u32x4*)(src + b);
-    } else if ((nb & 3) == 0 && ((uintptr_t)dst & 3) == 0) {
-      for (int b = 0; b < nb; b += 4)
-        *(uint32_t*)(dst + b) = *(const __attribute__((address_space(3))) uint32_t*)(src + b);
-    } else {
-      for (int b = 0; b < nb; b++) dst[b] = src[b];
-    }
-  }
+  quant_tile<MODE, EL>(x, R, C, q, s, qt, st, G, offsets, T, tr * TILE_ROWS, (lds8*)lq, (lds8*)lqt,
+                       (lds8*)ls, (lds8*)lst, tc * TILE_COLS);
 }
 
 // ---------------------------------------------------------------------------
@@ -417,24 +372,12 @@ hipError_t launch_quant_row(const void* x, int64_t n, void* q, void* s, int elem
   return hipGetLastError();
 }
 
-// Row tiles per workgroup (grouped column mode): the most, up to
-// TILE_MAX_RUN, that still leaves at least four workgroups per compute unit.
-static int tile_run(int mode, int64_t row_tiles, int64_t other_tiles) {
-  if (mode != TILE_GCOL) return 1;
-  int run = TILE_MAX_RUN;
-  while (run > 1 && ((row_tiles + run - 1) / run) * other_tiles < 4 * CHIP_CUS) run >>= 1;
-  return run;
-}
-
 template <int MODE, int EL>
 static void launch_tile(dim3 grid, const void* x, int64_t R, int64_t C, void* q, void* s, void* qt,
                         void* st, int64_t G, const int64_t* offsets, int64_t T, hipStream_t stream) {
-  const int64_t row_tiles = grid.x;
-  const int run = tile_run(MODE, row_tiles, (int64_t)grid.y * grid.z);
-  grid.x = (unsigned)((row_tiles + run - 1) / run);
   hipLaunchKernelGGL((quant_tile_kernel<MODE, EL>), grid, dim3(TILE_THREADS), 0, stream,
                      (const uint16_t*)x, R, C, (uint8_t*)q, (uint8_t*)s, (uint8_t*)qt, (uint8_t*)st,
-                     G, offsets, T, run);
+                     G, offsets, T);
 }
 
 template <int MODE>

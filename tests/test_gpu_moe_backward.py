@@ -59,24 +59,24 @@ def test_quant_grouped_col_exact(sizes, C):
 
 
 @pytest.mark.parametrize("sizes,C", [
-    # 266 row tiles of 128 in runs of 8 (the last run 2 tiles); scale rows of
-    # 1064 bytes, so the run's scales leave as 4-byte words
+    # 266 row tiles of 128 (more than one column tile's worth of scale
+    # lines); scale rows of 1064 bytes, not a whole number of 16-byte words
     ([4000, 0, 12345, 1, 7000, 33, 0, 9000, 622], 4096),
-    # 4067 row tiles in runs of 4 (the last run 3 tiles), a 32-column last tile
+    # 4067 row tiles, a 32-column last column tile
     ([100000, 200001, 0, 120000, 100000], 160),
 ])
-def test_quant_grouped_col_tile_runs(sizes, C):
-    """Shapes large enough that a workgroup walks a run of row tiles, with a
-    partial last run: every byte against the oracle."""
+def test_quant_grouped_col_many_tiles(sizes, C):
+    """Shapes with many row tiles in the column-tiles-first dispatch order
+    and partial edge tiles: every byte against the oracle."""
     off = _offsets(sizes)
     T = int(off[-1])
-    say(f"[moe-bwd] grouped col runs T={T} G={len(sizes)} C={C}")
+    say(f"[moe-bwd] grouped col many tiles T={T} G={len(sizes)} C={C}")
     x = W.normal_with_outliers_bf16((T, C), 1.0, 0.01, 100.0, T + 3 * C)
     q, s = mx.quant_grouped_col(x.cuda(), dev(off))
     torch.cuda.synchronize()
     wq, ws = oracle.quant_col_grouped(bits(x), off)
-    assert_bytes(q, wq, "grouped runs q_t")
-    assert_bytes(s, ws, "grouped runs s_t")
+    assert_bytes(q, wq, "grouped many tiles q_t")
+    assert_bytes(s, ws, "grouped many tiles s_t")
 
 
 def test_quant_grouped_col_special_values():
