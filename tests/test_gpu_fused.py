@@ -59,15 +59,53 @@ def test_fused_equals_quantised_gemm_and_oracle_bound(M, N, K, layout, bscale, o
     assert_bytes(q, host(q2), "fused payload vs quantised GEMM")
     assert_bytes(s, host(s2), "fused scales vs quantised GEMM")
     ref, bound = oracle.gemm(qa, sa, qb, sb, bk)
+    _assert_within_bound(host(q), host(s), ref, bound, out_elem)
+
+
+def _assert_within_bound(q, s, ref, bound, out_elem, what=""):
+    """Dequantised fused output within the GEMM tolerance plus the payload's
+    rounding of the binary64 product (the bound in the module docstring)."""
     elem = oracle.ELEMS[out_elem]
     table = oracle.e5m2_decode_table() if elem == oracle.ELEM_E5M2 else oracle.e4m3_decode_table()
-    e = host(s).astype(np.int64) - 127
-    deq = table[host(q)] * np.exp2(np.repeat(e, 32, axis=1))
+    e = s.astype(np.int64) - 127
+    deq = table[q] * np.exp2(np.repeat(e, 32, axis=1))
     tol = 2.0 ** -7 * bound + 1e-6
     u, sub = (2.0 ** -3, 17) if elem == oracle.ELEM_E5M2 else (2.0 ** -4, 10)
     lim = tol + u * (np.abs(ref) + tol) + np.exp2(np.repeat(e, 32, axis=1) - sub)
     bad = ~(np.abs(deq - ref) <= lim)
-    assert not bad.any(), (int(bad.sum()), np.argwhere(bad)[:4])
+    assert not bad.any(), (what, int(bad.sum()), np.argwhere(bad)[:4])
+
+
+@pytest.mark.parametrize("out_elem", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("M,N,K", [
+    (10168, 5088, 512),   # 40 x 20 = 800 tiles (at most 32 n-tiles: runs of 32 per XCD)
+    (1180, 28160, 512),   # 5 x 110 = 550 tiles: a contiguous eighth per XCD
+    (3032, 7648, 1024),   # 12 x 30 = 360 tiles; the last n-tile 224 columns wide
+])
+def test_fused_many_tiles(M, N, K, out_elem):
+    """The fused producer over hundreds of tiles with ragged edges, in both
+    workgroup-to-tile maps.  Outputs start as a sentinel byte: every byte
+    equals the row quantiser applied to the unfused GEMM's result (so every
+    tile was written), and one full row of every row of tiles lies within
+    the oracle bound."""
+    say(f"[fused] many tiles {M}x{N}x{K} -> {out_elem}")
+    qa, sa, qb, sb, bk = _operands(M, N, K, "fprop", "1x32", M + N + K + 7)
+    A, SA, B, SB = dev(qa), dev(sa), dev(qb), dev(sb)
+    q = torch.full((M, N), 0xA5, dtype=torch.uint8, device="cuda")
+    s = torch.full((M, N // 32), 0xA5, dtype=torch.uint8, device="cuda")
+    rc = mx.mx_gemm_quant(mx.GEMM_LAYOUTS["fprop"], mx.BSCALE_KINDS["1x32"], mx.ELEM_TYPES[out_elem],
+                          M, N, K, A.data_ptr(), SA.data_ptr(), B.data_ptr(), SB.data_ptr(),
+                          q.data_ptr(), s.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    assert rc == 0, mx.mx_last_error()
+    q2, s2 = mx.quant(mx.gemm(A, SA, B, SB), "row", out_elem)
+    torch.cuda.synchronize()
+    assert_bytes(q, host(q2), "fused payload vs quantised GEMM")
+    assert_bytes(s, host(s2), "fused scales vs quantised GEMM")
+    rng = np.random.default_rng(M + N)
+    rows = np.minimum(np.arange(0, M, 256) + rng.integers(0, 256, (M + 255) // 256), M - 1)
+    rows = np.unique(np.concatenate([rows, [M - 1]])).astype(np.int64)
+    ref, bound = oracle.gemm(qa[rows], sa[rows], qb, sb, bk)
+    _assert_within_bound(host(q)[rows], host(s)[rows], ref, bound, out_elem, "sampled rows")
 
 
 @pytest.mark.parametrize("layout,bscale,N", [("dgrad", "32x32", 512), ("fprop", "32x32", 544),
