@@ -17,7 +17,10 @@ multiple of 128 (the general variant), through the 32x32-weight forward
 (tile scales) and backward-data (the shared weight read transposed) forms,
 the grouped MoE GEMM, the per-expert weight gradient, and the fused
 producer, whose expected bytes are the oracle's row quantisation of the
-oracle's exact product."""
+oracle's exact product.  The persistent GEMM (more output tiles than compute
+units, the next tile's first stage loading under the current tile's
+stores) is run at the stack's K values and, with 32x32 weights, at
+K = 4096."""
 import numpy as np
 import pytest
 import torch
@@ -125,6 +128,52 @@ def test_tile_scales_dgrad_exact(K, N):
     torch.cuda.synchronize()
     ref, _ = oracle.gemm(qa, sa, qw, sw, oracle.BKIND_TILE_T, want_bound=False)
     assert_exact(c, ref, f"32x32 dgrad K={K} N={N}")
+
+
+def _persistent_rows(qa, M, K, rng):
+    """Rows checked in the persistent cases: 24 seeded rows of every 256-row
+    tile plus, in every tile, the rows whose nonzero lies in the first or
+    the last K step (the split prologue and the last stage)."""
+    k = np.argmax(qa != 0, axis=1)
+    step = k // 128
+    nks = K // 128
+    rows = []
+    for m0 in range(0, M, 256):
+        tile = np.arange(m0, min(m0 + 256, M))
+        rows.append(rng.choice(tile, min(24, len(tile)), replace=False))
+        rows.append(tile[(step[tile] == 0) | (step[tile] == nks - 1)])
+    return np.unique(np.concatenate(rows)).astype(np.int64)
+
+
+@pytest.mark.parametrize("K,bscale,layout", [(7168, "1x32", "fprop"), (18432, "1x32", "fprop"),
+                                             (32768, "1x32", "fprop"), (4096, "32x32", "fprop"),
+                                             (4096, "32x32", "dgrad")])
+def test_persistent_exact(K, bscale, layout):
+    """More output tiles than compute units (17 x 16 = 272): the persistent
+    GEMM, whose tiles after the first load their first stages while the
+    previous result is stored.  All rows one-hot; the checked rows cover
+    every tile row and, across the tiles, the first and last K steps; each
+    equals the oracle bit for bit over all N."""
+    M, N = 4352, 4096
+    say(f"[exact] persistent {bscale} {layout} M={M} N={N} K={K}")
+    qa, sa = one_hot_a(M, K, K + 11)
+    rng = np.random.default_rng(K + 12)
+    if bscale == "1x32":
+        qb, sb = random_b(N, K, K + 13)
+        bk = oracle.BKIND_ROW
+    elif layout == "fprop":
+        qb, sb = random_b(N, K, K + 13, scale_rows=N // 32)
+        bk = oracle.BKIND_TILE
+    else:
+        qb = rng.choice(_NONZERO, (K, N)).astype(np.uint8)
+        sb = rng.integers(120, 135, (K // 32, N // 32)).astype(np.uint8)
+        bk = oracle.BKIND_TILE_T
+    c = mx.gemm(dev(qa), dev(sa), dev(qb), dev(sb), layout, bscale)
+    torch.cuda.synchronize()
+    rows = _persistent_rows(qa, M, K, rng)
+    ref, _ = oracle.gemm(qa[rows], sa[rows], qb, sb, bk, want_bound=False)
+    assert_exact(c.index_select(0, torch.from_numpy(rows).cuda()), ref,
+                 f"persistent {bscale} {layout} K={K} ({len(rows)} rows)")
 
 
 def _offsets(sizes):
