@@ -20,7 +20,8 @@ producer, whose expected bytes are the oracle's row quantisation of the
 oracle's exact product.  The persistent GEMM (more output tiles than compute
 units, the next tile's first stage loading under the current tile's
 stores) is run at the stack's K values and, with 32x32 weights, at
-K = 4096."""
+K = 4096; the grouped GEMM walks two or three tiles per workgroup at the
+MoE K values."""
 import numpy as np
 import pytest
 import torch
@@ -198,6 +199,25 @@ def test_grouped_exact(K):
     torch.cuda.synchronize()
     ref, _ = oracle.grouped_gemm(off, qa, sa, qb, sb, want_bound=False)
     assert_exact(c, ref, f"grouped K={K}")
+
+
+@pytest.mark.parametrize("K", [4096, 2048])
+def test_grouped_persistent_exact(K):
+    """The grouped GEMM with 40 x 14 = 560 tiles: every workgroup walks two or
+    three, each tile after the first loading its first stage while the
+    previous result is stored; ragged and empty groups; every output equals
+    the oracle bit for bit."""
+    sizes = [1500, 700, 0, 2100, 900, 1300, 33, 2600]
+    off = _offsets(sizes)
+    T, N, G = int(off[-1]), 3584, len(sizes)
+    say(f"[exact] grouped persistent T={T} N={N} K={K} G={G}")
+    qa, sa = one_hot_a(T, K, K + 8)
+    qb, sb = random_b(G * N, K, K + 9)
+    qb, sb = qb.reshape(G, N, K), sb.reshape(G, N, K // 32)
+    c = mx.grouped_gemm(dev(off), dev(qa), dev(sa), dev(qb), dev(sb))
+    torch.cuda.synchronize()
+    ref, _ = oracle.grouped_gemm(off, qa, sa, qb, sb, want_bound=False)
+    assert_exact(c, ref, f"grouped persistent K={K}")
 
 
 @pytest.mark.parametrize("sizes", [[18000, 0, 9001, 13000], [4097, 2049, 130, 31]])
