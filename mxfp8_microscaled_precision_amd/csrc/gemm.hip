@@ -676,10 +676,11 @@ gemm_persistent_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict_
     tl.ss1 = (lds_u8*)sscale + SCALE_TILE;
     tl.pf_scratch = (lds_u8*)spf;
     tl.pf_a = (nt % (32 / GM_TILES) == 0) ? 0u : OOB;
-    // B only with more than 32 n-tiles: with at most 32 the XCDs take the
-    // runs of one group in turn, and prefetching B there measured 2.5-4.6%
-    // slower on the K = 18432 and 32768 shapes (N = 7168)
-    tl.pf_b = (mt % GM_TILES == 0 && BMODE != GEMM_B_TILE_T && nn > 32) ? 0u : OOB;
+    // B only where each XCD walks its own eighth of the order: where the
+    // XCDs take the runs of one group in turn, prefetching B measured
+    // 2.5-4.6% slower on the K = 18432 and 32768 shapes (N = 7168)
+    tl.pf_b = (mt % GM_TILES == 0 && BMODE != GEMM_B_TILE_T &&
+               !tile_runs_rr((uint32_t)nm, (uint32_t)nn)) ? 0u : OOB;
   };
   int64_t t = blockIdx.x;
   if (t >= tiles) return;

@@ -146,16 +146,19 @@ def _persistent_rows(qa, M, K, rng):
     return np.unique(np.concatenate(rows)).astype(np.int64)
 
 
-@pytest.mark.parametrize("K,bscale,layout", [(7168, "1x32", "fprop"), (18432, "1x32", "fprop"),
-                                             (32768, "1x32", "fprop"), (4096, "32x32", "fprop"),
-                                             (4096, "32x32", "dgrad")])
-def test_persistent_exact(K, bscale, layout):
-    """More output tiles than compute units (17 x 16 = 272): the persistent
-    GEMM, whose tiles after the first load their first stages while the
-    previous result is stored.  All rows one-hot; the checked rows cover
-    every tile row and, across the tiles, the first and last K steps; each
-    equals the oracle bit for bit over all N."""
-    M, N = 4352, 4096
+@pytest.mark.parametrize("K,bscale,layout,M,N", [
+    (7168, "1x32", "fprop", 4352, 4096), (18432, "1x32", "fprop", 4352, 4096),
+    (32768, "1x32", "fprop", 4352, 4096), (4096, "32x32", "fprop", 4352, 4096),
+    (4096, "32x32", "dgrad", 4352, 4096),
+    (18432, "1x32", "fprop", 4096, 10240),   # 16 x 40 = 640 tiles: a contiguous eighth per XCD
+])
+def test_persistent_exact(K, bscale, layout, M, N):
+    """More output tiles than compute units (17 x 16 = 272, runs of 32 dealt to
+    the XCDs in turn; 16 x 40 = 640, a contiguous eighth per XCD): the
+    persistent GEMM, whose tiles after the first load their first stages
+    while the previous result is stored.  All rows one-hot; the checked rows
+    cover every tile row and, across the tiles, the first and last K steps;
+    each equals the oracle bit for bit over all N."""
     say(f"[exact] persistent {bscale} {layout} M={M} N={N} K={K}")
     qa, sa = one_hot_a(M, K, K + 11)
     rng = np.random.default_rng(K + 12)

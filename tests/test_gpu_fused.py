@@ -79,7 +79,8 @@ def _assert_within_bound(q, s, ref, bound, out_elem, what=""):
 @pytest.mark.parametrize("out_elem", ["e4m3", "e5m2"])
 @pytest.mark.parametrize("M,N,K", [
     (10168, 5088, 512),   # 40 x 20 = 800 tiles (at most 32 n-tiles: runs of 32 per XCD)
-    (1180, 28160, 512),   # 5 x 110 = 550 tiles: a contiguous eighth per XCD
+    (1180, 28160, 512),   # 5 x 110 = 550 tiles: runs of 32 (eighths not whole groups)
+    (4056, 10240, 512),   # 16 x 40 = 640 tiles: a contiguous eighth per XCD
     (3032, 7648, 1024),   # 12 x 30 = 360 tiles; the last n-tile 224 columns wide
 ])
 def test_fused_many_tiles(M, N, K, out_elem):

@@ -318,7 +318,9 @@ def test_stack_layer_full_32x32_variant():
 @pytest.mark.parametrize("M,N,K", [
     (2088, 7264, 512),   # 9 x 29 = 261 tiles, at most 32 n-tiles: runs of 32 dealt to the XCDs
                          # in turn over the first 256, the last 5 in place; partial edge tiles
-    (2100, 8400, 512),   # 9 x 33 = 297 tiles: a contiguous eighth per XCD, 297 % 8 = 1
+    (2100, 8400, 512),   # 9 x 33 = 297 tiles: more than 32 n-tiles, eighths not whole
+                         # groups of 8 tiles, so runs of 32 round-robin again
+    (1948, 10216, 512),  # 8 x 40 = 320 tiles: a contiguous eighth of 40 tiles per XCD
 ])
 def test_every_tile_written(M, N, K):
     say(f"[gemm] tile coverage M={M} N={N} K={K}")
@@ -334,8 +336,9 @@ def test_every_tile_written(M, N, K):
 
 @pytest.mark.parametrize("M,N,K", [
     (10168, 5096, 512),   # 40 x 20 = 800 tiles (at most 32 n-tiles): 3 or 4 per workgroup
-    (1180, 28144, 1024),  # 5 x 110 = 550 tiles: a contiguous eighth per XCD, 2 or 3 each
+    (1180, 28144, 1024),  # 5 x 110 = 550 tiles, eighths not whole groups: runs of 32, 2 or 3 each
     (3032, 7672, 512),    # 12 x 30 = 360: the tiles past the first 256 keep their place
+    (4056, 10232, 512),   # 16 x 40 = 640 tiles: a contiguous eighth of 80 per XCD, 2 or 3 each
 ])
 def test_persistent_walk(M, N, K):
     """The 1x32 GEMM with more tiles than compute units runs one workgroup
@@ -363,7 +366,8 @@ def test_persistent_walk(M, N, K):
 
 @pytest.mark.parametrize("layout,M,N,K", [
     ("fprop", 10168, 5088, 512),   # 40 x 20 = 800 tiles; the last n-tile 224 columns wide
-    ("fprop", 1180, 28160, 512),   # 5 x 110 = 550 tiles: a contiguous eighth per XCD
+    ("fprop", 1180, 28160, 512),   # 5 x 110 = 550 tiles: runs of 32 (eighths not whole groups)
+    ("fprop", 4056, 10240, 512),   # 16 x 40 = 640 tiles: a contiguous eighth per XCD
     ("dgrad", 3032, 7552, 1024),   # 12 x 30 = 360 tiles; the last n-tile 128 columns wide
     ("dgrad", 10168, 5120, 512),   # 40 x 20 = 800 tiles
 ])
