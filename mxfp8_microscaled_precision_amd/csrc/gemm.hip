@@ -71,7 +71,7 @@ struct Tile {
   u32x4 ra, rb, rsa, rsb;
   uint32_t svoff;               // scale-tile load offset of this lane's row
   uint32_t svoff_b, sb_row;     // the same for B's scales; bytes per block index
-  // L2 prefetch (B_ROW with LDS_SCALES): the first workgroup of each
+  // L2 prefetch (the LDS_SCALES pipeline): the first workgroup of each
   // concurrently running group to need a K slice fetches it PF_DIST steps
   // ahead of use; pf_a / pf_b are 0 for the operands this workgroup
   // prefetches and OOB (no memory access) otherwise.
