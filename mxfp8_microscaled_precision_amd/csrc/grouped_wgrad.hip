@@ -337,6 +337,29 @@ grouped_wgrad_kernel(int64_t G, const int64_t* __restrict__ offsets, int64_t T, 
     int g;
     int64_t m0, m_end, n0;
   };
+  struct Pos {  // output tile u of an expert: its tiles and prefetch duties
+    uint32_t mt, nt;
+    bool pfa, pfb;
+  };
+  // tile u's place in the grouped order; A is prefetched by a run's first
+  // n-tile column, B by the first m-tile of each GM_TILES group (32-bit
+  // arithmetic: per < 2^31)
+  auto pos_of = [&](uint32_t u) -> Pos {
+    const uint32_t un = (uint32_t)nn, um = (uint32_t)nm, ur = (uint32_t)run;
+    const uint32_t L = (per & 7) == 0 ? (u & 7) * ur + (u >> 3) : u;
+    const uint32_t first = L / (GM_TILES * un) * GM_TILES;
+    const uint32_t gsz = (um - first) < GM_TILES ? (um - first) : GM_TILES;
+    const uint32_t in = L % (GM_TILES * un);
+    const uint32_t pos = (per & 7) == 0 ? (L % ur) : L;
+    Pos p;
+    p.mt = first + in % gsz;
+    p.nt = in / gsz;
+    p.pfa = pos < gsz;
+    p.pfb = p.mt == first;
+    return p;
+  };
+  // with groups, a workgroup keeps one output tile of every expert it runs
+  const Pos fixed = pos_of((uint32_t)(w % per));
   // LDS values read at uniform addresses come back in vector registers;
   // readfirstlane keeps the tile's bookkeeping in scalar ones
   auto rfl = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
@@ -361,12 +384,8 @@ grouped_wgrad_kernel(int64_t G, const int64_t* __restrict__ offsets, int64_t T, 
     }
     const int64_t lo = rfl(s_lo[g]), hi = rfl(s_hi[g]);
     const int64_t lo2 = g2 >= 0 ? rfl(s_lo[g2]) : 0, hi2 = g2 >= 0 ? rfl(s_hi[g2]) : 0;
-    const int64_t L = (per & 7) == 0 ? (u & 7) * run + (u >> 3) : u;
-    // grouped order inside the expert: GM_TILES m-tiles, n-tiles outer
-    const int64_t first = L / (GM_TILES * nn) * GM_TILES;
-    const int64_t gsz = (nm - first) < GM_TILES ? (nm - first) : GM_TILES;
-    const int64_t in = L % (GM_TILES * nn);
-    const int64_t mt = first + in % gsz, nt = in / gsz;
+    const Pos ps = groups > 0 ? fixed : pos_of((uint32_t)u);
+    const int64_t mt = ps.mt, nt = ps.nt;
     const int64_t P = 128 * (lo / 128 + g);
     const int64_t P2 = g2 >= 0 ? 128 * (lo2 / 128 + g2) : 0;
     wt.nk = (hi - lo + BK - 1) / BK;
@@ -382,11 +401,9 @@ grouped_wgrad_kernel(int64_t G, const int64_t* __restrict__ offsets, int64_t T, 
     cu.m_end = (cu.m0 + BM) < M ? cu.m0 + BM : M;
     const int64_t n_end = (cu.n0 + BN) < N ? cu.n0 + BN : N;
     wt.setup(a, sa, b, sb, ld, cu.m0, cu.m_end - cu.m0, cu.n0, n_end - cu.n0, P, P2, wave, lane);
-    // prefetch only where a run first needs a slice: A by the run's first
-    // n-tile column, B by the first m-tile of each GM_TILES group
-    const int64_t pos = (per & 7) == 0 ? (L % run) : L;
-    wt.pf_a = pos < gsz ? 0u : OOB;
-    wt.pf_b = mt == first ? 0u : OOB;
+    // prefetch only where a run first needs a slice
+    wt.pf_a = ps.pfa ? 0u : OOB;
+    wt.pf_b = ps.pfb ? 0u : OOB;
     return true;
   };
   // one WTile: after a tile's K loop it is set up over the next tile (the
