@@ -254,7 +254,12 @@ mx_status mx_gemm_quant(mx_gemm_layout layout, mx_bscale_kind bkind, mx_elem_typ
   } else {
     int bmode = mx::GEMM_B_ROW;
     if (bkind == MX_BSCALE_32x32) bmode = layout == MX_GEMM_DGRAD ? mx::GEMM_B_TILE_T : mx::GEMM_B_TILE;
-    e = mx::launch_gemm_q(bmode, (int)out_elem, M, N, K, a, sa, b, sb, q, s, stream);
+    int cus;
+    {
+      std::lock_guard<std::mutex> lk(g_mu);
+      cus = g_num_cus[dev];
+    }
+    e = mx::launch_gemm_q(bmode, (int)out_elem, M, N, K, a, sa, b, sb, q, s, cus, stream);
   }
   if (e != hipSuccess) return hip_fail(e, "fused GEMM kernel launch");
   return MX_OK;

@@ -520,13 +520,14 @@ struct Tile {
   // issue_first() loads stage 0 and the first scale group (17 or 18 ops
   // per wave), issue_second() stage 1 (16 ops); run_issued() waits for
   // stage 0 only (all but the ops issued after it: stage 1's, and with
-  // `stored` the 32 result stores of the halves epilogue issued between the
-  // two) and runs the K loop into acc.
+  // `stored` the NST result stores of the halves epilogue issued between
+  // the two: 32 for BF16, 33 quantised) and runs the K loop into acc.
   __device__ __forceinline__ void issue_first(int wave, int lane) {
     issue_stage(st0, 0, wave, lane);
     dma_scales(ss0, 0, wave);
   }
   __device__ __forceinline__ void issue_second(int wave, int lane) { issue_stage(st1, BK, wave, lane); }
+  template <int NST = 32>
   __device__ __forceinline__ void run_issued(v16f (&acc)[4][4], int wave, int lane, bool stored) {
     static_assert(LDS_SCALES, "the split prologue is the LDS-staged-scale pipeline's");
     const int wm = wave & 1, wn = wave >> 1;
@@ -535,7 +536,7 @@ struct Tile {
 #pragma unroll
       for (int y = 0; y < 4; y++) acc[x][y] = (v16f){};
     if (stored)
-      wait_vm<32 + 2 * CHUNKS>();
+      wait_vm<NST + 2 * CHUNKS>();
     else
       wait_vm<2 * CHUNKS>();
     __syncthreads();
@@ -654,21 +655,24 @@ gemm_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa,
   t.run();
 }
 
-// Persistent form of the GEMM (K a multiple of 512, BF16 result, N a
-// multiple of 8): one workgroup per compute unit walks tiles bid, bid +
+// Persistent form of the GEMM (K a multiple of 512, BF16 result with N a
+// multiple of 8, or with OUT the fused producer's quantised result with N a
+// multiple of 256): one workgroup per compute unit walks tiles bid, bid +
 // grid, ... of gemm_kernel's tile map (a grid that is a multiple of 8 keeps
 // every tile on the XCD it has there, index mod 8, so an XCD still runs the
 // same 32-tile groups at a time), and each tile's stage 0 loads while the
 // previous tile's result is stored.
-template <int BMODE, int FA, int FB>
+template <int BMODE, int FA, int FB, int OUT = 0>
 __global__ void __launch_bounds__(NT)
 gemm_persistent_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict__ sa,
                        const uint8_t* __restrict__ b, const uint8_t* __restrict__ sb,
-                       uint16_t* __restrict__ c, int64_t M, int64_t N, int64_t K) {
+                       uint16_t* __restrict__ c, uint8_t* __restrict__ q, uint8_t* __restrict__ s,
+                       int64_t M, int64_t N, int64_t K) {
   __shared__ __attribute__((aligned(16))) uint8_t smem0[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t smem1[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t sscale[2 * SCALE_TILE];
   __shared__ __attribute__((aligned(16))) uint8_t spf[2048];
+  __shared__ __attribute__((aligned(16))) uint8_t ssq[OUT ? 2048 : 16];  // OUT: a tile's scales
   const int64_t nm = (M + BM - 1) / BM, nn = (N + BN - 1) / BN, tiles = nm * nn;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -711,7 +715,7 @@ gemm_persistent_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict_
   for (;;) {
     tl.issue_second(wave, lane);
     v16f acc[4][4];
-    tl.run_issued(acc, wave, lane, stored);
+    tl.template run_issued<OUT ? 33 : 32>(acc, wave, lane, stored);
     const int64_t m0 = tl.m0, m_end = tl.m_end, n0 = tl.n0;
     // every load has landed (none may still be writing LDS) and every wave
     // is past its last read of the stage and scale buffers
@@ -731,8 +735,12 @@ gemm_persistent_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict_
       tl.setup(wave, ln);
       tl.issue_first(wave, ln);
     }
-    store_tile_bf16_lds_halves(acc, (lds_u8*)smem1, c, N, m0, m_end, n0, N, wave & 1, wave >> 1,
-                               wave, ln);
+    if constexpr (OUT == 0)
+      store_tile_bf16_lds_halves(acc, (lds_u8*)smem1, c, N, m0, m_end, n0, N, wave & 1, wave >> 1,
+                                 wave, ln);
+    else
+      store_tile_q_lds_halves<OUT - 1>(acc, (lds_u8*)smem1, (lds_u8*)ssq, q, s, N, m0, m_end, n0,
+                                       wave & 1, wave >> 1, wave, ln);
     stored = true;
     if (!more) break;
   }
@@ -930,7 +938,7 @@ hipError_t launch_gemm(int bmode, int a_elem, int b_elem, int64_t M, int64_t N, 
     dim3 pg((unsigned)cus);
 #define MX_GEMMP_LAUNCH(BM_, FA_, FB_)                                                            \
   hipLaunchKernelGGL((gemm_persistent_kernel<BM_, FA_, FB_>), pg, dim3(NT), 0, stream, A, SA, B, SB, \
-                     C, M, N, K)
+                     C, (uint8_t*)nullptr, (uint8_t*)nullptr, M, N, K)
 #define MX_GEMMP_FMT(BM_)                                            \
   do {                                                               \
     if (a_elem == 0 && b_elem == 0) MX_GEMMP_LAUNCH(BM_, 0, 0);      \
@@ -971,7 +979,7 @@ hipError_t launch_gemm(int bmode, int a_elem, int b_elem, int64_t M, int64_t N, 
 
 hipError_t launch_gemm_q(int bmode, int out_elem, int64_t M, int64_t N, int64_t K, const void* a,
                          const void* sa, const void* b, const void* sb, void* q, void* s,
-                         hipStream_t stream) {
+                         int num_cus, hipStream_t stream) {
   if ((out_elem != 0 && out_elem != 1) || N % 32 != 0) return hipErrorInvalidValue;
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   dim3 grid((unsigned)tiles);
@@ -979,6 +987,28 @@ hipError_t launch_gemm_q(int bmode, int out_elem, int64_t M, int64_t N, int64_t 
                 *SB = (const uint8_t*)sb;
   uint8_t *Q = (uint8_t*)q, *S = (uint8_t*)s;
   const int pipe = pipe_of(bmode, N, K);
+  // persistent as the BF16 GEMM (same rule), its result quantised through
+  // the LDS halves epilogue (whole 256-byte payload rows, 8-byte scale
+  // pieces: N a multiple of 256); not with the transposed 32x32 weight,
+  // whose persistent form would spill there
+  const int64_t cus = (num_cus > 0 ? num_cus : 256) / 8 * 8;
+  if (pipe == 1 && N % 256 == 0 && (int64_t)BM * N < ((int64_t)1 << 31) && cus >= 8 &&
+      tiles > cus && (bmode == GEMM_B_ROW || (bmode == GEMM_B_TILE && K <= 4096))) {
+    dim3 pg((unsigned)cus);
+#define MX_GEMMPQ_LAUNCH(BM_, OUT_)                                                               \
+  hipLaunchKernelGGL((gemm_persistent_kernel<BM_, 0, 0, OUT_>), pg, dim3(NT), 0, stream, A, SA, B, \
+                     SB, (uint16_t*)nullptr, Q, S, M, N, K)
+#define MX_GEMMPQ_OUT(BM_)                        \
+  do {                                            \
+    if (out_elem == 0) MX_GEMMPQ_LAUNCH(BM_, 1);  \
+    else MX_GEMMPQ_LAUNCH(BM_, 2);                \
+  } while (0)
+    if (bmode == GEMM_B_ROW) MX_GEMMPQ_OUT(GEMM_B_ROW);
+    else MX_GEMMPQ_OUT(GEMM_B_TILE);
+#undef MX_GEMMPQ_OUT
+#undef MX_GEMMPQ_LAUNCH
+    return hipGetLastError();
+  }
 #define MX_GEMMQ_LAUNCH(BM_, KA_)                                                                 \
   do {                                                                                            \
     if (out_elem == 0)                                                                            \

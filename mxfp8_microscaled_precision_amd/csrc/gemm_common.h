@@ -468,6 +468,111 @@ __device__ __forceinline__ void store_tile_q(const v16f (&acc)[4][4], uint8_t* _
   }
 }
 
+// The halves epilogue of store_tile_bf16_lds_halves for the fused producer:
+// the BF16 rows staged in LDS are quantised in 1x32 blocks on their way out
+// (the four lanes holding a block's 16-byte chunks share its amax through a
+// quad DPP reduction; the same rounding to BF16 and the same scale rule as
+// the row quantiser), payload rows leave whole (8 bytes per lane, 256 bytes
+// per row), and each row's 8 scale bytes are gathered in `sst` (2 KB) and
+// stored as one 8-byte piece at the end.  Exactly 33 buffer stores per wave
+// (32 payload, 1 scale), rows past m_end at an out-of-range offset.
+// Requires N % 256 == 0 (whole tiles, 8-byte aligned scale pieces) and
+// 256 N < 2^31.
+template <int EL, int QR = 2>
+__device__ __forceinline__ void store_tile_q_lds_halves(const v16f (&acc)[4][4], lds_u8* buf,
+                                                        lds_u8* sst, uint8_t* __restrict__ q,
+                                                        uint8_t* __restrict__ s, int64_t N,
+                                                        int64_t m0, int64_t m_end, int64_t n0,
+                                                        int wm, int wn, int wave, int lane) {
+  const int g = lane >> 5, i = lane & 31;
+  const int k = lane & 31;
+  const int64_t mrows = m_end - m0;
+  const int64_t lds_ = N >> 5;  // scale bytes per row
+  const uint64_t qb = (uint64_t)(uintptr_t)(q + m0 * N);
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(uintptr_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(qb >> 32)) << 32) |
+                         (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)qb)),
+      0, __builtin_amdgcn_readfirstlane((int)(mrows * N)), 0x00020000);
+  const uint64_t sbase = (uint64_t)(uintptr_t)(s + m0 * lds_);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(uintptr_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(sbase >> 32)) << 32) |
+                         (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)sbase)),
+      0, __builtin_amdgcn_readfirstlane((int)(mrows * lds_)), 0x00020000);
+  // store j (< 16) of half h: local row lr = 32 wave + 2 j + lane / 32, tile
+  // row tr0 + 64 h + 2 j as in the BF16 form; payload byte offset
+  // off0 + (64 h + 2 j) N
+  const int lr0 = 32 * wave + (lane >> 5);
+  const int tr0 = 128 * (wave >> 1) + (lr0 & 63);
+  uint32_t rowq = (uint32_t)__builtin_amdgcn_readfirstlane((int)N);
+  uint32_t off0 = (uint32_t)tr0 * rowq + (uint32_t)(8 * k) +
+                  (uint32_t)__builtin_amdgcn_readfirstlane((int)n0);
+  int lim = (int)mrows - tr0;
+  // opaque, as in the BF16 form: not hoisted across a caller's K loop
+  asm volatile("" : "+s"(rowq), "+v"(off0), "+v"(lim));
+#pragma unroll
+  for (int h = 0; h < 2; h++) {
+#pragma unroll
+    for (int fn = 0; fn < 4; fn++) {
+#pragma unroll
+      for (int f2 = 0; f2 < 2; f2++) {
+        const v16f& v = acc[fn][2 * h + f2];
+        uint32_t p[4][2];
+#pragma unroll
+        for (int r4 = 0; r4 < 4; r4++) {
+          p[r4][0] = cvt_pk_bf16(v[4 * r4 + 0], v[4 * r4 + 1]);
+          p[r4][1] = cvt_pk_bf16(v[4 * r4 + 2], v[4 * r4 + 3]);
+        }
+#pragma unroll
+        for (int hh = 0; hh < 2; hh++)
+#pragma unroll
+          for (int d = 0; d < 2; d++) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(p[2 * hh][d], p[2 * hh + 1][d], false, false);
+            p[2 * hh][d] = sw[0];
+            p[2 * hh + 1][d] = sw[1];
+          }
+        const int row = 64 * wm + 32 * f2 + i;  // local row
+#pragma unroll
+        for (int hh = 0; hh < 2; hh++) {
+          const int chunk = 16 * wn + 4 * fn + 2 * hh + g;
+          *(lds_v4i*)(buf + row * 512 + ((chunk ^ (row & 31)) << 4)) =
+              (v4i){(int)p[2 * hh][0], (int)p[2 * hh][1], (int)p[2 * hh + 1][0], (int)p[2 * hh + 1][1]};
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int jb = 0; jb < 16; jb += QR) {
+      v4i w[QR];
+#pragma unroll
+      for (int u = 0; u < QR; u++) {
+        const int lr = lr0 + 2 * (jb + u);
+        w[u] = *(const lds_v4i*)(buf + lr * 512 + ((k ^ (lr & 31)) << 4));
+      }
+#pragma unroll
+      for (int u = 0; u < QR; u++) {
+        const int j = jb + u;
+        const uint4 x = make_uint4((uint32_t)w[u].x, (uint32_t)w[u].y, (uint32_t)w[u].z,
+                                   (uint32_t)w[u].w);
+        const uint32_t sb = scale_byte_t<EL>(quad_max(chunk_absmax(x)));
+        const uint2 pq = cvt8_t<EL>(x, sb);
+        // block k / 4 of tile row tr0 + 64 h + 2 j
+        if ((k & 3) == 0) sst[(tr0 + 64 * h + 2 * j) * 8 + (k >> 2)] = (uint8_t)sb;
+        uint32_t off = 64 * h + 2 * j < lim ? off0 + (uint32_t)(64 * h + 2 * j) * rowq : OOB;
+        asm volatile("" : "+v"(off));
+        __builtin_amdgcn_raw_buffer_store_b64((v2i){(int)pq.x, (int)pq.y}, rq, (int)off, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+  // the tile's scales: row 64 wave + lane, 8 bytes at column block n0 / 32
+  const int r = 64 * wave + lane;
+  const v2i sv = *(const lds_v2i*)(sst + r * 8);
+  uint32_t soff = r < (int)mrows ? (uint32_t)r * (uint32_t)lds_ + (uint32_t)(n0 >> 5) : OOB;
+  asm volatile("" : "+v"(soff));
+  __builtin_amdgcn_raw_buffer_store_b64(sv, rs, (int)soff, 0, 0);
+}
+
 // Linear workgroup id -> position t in the grouped tile order (GM_TILES
 // m-tiles, n-tiles outer), so that the 32 tiles an XCD runs at once (8 along
 // M x 4 along N) share A rows and B rows in that XCD's L2.  Workgroups are

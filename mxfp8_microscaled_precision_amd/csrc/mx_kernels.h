@@ -40,7 +40,7 @@ hipError_t launch_gemm(int bmode, int a_elem, int b_elem, int64_t M, int64_t N, 
 // blocks along N (out_elem 0 = E4M3, 1 = E5M2): q [M, N], s [M, N/32].
 hipError_t launch_gemm_q(int bmode, int out_elem, int64_t M, int64_t N, int64_t K, const void* a,
                          const void* sa, const void* b, const void* sb, void* q, void* s,
-                         hipStream_t stream);
+                         int num_cus, hipStream_t stream);
 
 // a_elem / b_elem: payload element types of the token rows and the expert
 // weights.

@@ -300,6 +300,40 @@ def test_fused_producer_bytes_equal_oracle(M, N, K, layout, bscale, out_elem):
     assert_bytes(s, ws, f"fused scales {layout} {bscale} K={K}")
 
 
+@pytest.mark.parametrize("out_elem", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("M,N,K,bscale", [
+    (4200, 4096, 1024, "1x32"),    # 17 x 16 = 272 tiles, the last row of tiles ragged
+    (4200, 4096, 2048, "32x32"),   # the 32x32 weight's persistent walk
+    (2100, 9216, 512, "1x32"),     # 9 x 36 = 324 tiles: a contiguous eighth per XCD
+])
+def test_fused_producer_persistent_sampled_rows(M, N, K, bscale, out_elem):
+    """More tiles than compute units with N a multiple of 256: the fused
+    producer walks its tiles persistently and quantises each result on its
+    way out of LDS.  The first and last row of every row of tiles and a few
+    seeded rows (all N columns) equal the oracle's row quantisation of its
+    exact product; rows past M are never written (a sentinel stays)."""
+    say(f"[exact] fused persistent {bscale} {M}x{N}x{K} -> {out_elem}")
+    qa, sa, qb, sb, bk = _fused_operands(M, N, K, "fprop", bscale, M + N + K + 11)
+    Mp = M + 32                    # sentinel rows below the result
+    q = torch.full((Mp, N), 0xA5, dtype=torch.uint8, device="cuda")
+    s = torch.full((Mp, N // 32), 0xA5, dtype=torch.uint8, device="cuda")
+    A, SA, B, SB = dev(qa), dev(sa), dev(qb), dev(sb)
+    rc = mx.mx_gemm_quant(mx.GEMM_LAYOUTS["fprop"], mx.BSCALE_KINDS[bscale], mx.ELEM_TYPES[out_elem],
+                          M, N, K, A.data_ptr(), SA.data_ptr(), B.data_ptr(), SB.data_ptr(),
+                          q.data_ptr(), s.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    assert rc == 0, mx.mx_last_error()
+    torch.cuda.synchronize()
+    edges = np.concatenate([np.arange(0, M, 256), np.minimum(np.arange(255, M + 255, 256), M - 1)])
+    extra = np.random.default_rng(M + K).choice(M, 8, replace=False)
+    rows = np.unique(np.concatenate([edges, extra])).astype(np.int64)
+    ref, _ = oracle.gemm(qa[rows], sa[rows], qb, sb, bk, want_bound=False)
+    wq, ws = oracle.quant_row(bf16_bits_exact(ref), oracle.ELEMS[out_elem])
+    ri = torch.from_numpy(rows).cuda()
+    assert_bytes(q.index_select(0, ri), wq, "fused persistent payload rows")
+    assert_bytes(s.index_select(0, ri), ws, "fused persistent scale rows")
+    assert torch.all(q[M:] == 0xA5) and torch.all(s[M:] == 0xA5), "rows past M were written"
+
+
 def test_fused_producer_full_size_sampled_rows():
     """The up projection's shape (32768 x 18432 x 7168) through the fused
     producer with one-hot token rows against the oracle-quantised stack
