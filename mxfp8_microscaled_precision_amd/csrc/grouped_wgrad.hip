@@ -312,25 +312,47 @@ grouped_wgrad_kernel(int64_t G, const int64_t* __restrict__ offsets, int64_t T, 
       s_order[r] = (short)g;
     }
     __syncthreads();
-    if (wave == 0) {
-      // lane j < groups holds group j's work; the least loaded is the
-      // smallest (work << 6 | j), found as the complement of a maximum
-      const int mine = (int)(w / per);
-      uint32_t load = 0;
-      for (int64_t p = 0; p < G; p++) {
-        const int g = s_order[p];
-        const uint32_t key = lane < groups ? (load << 6) | (uint32_t)lane : 0xFFFFFFFFu;
-        const int j = (int)(~wave_max(~key) & 63u);
-        if (lane == j) load += (s_key[g] >> 9) + W_TILE_COST;
-        if (j == mine) {
-          if (lane == 0) s_list[cnt] = (short)g;
-          cnt++;
+    if (groups == 1) {
+      // one group takes every expert, in the order
+      for (int64_t p = threadIdx.x; p < G; p += NT) s_list[p] = s_order[p];
+      cnt = (int)G;
+      __syncthreads();
+    } else {
+      if (wave == 0) {
+        // the order and each expert's work in registers (lane l of word m:
+        // position 64 m + l), read back with readlane; lane j < groups
+        // holds group j's work; the least loaded is the smallest
+        // (work << 6 | j), found as the complement of a maximum
+        int ord[W_MAX_GROUPS / 64];
+        uint32_t wk[W_MAX_GROUPS / 64];
+#pragma unroll
+        for (int m = 0; m < W_MAX_GROUPS / 64; m++) {
+          const int p = 64 * m + lane;
+          ord[m] = p < G ? s_order[p] : 0;
+          wk[m] = p < G ? (s_key[ord[m]] >> 9) + W_TILE_COST : 0u;
         }
+        const int mine = (int)(w / per);
+        uint32_t load = 0;
+#pragma unroll
+        for (int m = 0; m < W_MAX_GROUPS / 64; m++) {
+          const int lim = (int)(G - 64 * m) < 64 ? (int)(G - 64 * m) : 64;
+          for (int l = 0; l < lim; l++) {
+            const int g = __builtin_amdgcn_readlane(ord[m], l);
+            const uint32_t wg = (uint32_t)__builtin_amdgcn_readlane((int)wk[m], l);
+            const uint32_t key = lane < groups ? (load << 6) | (uint32_t)lane : 0xFFFFFFFFu;
+            const int j = (int)(~wave_max(~key) & 63u);
+            if (lane == j) load += wg;
+            if (j == mine) {
+              if (lane == 0) s_list[cnt] = (short)g;
+              cnt++;
+            }
+          }
+        }
+        if (lane == 0) s_cnt = cnt;
       }
-      if (lane == 0) s_cnt = cnt;
+      __syncthreads();
+      cnt = s_cnt;
     }
-    __syncthreads();
-    cnt = s_cnt;
   }
   const int64_t run = per >> 3;
   struct Cur {  // where a tile's result goes: expert, rows, first column

@@ -259,6 +259,7 @@ def test_wgrad_equals_dense_gemm_per_expert():
      1024, 1024),
     ([3000, 129, 2500, 600, 0, 1800, 64, 1100, 4000], 2048, 2048),   # 64 per expert: 4 groups
     ([5000, 300, 2600, 1, 700], 4096, 2048),                          # 128 per expert: 2 groups
+    ([900, 0, 2000, 130, 1], 4096, 4096),                             # 256 per expert: one group
     ([700, 260], 4608, 4608),        # 324 tiles per expert, more than the grid: a strided walk
     ([(37 * g) % 300 for g in range(100)], 768, 256),                # 3 per expert: a strided walk
     # every step count from 1 to 24: a workgroup's consecutive tiles have odd
